@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle's callers.
+
+This module draws numbers and rounds them to the storage dtype; it contains none of
+the attention arithmetic.  Both the HIP path and the CPU oracle receive the very same
+bytes: fp32 N(0,1) samples rounded to bf16 (round to nearest, ties to even) on the
+host for bf16 workloads, plain fp32 samples for fp32 workloads.
+
+Streams: numpy PCG64 seeded by SeedSequence(seed).spawn(...) in the fixed tensor order
+below.  Large tensors are generated in fixed blocks of BLOCK elements, each from its own
+spawned child, so the values do not depend on the number of threads used.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from .configs import Workload
+
+STREAMS = ["q", "k_p", "v_p", "k_r", "v_r", "d_o", "q_idx", "k_idx", "r_len", "rows"]
+BLOCK = 1 << 22
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _stream_seed(seed: int, name: str) -> np.random.SeedSequence:
+    return np.random.SeedSequence(seed).spawn(len(STREAMS))[STREAMS.index(name)]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal(seed: int, name: str, shape: Sequence[int], dtype: str) -> np.ndarray:
+    """N(0,1) tensor of `shape`: fp32 values (dtype "f32") or bf16 bit patterns (dtype "bf16")."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    nblk = max(1, -(-n // BLOCK))
+    kids = _stream_seed(seed, name).spawn(nblk)
+
+    def fill(i: int) -> None:
+        lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+        x = np.random.Generator(np.random.PCG64(kids[i])).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    if nblk == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored values (fp32, or bf16 bit patterns) to fp64 for the oracle."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64)
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+def response_lengths(w: Workload) -> np.ndarray:
+    """Lengths R_g of the G serially replayed members (integers, inclusive range)."""
+    if w.r_min is None:
+        return np.full(w.G, w.R, dtype=np.int64)
+    g = np.random.Generator(np.random.PCG64(_stream_seed(w.seed, "r_len")))
+    return g.integers(w.r_min, w.R, size=w.G, endpoint=True).astype(np.int64)
+
+
+def resident(w: Workload) -> Dict[str, np.ndarray]:
+    """Resident prompt state: K_p, V_p `[P][Hkv][d]` (dense) or the latent rows `[P][d_qk]`
+    plus fp32 index keys `[P][idx_dim]` (latent variant)."""
+    if w.latent:
+        out = {"latent_p": normal(w.seed, "k_p", (w.P, w.d_qk), w.dtype)}
+        if w.topk:
+            out["k_idx"] = normal(w.seed, "k_idx", (w.P, w.idx_dim), "f32")
+        return out
+    return {"k_p": normal(w.seed, "k_p", (w.P, w.Hkv, w.d_qk), w.dtype),
+            "v_p": normal(w.seed, "v_p", (w.P, w.Hkv, w.d_v), w.dtype)}
+
+
+def member(w: Workload, g: int = 0, R: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of replayed member g: Q, the response's own K/V, upstream dO (and q_idx).
+
+    Member g > 0 draws from seed (w.seed + 7919 * g) so every member has its own tensors.
+    """
+    R = w.R if R is None else R
+    seed = w.seed + 7919 * g
+    out = {"q": normal(seed, "q", (R, w.Hq, w.d_qk), w.dtype),
+           "d_o": normal(seed, "d_o", (R, w.Hq, w.d_v), w.dtype)}
+    if w.latent:
+        out["latent_r"] = normal(seed, "k_r", (R, w.d_qk), w.dtype)
+        if w.topk:
+            out["q_idx"] = normal(seed, "q_idx", (R, w.idx_dim), "f32")
+    else:
+        out["k_r"] = normal(seed, "k_r", (R, w.Hkv, w.d_qk), w.dtype)
+        out["v_r"] = normal(seed, "v_r", (R, w.Hkv, w.d_v), w.dtype)
+    return out
+
+
+def sample_rows(seed: int, R: int, n: int, block: int) -> np.ndarray:
+    """Sorted query rows to check at full size: row 0, row R-1, both sides of every block
+    boundary, the first row of a partial last block, then seeded rows without replacement."""
+    must = {0, R - 1}
+    for b in range(block, R, block):
+        must.update({b - 1, b})
+    must = sorted(r for r in must if 0 <= r < R)
+    if len(must) >= n or len(must) >= R:
+        return np.array(must[:max(n, 0)] if len(must) > n else must, dtype=np.int64)
+    g = np.random.Generator(np.random.PCG64(_stream_seed(seed, "rows")))
+    rest = np.setdiff1d(np.arange(R), np.array(must))
+    extra = g.choice(rest, size=min(n - len(must), rest.size), replace=False)
+    return np.sort(np.concatenate([np.array(must), extra])).astype(np.int64)
