@@ -1,0 +1,58 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rr_internal.h"
+
+namespace rr {
+
+struct AttnPtrs {
+  const void* q;      // [K][R][Hq][d_qk]
+  const void* k_p;    // [P][Hkv][d_qk]
+  const void* v_p;    // [P][Hkv][d_v]
+  const void* k_r;    // [K][R][Hkv][d_qk]
+  const void* v_r;    // [K][R][Hkv][d_v]
+  const void* d_o;    // [K][R][Hq][d_v]           (backward)
+  const float* lse;   // [K][R][Hq]                (backward; global statistics)
+  const float* Dvec;  // [K][R][Hq]                (backward)
+  float* part_o;      // [n_parts][K][R][Hq][d_v]  (forward partials)
+  float* part_lse;    // [n_parts][K][R][Hq]
+  float* dq_part;     // [n_parts][K][R][Hq][d_qk] (backward partials)
+  float* dk_r;        // [K][R][Hkv][d_qk]
+  float* dv_r;        // [K][R][Hkv][d_v]
+};
+
+// Forward partials: one softmax-statistics partial per prompt chunk plus the causal
+// response part, for query rows [g.row_lo, g.row_hi).
+hipError_t launch_fwd_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s);
+
+// Exact merge of n partials.  With `geom` non-null the rows are (k, r, h) of that
+// geometry and padding rows (r >= r_len[k]) get O = 0, lse = -inf without reading parts.
+hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
+                        const float* part_lse, float* o, float* lse, const Geom* geom,
+                        hipStream_t s);
+
+// D = rowsum(dO * O) for rows [g.row_lo, g.row_hi); padding rows get 0.
+hipError_t launch_bwd_pre(const Geom& g, int dtype, const float* o, const void* d_o,
+                          float* Dvec, hipStream_t s);
+
+// dQ partials over every part for query rows [g.row_lo, g.row_hi).
+hipError_t launch_dq_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s);
+
+// dq (= or +=) sum over parts in part order, rows [g.row_lo, g.row_hi); padding rows 0.
+hipError_t launch_dq_reduce(const Geom& g, const float* dq_part, float* dq, int accumulate,
+                            hipStream_t s);
+
+// dk_r/dv_r += contributions of query rows [g.row_lo, g.row_hi) to response keys
+// [0, key_hi).
+hipError_t launch_dkdv(const Geom& g, int dtype, const AttnPtrs& a, int key_hi, hipStream_t s);
+
+// Zero rows [lo, hi) of every response in a [K][R][row_elems] fp32 tensor.
+hipError_t launch_zero_rows(float* x, int K, int R, int lo, int hi, int64_t row_elems,
+                            hipStream_t s);
+
+// acc[e] += scale * g[e], e < n.
+hipError_t launch_axpy(float* acc, const float* g, int64_t n, float scale, hipStream_t s);
+
+}  // namespace rr

@@ -1,0 +1,260 @@
+// C ABI entry points: validate, carve the caller's workspace, launch on the caller's
+// stream.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "rr_internal.h"
+
+namespace rr {
+
+hipError_t launch_fwd_partials_f32(const Geom& g, const AttnPtrs& a, hipStream_t s);
+hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
+hipError_t launch_dq_partials_f32(const Geom& g, const AttnPtrs& a, hipStream_t s);
+hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
+hipError_t launch_dkdv_f32(const Geom& g, const AttnPtrs& a, int key_hi, hipStream_t s);
+hipError_t launch_dkdv_bf16(const Geom& g, const AttnPtrs& a, int key_hi, hipStream_t s);
+
+hipError_t launch_fwd_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s) {
+  return dtype == RR_BF16 ? launch_fwd_partials_bf16(g, a, s) : launch_fwd_partials_f32(g, a, s);
+}
+hipError_t launch_dq_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s) {
+  return dtype == RR_BF16 ? launch_dq_partials_bf16(g, a, s) : launch_dq_partials_f32(g, a, s);
+}
+hipError_t launch_dkdv(const Geom& g, int dtype, const AttnPtrs& a, int key_hi, hipStream_t s) {
+  return dtype == RR_BF16 ? launch_dkdv_bf16(g, a, key_hi, s) : launch_dkdv_f32(g, a, key_hi, s);
+}
+
+// ---- profiling: HIP events around every launch -----------------------------------------
+namespace {
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRec> recs;
+};
+
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  Prof& P = prof();
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    on = P.on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  hipError_t e = hipEventCreate(&a);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventCreate(&b)) != hipSuccess) return e;
+  if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
+  e = launch();
+  const hipError_t e2 = hipEventRecord(b, s);
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.recs.push_back({name, a, b});
+  }
+  return e != hipSuccess ? e : e2;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_error(RR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+float* carve(void* base, size_t offset) {
+  return reinterpret_cast<float*>(static_cast<char*>(base) + offset);
+}
+
+}  // namespace
+
+}  // namespace rr
+
+using namespace rr;
+
+extern "C" {
+
+int rr_attn_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                const void* v_r, const int32_t* r_len, const float* q_idx, float* o, float* lse,
+                float* part_o, float* part_lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                void* stream) {
+  clear_error();
+  int rc = validate_fwd(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx, ws,
+                        ws_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Geom g = make_geom(p, r_len);
+  const size_t rows = (size_t)p->K * p->R_max * p->Hq;
+  float* po = part_o;
+  float* pl = part_lse;
+  if (!po) {
+    po = carve(ws, 0);
+    pl = carve(ws, align_up((size_t)g.n_parts * rows * p->d_v * sizeof(float), 256));
+  }
+  AttnPtrs a{};
+  a.q = q;
+  a.k_p = kv->k_p;
+  a.v_p = kv->v_p;
+  a.k_r = k_r;
+  a.v_r = v_r;
+  a.part_o = po;
+  a.part_lse = pl;
+  hipError_t e = timed("fwd_partials", s, [&] { return launch_fwd_partials(g, p->dtype, a, s); });
+  if (e != hipSuccess) return hip_fail(e, "fwd_partials");
+  if (o) {
+    e = timed("lse_merge", s, [&] {
+      return launch_merge(g.n_parts, (int64_t)rows, p->d_v, po, pl, o, lse, &g, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "lse_merge");
+  }
+  return RR_OK;
+}
+
+int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
+                 const float* part_lse, float* o, float* lse, void* stream) {
+  clear_error();
+  int rc = validate_merge(n_parts, rows, d_v, part_o, part_lse, o, lse);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("lse_merge", s, [&] {
+    return launch_merge(n_parts, rows, d_v, part_o, part_lse, o, lse, nullptr, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "lse_merge");
+  return RR_OK;
+}
+
+int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                const void* v_r, const int32_t* r_len, const int32_t* topk_idx, const float* o,
+                const float* lse, const void* d_o, float* dq, float* dk_r, float* dv_r,
+                int32_t accumulate, int32_t block_idx, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = validate_bwd(p, kv, q, k_r, v_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r, accumulate,
+                        block_idx, ws, ws_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Geom g = make_geom(p, r_len);
+  const size_t rows = (size_t)p->K * p->R_max * p->Hq;
+  float* Dvec = carve(ws, 0);
+  float* dq_part = carve(ws, align_up(rows * sizeof(float), 256));
+  AttnPtrs a{};
+  a.q = q;
+  a.k_p = kv->k_p;
+  a.v_p = kv->v_p;
+  a.k_r = k_r;
+  a.v_r = v_r;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.Dvec = Dvec;
+  a.dq_part = dq_part;
+  a.dk_r = dk_r;
+  a.dv_r = dv_r;
+  const int nb = (p->R_max + p->block - 1) / p->block;
+  const int64_t kv_row = (int64_t)p->Hkv * p->d_qk;
+  if (block_idx >= 0) {
+    g.row_lo = block_idx * p->block;
+    g.row_hi = std::min(p->R_max, g.row_lo + p->block);
+  }
+  hipError_t e;
+  if ((e = timed("bwd_pre", s, [&] { return launch_bwd_pre(g, p->dtype, o, d_o, Dvec, s); })))
+    return hip_fail(e, "bwd_pre");
+  if ((e = timed("dq_partials", s, [&] { return launch_dq_partials(g, p->dtype, a, s); })))
+    return hip_fail(e, "dq_partials");
+  if ((e = timed("dq_reduce", s, [&] { return launch_dq_reduce(g, dq_part, dq, accumulate, s); })))
+    return hip_fail(e, "dq_reduce");
+  const int key_top = g.row_hi;   // response keys reachable from the launch's rows
+  if (!accumulate) {
+    if ((e = timed("zero_rows", s, [&] {
+           hipError_t e1 = launch_zero_rows(dk_r, p->K, p->R_max, 0, key_top, kv_row, s);
+           return e1 != hipSuccess ? e1 : launch_zero_rows(dv_r, p->K, p->R_max, 0, key_top, kv_row, s);
+         })))
+      return hip_fail(e, "zero_rows");
+  }
+  const int b_hi = block_idx >= 0 ? block_idx : nb - 1;
+  const int b_lo = block_idx >= 0 ? block_idx : 0;
+  for (int b = b_hi; b >= b_lo; --b) {   // reverse block walk
+    Geom gb = g;
+    gb.row_lo = b * p->block;
+    gb.row_hi = std::min(p->R_max, gb.row_lo + p->block);
+    if ((e = timed("dkdv", s, [&] { return launch_dkdv(gb, p->dtype, a, gb.row_hi, s); })))
+      return hip_fail(e, "dkdv");
+  }
+  return RR_OK;
+}
+
+int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version, const float* const* grads,
+                  const int64_t* n_elems, float scale, void* stream) {
+  clear_error();
+  int rc = validate_accum(acc, member_g, version, grads, n_elems);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < acc->n_bufs; ++i) {
+    hipError_t e = timed("grad_accum", s, [&] { return launch_axpy(acc->buf[i], grads[i], n_elems[i], scale, s); });
+    if (e != hipSuccess) return hip_fail(e, "grad_accum");
+  }
+  acc->seen[member_g] = 1;
+  return RR_OK;
+}
+
+int rr_profile_begin(void) {
+  clear_error();
+  Prof& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  for (auto& r : P.recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  P.recs.clear();
+  P.on = true;
+  return RR_OK;
+}
+
+int rr_profile_end(rr_profile_entry* out, int32_t max_entries, int32_t* n_out) {
+  clear_error();
+  Prof& P = prof();
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.on = false;
+    recs.swap(P.recs);
+  }
+  std::vector<rr_profile_entry> agg;
+  int rc = RR_OK;
+  for (auto& r : recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess && rc == RR_OK) rc = hip_fail(e, "profile events");
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+    size_t i = 0;
+    while (i < agg.size() && strcmp(agg[i].name, r.name) != 0) ++i;
+    if (i == agg.size()) {
+      rr_profile_entry z;
+      memset(&z, 0, sizeof(z));
+      strncpy(z.name, r.name, sizeof(z.name) - 1);
+      agg.push_back(z);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+  }
+  const int n = (int)agg.size() < max_entries ? (int)agg.size() : max_entries;
+  if (out)
+    for (int i = 0; i < n; ++i) out[i] = agg[i];
+  if (n_out) *n_out = n;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host library sources (not part of the C ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rr_attn.h"
+
+namespace rr {
+
+// Geometry of one launch, passed to kernels by value.
+struct Geom {
+  int64_t P;          // resident prompt positions
+  int64_t chunk;      // prompt chunk length
+  int32_t R;          // row stride (R_max)
+  int32_t K;          // responses in the microbatch
+  int32_t Hq, Hkv, grp;
+  int32_t dqk, dv;
+  int32_t n_chunks;   // prompt chunks
+  int32_t n_parts;    // n_chunks + 1 (the response's causal keys are the last part)
+  int32_t row_lo;     // query rows [row_lo, row_hi) handled by this launch
+  int32_t row_hi;
+  float tau;          // softmax scale
+  float c2;           // tau * log2(e): scores in base-2 units
+  int32_t r_len[RR_MAX_K];
+};
+
+// ---- validation (HIP-free; rr_validate.cpp) ----------------------------------------
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+int validate_problem(const rr_problem* p);
+int64_t n_chunks_of(const rr_problem* p);
+int32_t n_parts_of(const rr_problem* p);
+size_t ws_fwd_bytes(const rr_problem* p, bool exported);
+size_t ws_bwd_bytes(const rr_problem* p);
+int validate_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                 const void* v_r, const int32_t* r_len, const float* q_idx, const float* o,
+                 const float* lse, const float* part_o, const float* part_lse,
+                 const int32_t* topk_idx, const void* ws, size_t ws_bytes);
+int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                 const void* v_r, const int32_t* r_len, const int32_t* topk_idx,
+                 const float* o, const float* lse, const void* d_o, const float* dq,
+                 const float* dk_r, const float* dv_r, int32_t accumulate, int32_t block_idx,
+                 const void* ws, size_t ws_bytes);
+int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
+                   const float* part_lse, const float* o, const float* lse);
+int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
+                   const float* const* grads, const int64_t* n_elems);
+Geom make_geom(const rr_problem* p, const int32_t* r_len);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace rr

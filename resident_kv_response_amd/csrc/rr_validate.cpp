@@ -1,0 +1,241 @@
+// Argument validation, workspace sizing and error reporting.  HIP-free: every check
+// here runs on the host before anything is launched, so an invalid call has no side
+// effects on the device.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+#include "rr_internal.h"
+
+namespace rr {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+const char* last_error() { return g_err; }
+
+int validate_problem(const rr_problem* p) {
+  if (!p) return set_error(RR_E_NULL, "problem is NULL");
+  if (p->P < 1) return set_error(RR_E_SHAPE, "P must be >= 1 (got %lld)", (long long)p->P);
+  if (p->R_max < 1) return set_error(RR_E_SHAPE, "R_max must be >= 1 (got %d)", p->R_max);
+  if (p->K < 1 || p->K > RR_MAX_K)
+    return set_error(RR_E_SHAPE, "K must be in [1, %d] (got %d)", RR_MAX_K, p->K);
+  if (p->Hq < 1 || p->Hkv < 1)
+    return set_error(RR_E_SHAPE, "Hq and Hkv must be >= 1 (got %d, %d)", p->Hq, p->Hkv);
+  if (p->Hq % p->Hkv != 0)
+    return set_error(RR_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->chunk < 1) return set_error(RR_E_SHAPE, "chunk must be >= 1 (got %lld)", (long long)p->chunk);
+  if (p->block < 1) return set_error(RR_E_SHAPE, "block must be >= 1 (got %d)", p->block);
+  if (!(p->tau > 0.0f) || !std::isfinite(p->tau))
+    return set_error(RR_E_SHAPE, "tau must be finite and > 0");
+  if (p->dtype != RR_F32 && p->dtype != RR_BF16)
+    return set_error(RR_E_SHAPE, "dtype must be RR_F32 or RR_BF16 (got %d)", p->dtype);
+  if (p->topk < 0) return set_error(RR_E_SHAPE, "topk must be >= 0");
+  if (p->latent) {
+    return set_error(RR_E_UNSUPPORTED, "latent pages are not supported by this build");
+  }
+  if (p->topk != 0)
+    return set_error(RR_E_UNSUPPORTED, "top-k selection needs latent pages");
+  if (p->d_qk != p->d_v || (p->d_qk != 64 && p->d_qk != 128))
+    return set_error(RR_E_UNSUPPORTED, "dense head dims must be d_qk == d_v in {64, 128} (got %d, %d)",
+                     p->d_qk, p->d_v);
+  // 32-bit index products inside kernels: rows * heads * dims per response tensor
+  const int64_t row_elems = (int64_t)p->K * p->R_max * p->Hq * (int64_t)p->d_qk;
+  if (row_elems > (int64_t)1 << 31)
+    return set_error(RR_E_SHAPE, "K*R_max*Hq*d_qk exceeds 2^31 elements");
+  if (n_parts_of(p) > (1 << 20)) return set_error(RR_E_SHAPE, "too many prompt chunks");
+  return RR_OK;
+}
+
+int64_t n_chunks_of(const rr_problem* p) { return (p->P + p->chunk - 1) / p->chunk; }
+
+int32_t n_parts_of(const rr_problem* p) { return (int32_t)(n_chunks_of(p) + 1); }
+
+static bool a16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
+
+static int check_aligned(const char* what, std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (x && !a16(x)) return set_error(RR_E_SHAPE, "%s must be 16-byte aligned", what);
+  return RR_OK;
+}
+
+static size_t rows_total(const rr_problem* p) { return (size_t)p->K * p->R_max * p->Hq; }
+
+size_t ws_fwd_bytes(const rr_problem* p, bool exported) {
+  if (exported) return 0;
+  const size_t n = (size_t)n_parts_of(p) * rows_total(p);
+  return align_up(n * p->d_v * sizeof(float), 256) + align_up(n * sizeof(float), 256);
+}
+
+size_t ws_bwd_bytes(const rr_problem* p) {
+  const size_t rows = rows_total(p);
+  return align_up(rows * sizeof(float), 256) +
+         align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256);
+}
+
+static int check_r_len(const rr_problem* p, const int32_t* r_len) {
+  if (!r_len) return set_error(RR_E_NULL, "r_len is NULL");
+  for (int k = 0; k < p->K; ++k)
+    if (r_len[k] < 0 || r_len[k] > p->R_max)
+      return set_error(RR_E_SHAPE, "r_len[%d] = %d outside [0, R_max=%d]", k, r_len[k], p->R_max);
+  return RR_OK;
+}
+
+static int check_resident(const rr_problem* p, const rr_resident* kv) {
+  if (!kv) return set_error(RR_E_NULL, "resident is NULL");
+  if (!kv->k_p || !kv->v_p) return set_error(RR_E_NULL, "resident k_p / v_p is NULL");
+  if (kv->P != p->P)
+    return set_error(RR_E_SHAPE, "resident P (%lld) != problem P (%lld)", (long long)kv->P,
+                     (long long)p->P);
+  return RR_OK;
+}
+
+int validate_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                 const void* v_r, const int32_t* r_len, const float* q_idx, const float* o,
+                 const float* lse, const float* part_o, const float* part_lse,
+                 const int32_t* topk_idx, const void* ws, size_t ws_bytes) {
+  (void)q_idx;
+  (void)topk_idx;
+  int rc = validate_problem(p);
+  if (rc) return rc;
+  if ((rc = check_resident(p, kv))) return rc;
+  if (!q || !k_r || !v_r) return set_error(RR_E_NULL, "q / k_r / v_r is NULL");
+  if ((rc = check_r_len(p, r_len))) return rc;
+  if ((o == nullptr) != (lse == nullptr))
+    return set_error(RR_E_NULL, "o and lse must both be given or both be NULL");
+  if ((part_o == nullptr) != (part_lse == nullptr))
+    return set_error(RR_E_NULL, "part_o and part_lse must both be given or both be NULL");
+  if (!o && !part_o) return set_error(RR_E_NULL, "no output: give o/lse, part_o/part_lse or both");
+  if ((rc = check_aligned("q / k_r / v_r / k_p / v_p / o / part_o", {q, k_r, v_r, kv->k_p, kv->v_p, o, part_o})))
+    return rc;
+  const size_t need = ws_fwd_bytes(p, part_o != nullptr);
+  if (need && (!ws || ws_bytes < need))
+    return set_error(RR_E_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                     ws ? "" : ", NULL");
+  return RR_OK;
+}
+
+int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                 const void* v_r, const int32_t* r_len, const int32_t* topk_idx,
+                 const float* o, const float* lse, const void* d_o, const float* dq,
+                 const float* dk_r, const float* dv_r, int32_t accumulate, int32_t block_idx,
+                 const void* ws, size_t ws_bytes) {
+  (void)topk_idx;
+  int rc = validate_problem(p);
+  if (rc) return rc;
+  if ((rc = check_resident(p, kv))) return rc;
+  if (!q || !k_r || !v_r || !o || !lse || !d_o)
+    return set_error(RR_E_NULL, "q / k_r / v_r / o / lse / d_o is NULL");
+  if (!dq || !dk_r || !dv_r) return set_error(RR_E_NULL, "dq / dk_r / dv_r is NULL");
+  if ((rc = check_r_len(p, r_len))) return rc;
+  if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
+  if ((rc = check_aligned("q / k_r / v_r / k_p / v_p / o / d_o / dq / dk_r / dv_r",
+                          {q, k_r, v_r, kv->k_p, kv->v_p, o, d_o, dq, dk_r, dv_r})))
+    return rc;
+  const int32_t nb = (p->R_max + p->block - 1) / p->block;
+  if (block_idx < -1 || block_idx >= nb)
+    return set_error(RR_E_SHAPE, "block_idx %d outside [-1, %d)", block_idx, nb);
+  const size_t need = ws_bwd_bytes(p);
+  if (!ws || ws_bytes < need)
+    return set_error(RR_E_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                     ws ? "" : ", NULL");
+  return RR_OK;
+}
+
+int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
+                   const float* part_lse, const float* o, const float* lse) {
+  if (n_parts < 1) return set_error(RR_E_SHAPE, "n_parts must be >= 1 (got %d)", n_parts);
+  if (rows < 0) return set_error(RR_E_SHAPE, "rows must be >= 0");
+  if (d_v < 1 || d_v > 4096) return set_error(RR_E_SHAPE, "d_v must be in [1, 4096] (got %d)", d_v);
+  if ((int64_t)n_parts * rows * d_v > ((int64_t)1 << 40))
+    return set_error(RR_E_SHAPE, "merge too large");
+  if (rows > 0 && (!part_o || !part_lse || !o || !lse))
+    return set_error(RR_E_NULL, "part_o / part_lse / o / lse is NULL");
+  return RR_OK;
+}
+
+int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
+                   const float* const* grads, const int64_t* n_elems) {
+  if (!acc) return set_error(RR_E_NULL, "accumulator is NULL");
+  if (acc->n_bufs < 1 || acc->n_bufs > RR_MAX_ACC)
+    return set_error(RR_E_SHAPE, "n_bufs must be in [1, %d] (got %d)", RR_MAX_ACC, acc->n_bufs);
+  if (acc->G < 1) return set_error(RR_E_SHAPE, "G must be >= 1");
+  if (!acc->seen) return set_error(RR_E_NULL, "seen mask is NULL");
+  if (member_g < 0 || member_g >= acc->G)
+    return set_error(RR_E_RANGE, "member %d outside [0, G=%d)", member_g, acc->G);
+  if (version != acc->version)
+    return set_error(RR_E_STALE, "member %d computed against resident version %llu, window is at %llu",
+                     member_g, (unsigned long long)version, (unsigned long long)acc->version);
+  if (acc->seen[member_g])
+    return set_error(RR_E_DUPLICATE, "member %d already accumulated in this window", member_g);
+  if (!grads || !n_elems) return set_error(RR_E_NULL, "grads / n_elems is NULL");
+  for (int i = 0; i < acc->n_bufs; ++i) {
+    if (n_elems[i] < 0 || n_elems[i] > acc->n[i])
+      return set_error(RR_E_SHAPE, "buffer %d: %lld elements exceed the accumulator's %lld", i,
+                       (long long)n_elems[i], (long long)acc->n[i]);
+    if (n_elems[i] > 0 && (!grads[i] || !acc->buf[i]))
+      return set_error(RR_E_NULL, "buffer %d: gradient or accumulator pointer is NULL", i);
+  }
+  return RR_OK;
+}
+
+Geom make_geom(const rr_problem* p, const int32_t* r_len) {
+  Geom g;
+  memset(&g, 0, sizeof(g));
+  g.P = p->P;
+  g.chunk = p->chunk;
+  g.R = p->R_max;
+  g.K = p->K;
+  g.Hq = p->Hq;
+  g.Hkv = p->Hkv;
+  g.grp = p->Hq / p->Hkv;
+  g.dqk = p->d_qk;
+  g.dv = p->d_v;
+  g.n_chunks = (int32_t)n_chunks_of(p);
+  g.n_parts = g.n_chunks + 1;
+  g.row_lo = 0;
+  g.row_hi = p->R_max;
+  g.tau = p->tau;
+  g.c2 = (float)(p->tau * 1.4426950408889634);
+  for (int k = 0; k < p->K; ++k) g.r_len[k] = r_len[k];
+  return g;
+}
+
+}  // namespace rr
+
+extern "C" {
+
+size_t rr_workspace_bytes(const rr_problem* p, int op) {
+  if (rr::validate_problem(p)) return 0;
+  if (op == RR_OP_FWD) return rr::ws_fwd_bytes(p, false);
+  if (op == RR_OP_BWD) return rr::ws_bwd_bytes(p);
+  rr::set_error(RR_E_SHAPE, "unknown op %d", op);
+  return 0;
+}
+
+int32_t rr_num_parts(const rr_problem* p) {
+  if (rr::validate_problem(p)) return 0;
+  return rr::n_parts_of(p);
+}
+
+int rr_accum_check_complete(const rr_accum* acc) {
+  if (!acc || !acc->seen) return rr::set_error(RR_E_NULL, "accumulator or seen mask is NULL");
+  for (int g = 0; g < acc->G; ++g)
+    if (!acc->seen[g]) return rr::set_error(RR_E_MISSING, "member %d of %d was never accumulated", g, acc->G);
+  return RR_OK;
+}
+
+const char* rr_last_error(void) { return rr::last_error(); }
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+"""GPU-side helpers for the parity tests: numpy inputs -> device tensors -> the C ABI.
+
+Everything here is marshalling; the computation runs in librr_attn.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from resident_kv_response_amd import rr_attn as R
+from resident_kv_response_amd.synth import as_f64
+
+DEV = "cuda"
+
+
+def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def stack_members(members, R_max, keys=("q", "k_r", "v_r", "d_o")):
+    """Stack per-member arrays [R_g][...] into [K][R_max][...], zero-padded."""
+    out = {}
+    for key in keys:
+        first = members[0][key]
+        arr = np.zeros((len(members), R_max) + first.shape[1:], dtype=first.dtype)
+        for i, m in enumerate(members):
+            arr[i, :m[key].shape[0]] = m[key]
+        out[key] = arr
+    return out
+
+
+def problem(P, R_max, Hq, Hkv, d, chunk, block, dtype, K=1, tau=None):
+    return R.Problem(P=P, R_max=R_max, Hq=Hq, Hkv=Hkv, d_qk=d, d_v=d, chunk=chunk, block=block,
+                     tau=float(tau if tau is not None else 1.0 / np.sqrt(d)),
+                     dtype=R.RR_BF16 if dtype == "bf16" else R.RR_F32, K=K)
+
+
+class Run:
+    """Device copies of one problem's inputs plus its outputs."""
+
+    def __init__(self, prob: R.Problem, dtype: str, k_p, v_p, stacked, r_len, version=0):
+        self.p, self.dtype, self.r_len = prob, dtype, [int(x) for x in r_len]
+        self.k_p, self.v_p = to_dev(k_p, dtype), to_dev(v_p, dtype)
+        self.q = to_dev(stacked["q"], dtype)
+        self.k_r = to_dev(stacked["k_r"], dtype)
+        self.v_r = to_dev(stacked["v_r"], dtype)
+        self.d_o = to_dev(stacked["d_o"], dtype)
+        self.kv = R.resident(self.k_p, self.v_p, version=version)
+        K, Rm, Hq, d = prob.K, prob.R_max, prob.Hq, prob.d_qk
+        f = dict(device=DEV, dtype=torch.float32)
+        self.o = torch.full((K, Rm, Hq, prob.d_v), float("nan"), **f)
+        self.lse = torch.full((K, Rm, Hq), float("nan"), **f)
+        self.dq = torch.full((K, Rm, Hq, d), float("nan"), **f)
+        self.dk = torch.full((K, Rm, prob.Hkv, d), float("nan"), **f)
+        self.dv = torch.full((K, Rm, prob.Hkv, prob.d_v), float("nan"), **f)
+        self.ws_f = R.workspace(prob, R.RR_OP_FWD, DEV)
+        self.ws_b = R.workspace(prob, R.RR_OP_BWD, DEV)
+
+    def fwd(self, **kw):
+        R.rr_attn_fwd(self.p, self.kv, self.q, self.k_r, self.v_r, self.r_len, o=self.o, lse=self.lse,
+                      ws=self.ws_f, **kw)
+        return self
+
+    def bwd(self, accumulate=0, block_idx=-1):
+        R.rr_attn_bwd(self.p, self.kv, self.q, self.k_r, self.v_r, self.r_len, self.o, self.lse,
+                      self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate,
+                      block_idx=block_idx, ws=self.ws_b)
+        return self
+
+    def numpy(self):
+        torch.cuda.synchronize()
+        return {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
+
+
+def oracle_member(dense, dtype, k_p, v_p, stacked, kk, rl, tau, rows=None, grads=True):
+    """Oracle of member kk (its first rl rows) in fp64 from the identical stored values."""
+    f = lambda x: as_f64(x, dtype)
+    q, kr, vr, do = (f(stacked[n][kk, :rl]) for n in ("q", "k_r", "v_r", "d_o"))
+    kp, vp = f(k_p), f(v_p)
+    o, lse = dense.attend(q, kp, vp, kr, vr, tau, rows=rows)
+    out = {"o": o, "lse": lse}
+    if grads:
+        out.update(dense.attend_bwd(q, kp, vp, kr, vr, do, tau, rows=rows))
+    return out

@@ -1,0 +1,155 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the header declares,
+and rejects invalid calls on the host before any launch (no GPU needed: every call here
+fails validation, so nothing reaches HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from resident_kv_response_amd import rr_attn as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rr_attn.h")
+FAKE = 0x100000   # a 16-byte aligned stand-in device address; never dereferenced here
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(rr_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(R.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = R.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _prob(**kw):
+    base = dict(P=4096, R_max=256, Hq=4, Hkv=1, d_qk=64, d_v=64, chunk=1024, block=256, tau=0.125,
+                dtype=R.RR_F32)
+    base.update(kw)
+    return R.Problem(**base)
+
+
+def _fwd(p, r_len=(256,), q=FAKE, kv=None, o=FAKE, lse=FAKE, part_o=None, part_lse=None, ws=FAKE,
+         ws_bytes=1 << 40):
+    L = R.lib()
+    kv = kv or R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
+    cp = p.c()
+    arr = (ctypes.c_int32 * len(r_len))(*r_len)
+    rc = L.rr_attn_fwd(ctypes.byref(cp), ctypes.byref(kv), q, FAKE, FAKE, arr, None, o, lse, part_o,
+                       part_lse, None, ws, ws_bytes, None)
+    return rc, L.rr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(Hq=5, Hkv=2), R.RR_E_SHAPE, "multiple"),
+    (dict(P=0), R.RR_E_SHAPE, "P must"),
+    (dict(R_max=0), R.RR_E_SHAPE, "R_max"),
+    (dict(K=0), R.RR_E_SHAPE, "K must"),
+    (dict(K=65), R.RR_E_SHAPE, "K must"),
+    (dict(chunk=0), R.RR_E_SHAPE, "chunk"),
+    (dict(block=0), R.RR_E_SHAPE, "block"),
+    (dict(tau=0.0), R.RR_E_SHAPE, "tau"),
+    (dict(tau=float("inf")), R.RR_E_SHAPE, "tau"),
+    (dict(dtype=7), R.RR_E_SHAPE, "dtype"),
+    (dict(d_qk=96, d_v=96), R.RR_E_UNSUPPORTED, "head dims"),
+    (dict(d_qk=128, d_v=64), R.RR_E_UNSUPPORTED, "head dims"),
+])
+def test_fwd_rejects_bad_problems(kw, code, frag):
+    rc, msg = _fwd(_prob(**kw))
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_fwd_rejects_bad_arguments():
+    p = _prob()
+    assert _fwd(p, r_len=(257,))[0] == R.RR_E_SHAPE
+    assert _fwd(p, r_len=(-1,))[0] == R.RR_E_SHAPE
+    assert _fwd(p, q=None)[0] == R.RR_E_NULL
+    assert _fwd(p, q=FAKE + 2)[0] == R.RR_E_SHAPE          # misaligned
+    assert _fwd(p, o=None)[0] == R.RR_E_NULL                # o without lse
+    assert _fwd(p, o=None, lse=None)[0] == R.RR_E_NULL      # no output at all
+    assert _fwd(p, ws=None)[0] == R.RR_E_WORKSPACE
+    assert _fwd(p, ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_FWD) - 1)[0] == R.RR_E_WORKSPACE
+    bad_kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P + 1, version=0)
+    assert _fwd(p, kv=bad_kv)[0] == R.RR_E_SHAPE
+    null_kv = R.CResident(k_p=None, v_p=FAKE, k_idx=None, P=p.P, version=0)
+    assert _fwd(p, kv=null_kv)[0] == R.RR_E_NULL
+
+
+def test_bwd_rejects_bad_arguments():
+    L = R.lib()
+    p = _prob()
+    cp = p.c()
+    kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
+    arr = (ctypes.c_int32 * 1)(256)
+
+    def call(accumulate=0, block_idx=-1, ws=FAKE, ws_bytes=1 << 40, dq=FAKE):
+        return L.rr_attn_bwd(ctypes.byref(cp), ctypes.byref(kv), FAKE, FAKE, FAKE, arr, None, FAKE,
+                             FAKE, FAKE, dq, FAKE, FAKE, accumulate, block_idx, ws, ws_bytes, None)
+
+    assert call(block_idx=1) == R.RR_E_SHAPE          # one block of 256 rows only
+    assert call(block_idx=-2) == R.RR_E_SHAPE
+    assert call(accumulate=2) == R.RR_E_SHAPE
+    assert call(dq=None) == R.RR_E_NULL
+    assert call(ws=None) == R.RR_E_WORKSPACE
+    assert call(ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_BWD) - 1) == R.RR_E_WORKSPACE
+
+
+def test_merge_rejects_bad_arguments():
+    L = R.lib()
+    assert L.rr_lse_merge(0, 10, 64, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lse_merge(2, -1, 64, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lse_merge(2, 10, 0, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lse_merge(2, 10, 64, None, FAKE, FAKE, FAKE, None) == R.RR_E_NULL
+
+
+def test_workspace_and_parts_formulas():
+    p = _prob(P=2097152, R_max=8192, Hq=24, Hkv=4, d_qk=128, d_v=128, chunk=131072, dtype=R.RR_BF16)
+    assert R.rr_num_parts(p) == 17
+    rows = 8192 * 24
+    up = lambda x: -(-x // 256) * 256
+    assert R.rr_workspace_bytes(p, R.RR_OP_FWD) == up(17 * rows * 128 * 4) + up(17 * rows * 4)
+    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == up(rows * 4) + up(17 * rows * 128 * 4)
+    with pytest.raises(R.RRError):
+        R.rr_workspace_bytes(_prob(Hq=3, Hkv=2), R.RR_OP_FWD)
+
+
+def _accum(G=8, version=5):
+    acc = R.CAccum()
+    seen = (ctypes.c_uint8 * G)()
+    acc.n_bufs = 2
+    acc.buf[0], acc.buf[1] = FAKE, FAKE
+    acc.n[0], acc.n[1] = 100, 50
+    acc.G, acc.version = G, version
+    acc.seen = ctypes.cast(seen, ctypes.POINTER(ctypes.c_uint8))
+    return acc, seen
+
+
+def _accum_call(acc, g, version, n=(100, 50)):
+    L = R.lib()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ns = (ctypes.c_int64 * 2)(*n)
+    return L.rr_grad_accum(ctypes.byref(acc), g, version, ptrs, ns, 1.0, None)
+
+
+def test_accumulator_hazards_are_rejected_before_launch():
+    acc, seen = _accum()
+    assert _accum_call(acc, 8, 5) == R.RR_E_RANGE           # member outside the window
+    assert _accum_call(acc, -1, 5) == R.RR_E_RANGE
+    assert _accum_call(acc, 3, 6) == R.RR_E_STALE           # mixed versions
+    seen[3] = 1                                              # member 3 already accumulated
+    assert _accum_call(acc, 3, 5) == R.RR_E_DUPLICATE       # a retry must not count twice
+    assert bytes(seen) == bytes([0, 0, 0, 1, 0, 0, 0, 0])   # rejections leave the mask alone
+    assert _accum_call(acc, 2, 5, n=(101, 50)) == R.RR_E_SHAPE
+    L = R.lib()
+    assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_E_MISSING
+    assert "member 0" in L.rr_last_error().decode()
+    for g in range(8):
+        seen[g] = 1
+    assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_OK

@@ -1,0 +1,150 @@
+"""GPU invariants of the method (needs an MI355X): chunking and blocking do not change the
+result, the reverse block walk finalises block b at step b, exported partials merged by
+rr_lse_merge equal the fused output, results are bitwise deterministic, the resident
+prompt KV is never written, and serial accumulation equals the sum of replays."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dense
+from resident_kv_response_amd import configs, rr_attn as R, synth
+from tests._helpers import assert_bf16_close
+
+pytestmark = pytest.mark.gpu
+
+W = configs.SHARE_P256K.with_(P=4100, R=520, chunk=1024, block=128, seed=5001)
+
+
+def _setup(w=W, R_list=None, chunk=None, block=None):
+    from tests import _gpu as G
+    R_list = R_list or [w.R]
+    res = synth.resident(w)
+    mem = [synth.member(w, g, R=r) for g, r in enumerate(R_list)]
+    st = G.stack_members(mem, max(R_list))
+    prob = G.problem(w.P, max(R_list), w.Hq, w.Hkv, w.d_qk, chunk or w.chunk, block or w.block,
+                     w.dtype, K=len(R_list), tau=w.tau)
+    return G, res, st, prob, R_list
+
+
+def test_chunk_and_block_invariance():
+    outs = []
+    for chunk, block in [(4100, 520), (1024, 128), (333, 77), (64, 64)]:
+        G, res, st, prob, rl = _setup(chunk=chunk, block=block)
+        print(f"[invariance] chunk={chunk} block={block}", flush=True)
+        outs.append(G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl).fwd().bwd().numpy())
+    for o in outs[1:]:
+        for key in ("o", "dq", "dk", "dv"):
+            assert_bf16_close(key, o[key], outs[0][key])
+
+
+def test_deterministic_and_prompt_untouched():
+    G, res, st, prob, rl = _setup()
+    a = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl)
+    kp0, vp0 = a.k_p.clone(), a.v_p.clone()
+    x = a.fwd().bwd().numpy()
+    y = a.fwd().bwd().numpy()
+    for key in x:
+        np.testing.assert_array_equal(x[key], y[key])
+    assert torch.equal(a.k_p.view(torch.int16), kp0.view(torch.int16))
+    assert torch.equal(a.v_p.view(torch.int16), vp0.view(torch.int16))
+
+
+def test_caller_driven_reverse_walk():
+    G, res, st, prob, rl = _setup()
+    full = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl).fwd().bwd().numpy()
+    run = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl).fwd()
+    run.dq.zero_()
+    run.dk.zero_()
+    run.dv.zero_()
+    nb = -(-W.R // W.block)
+    for b in range(nb - 1, -1, -1):
+        run.bwd(accumulate=1, block_idx=b)
+        now = run.numpy()
+        lo, hi = b * W.block, min(W.R, (b + 1) * W.block)
+        # after step b, the rows of block b are final
+        np.testing.assert_allclose(now["dk"][0, lo:hi], full["dk"][0, lo:hi], rtol=0, atol=1e-6)
+        np.testing.assert_allclose(now["dv"][0, lo:hi], full["dv"][0, lo:hi], rtol=0, atol=1e-6)
+        np.testing.assert_allclose(now["dq"][0, lo:hi], full["dq"][0, lo:hi], rtol=0, atol=1e-6)
+
+
+def test_exported_partials_merge():
+    G, res, st, prob, rl = _setup()
+    run = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl)
+    n_parts = R.rr_num_parts(prob)
+    po = torch.empty((n_parts, 1, W.R, W.Hq, W.d_v), device="cuda", dtype=torch.float32)
+    pl = torch.empty((n_parts, 1, W.R, W.Hq), device="cuda", dtype=torch.float32)
+    run.fwd(part_o=po, part_lse=pl)
+    o2 = torch.empty_like(run.o)
+    l2 = torch.empty_like(run.lse)
+    R.rr_lse_merge(po, pl, o2, l2)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o2.cpu().numpy(), run.o.cpu().numpy(), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(l2.cpu().numpy(), run.lse.cpu().numpy(), rtol=0, atol=1e-6)
+    # per-part statistics against the oracle's chunk partials (rows 0 and R-1)
+    f = lambda x: synth.as_f64(x, W.dtype)
+    rows = np.array([0, 255, W.R - 1])
+    ref_o, ref_l = dense.chunk_partials(f(st["q"][0]), f(res["k_p"]), f(res["v_p"]), f(st["k_r"][0]),
+                                        f(st["v_r"][0]), W.tau, dense.chunk_bounds(W.P, W.chunk), rows=rows)
+    got_o = po.cpu().numpy()[:, 0][:, rows]
+    got_l = pl.cpu().numpy()[:, 0][:, rows]
+    assert_bf16_close("part_o", got_o, ref_o)
+    assert np.max(np.abs(got_l - ref_l)) <= 2e-2
+
+
+def test_merge_handles_empty_parts():
+    po = torch.randn(3, 5, 8, device="cuda")
+    pl = torch.randn(3, 5, device="cuda")
+    pl[1] = float("-inf")
+    pl[:, 4] = float("-inf")
+    o = torch.empty(5, 8, device="cuda")
+    lse = torch.empty(5, device="cuda")
+    R.rr_lse_merge(po, pl, o, lse)
+    ro, rl_ = dense.merge(po.double().cpu().numpy(), pl.double().cpu().numpy())
+    np.testing.assert_allclose(o.cpu().numpy(), ro, atol=1e-6)
+    assert np.isneginf(lse[4].item()) and np.all(o[4].cpu().numpy() == 0)
+    np.testing.assert_allclose(lse.cpu().numpy()[:4], rl_[:4], atol=1e-6)
+
+
+def test_serial_group_accumulation():
+    """G = 8 members replayed one at a time, accumulated into position-aligned fp32
+    buffers; equals the oracle's sum of 8 independent replays.  A retried member is
+    rejected, a stale version is rejected, a missing member is reported."""
+    from tests import _gpu as G
+    w = configs.FULL_P2M.with_(P=2048, R=192, r_min=64, chunk=512, block=64, seed=6001)
+    res = synth.resident(w)
+    lens = synth.response_lengths(w)
+    Rm = w.R
+    acc_dq = torch.zeros(Rm, w.Hq, w.d_qk, device="cuda")
+    acc_dk = torch.zeros(Rm, w.Hkv, w.d_qk, device="cuda")
+    acc_dv = torch.zeros(Rm, w.Hkv, w.d_v, device="cuda")
+    win = R.Accum([acc_dq, acc_dk, acc_dv], G=w.G, version=7)
+    refs = {"dq": [], "dk_r": [], "dv_r": []}
+    peak = []
+    for g in range(w.G):
+        rg = int(lens[g])
+        m = synth.member(w, g, R=rg)
+        st = G.stack_members([m], rg)
+        prob = G.problem(w.P, rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+        run = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [rg], version=7).fwd().bwd()
+        R.rr_grad_accum(win, g, 7, [run.dq[0], run.dk[0], run.dv[0]])
+        if g == 0:
+            with pytest.raises(R.RRError) as e:
+                R.rr_grad_accum(win, 0, 7, [run.dq[0], run.dk[0], run.dv[0]])
+            assert e.value.code == R.RR_E_DUPLICATE
+            with pytest.raises(R.RRError) as e:
+                R.rr_accum_check_complete(win)
+            assert e.value.code == R.RR_E_MISSING
+        if g == 1:
+            with pytest.raises(R.RRError) as e:
+                R.rr_grad_accum(win, 2, 8, [run.dq[0], run.dk[0], run.dv[0]])
+            assert e.value.code == R.RR_E_STALE
+        f = lambda x: synth.as_f64(x, w.dtype)
+        gr = dense.attend_bwd(f(m["q"]), f(res["k_p"]), f(res["v_p"]), f(m["k_r"]), f(m["v_r"]),
+                              f(m["d_o"]), w.tau)
+        for key in refs:
+            refs[key].append(gr[key])
+    R.rr_accum_check_complete(win)
+    torch.cuda.synchronize()
+    assert_bf16_close("acc dq", acc_dq.cpu().numpy(), dense.accumulate(refs["dq"], Rm))
+    assert_bf16_close("acc dk", acc_dk.cpu().numpy(), dense.accumulate(refs["dk_r"], Rm))
+    assert_bf16_close("acc dv", acc_dv.cpu().numpy(), dense.accumulate(refs["dv_r"], Rm))

@@ -1,0 +1,108 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Tolerances: fp32 inputs, max-abs <= 1e-5 on O, lse, dQ, dK, dV; bf16 inputs, rel-L2 <= 5e-3
+and max-abs <= 2e-2 on O, dQ, dK, dV (lse max-abs <= 2e-2).  Padding rows (i >= r_len)
+must hold O = 0, lse = -inf and zero gradients.
+"""
+import numpy as np
+import pytest
+
+from oracle import dense
+from resident_kv_response_amd import configs, synth
+from tests._helpers import assert_bf16_close, assert_f32_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w, members_R):
+    res = synth.resident(w)
+    mem = [synth.member(w, g, R=rg) for g, rg in enumerate(members_R)]
+    return res, mem
+
+
+def _run_and_check(w, members_R, R_max=None, chunk=None, block=None, check_rows=None):
+    from tests import _gpu as G
+    R_max = R_max or max(members_R)
+    chunk = chunk or w.chunk
+    block = block or w.block
+    res, mem = _inputs(w, members_R)
+    st = G.stack_members(mem, R_max)
+    prob = G.problem(w.P, R_max, w.Hq, w.Hkv, w.d_qk, chunk, block, w.dtype, K=len(members_R), tau=w.tau)
+    print(f"[parity] {w.name} K={len(members_R)} R={members_R} chunk={chunk} block={block}", flush=True)
+    run = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, members_R).fwd().bwd()
+    got = run.numpy()
+    for kk, rl in enumerate(members_R):
+        rows = None if check_rows is None else check_rows
+        ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, kk, rl, w.tau, rows=rows)
+        sel = slice(0, rl) if rows is None else rows
+        pairs = [("o", got["o"][kk][sel], ref["o"]), ("dq", got["dq"][kk][sel], ref["dq"])]
+        if rows is None:
+            pairs += [("dk_r", got["dk"][kk][:rl], ref["dk_r"]), ("dv_r", got["dv"][kk][:rl], ref["dv_r"])]
+        for name, a, b in pairs:
+            if w.dtype == "f32":
+                assert_f32_close(f"{name}[k={kk}]", a, b)
+            else:
+                assert_bf16_close(f"{name}[k={kk}]", a, b)
+        lse_tol = 1e-5 if w.dtype == "f32" else 2e-2
+        if rl > 0:
+            assert np.max(np.abs(got["lse"][kk][sel] - ref["lse"])) <= lse_tol
+        # padding rows
+        assert np.all(got["o"][kk][rl:] == 0) and np.all(np.isneginf(got["lse"][kk][rl:]))
+        assert np.all(got["dq"][kk][rl:] == 0)
+        assert np.all(got["dk"][kk][rl:] == 0) and np.all(got["dv"][kk][rl:] == 0)
+    return got
+
+
+def test_tiny_f32_config():
+    w = configs.TINY_F32
+    _run_and_check(w, [w.R])
+
+
+@pytest.mark.parametrize("chunk,block", [(1000, 64), (4096, 100), (4097, 256), (333, 17)])
+def test_tiny_f32_partitions(chunk, block):
+    w = configs.TINY_F32.with_(P=2500, R=200, seed=2001)
+    _run_and_check(w, [w.R], chunk=chunk, block=block)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 8, 2), (128, 12, 2), (128, 4, 4)])
+def test_bf16_multitile_ragged(d, Hq, Hkv):
+    # several row tiles, ragged chunk and block tails, causal response across tiles
+    w = configs.GQA_P128K.with_(P=5000, R=600, Hq=Hq, Hkv=Hkv, d_qk=d, d_v=d, chunk=2048, block=256,
+                                seed=3000 + d + Hq)
+    _run_and_check(w, [w.R])
+
+
+def test_bf16_varlen_microbatch():
+    # K = 4 responses of different lengths in one call, including a one-row and an empty one
+    w = configs.SHARE_P256K.with_(P=3000, R=400, chunk=1024, block=128, seed=4001)
+    _run_and_check(w, [400, 263, 1, 0], R_max=400)
+
+
+def test_f32_varlen_microbatch():
+    w = configs.TINY_F32.with_(P=700, R=90, seed=4002)
+    _run_and_check(w, [90, 33, 0], R_max=96, chunk=256, block=32)
+
+
+@pytest.mark.parametrize("cfg", ["GQA_P128K", "SHARE_P256K"])
+def test_full_size_sampled_rows(cfg):
+    """Full-size configurations: every output of the GPU path is produced; O, lse and dQ of
+    seeded sampled rows (block boundaries included) are compared with the oracle, and
+    dK/dV of the last response keys, whose gradients only rows near the end reach."""
+    from tests import _gpu as G
+    w = getattr(configs, cfg)
+    res, mem = _inputs(w, [w.R])
+    st = G.stack_members(mem, w.R)
+    prob = G.problem(w.P, w.R, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+    print(f"[parity] {w.name} full size", flush=True)
+    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [w.R]).fwd().bwd().numpy()
+    rows = synth.sample_rows(w.seed, w.R, 24, w.block)
+    tail = np.arange(w.R - 8, w.R)
+    rows = np.union1d(rows, tail)
+    ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, 0, w.R, w.tau, rows=rows)
+    assert_bf16_close("o", got["o"][0][rows], ref["o"])
+    assert_bf16_close("dq", got["dq"][0][rows], ref["dq"])
+    assert np.max(np.abs(got["lse"][0][rows] - ref["lse"])) <= 2e-2
+    # response keys j >= R-8 receive gradient only from rows >= R-8, all included above
+    assert_bf16_close("dk_r tail", got["dk"][0][w.R - 8:], ref["dk_r"][w.R - 8:])
+    assert_bf16_close("dv_r tail", got["dv"][0][w.R - 8:], ref["dv_r"][w.R - 8:])
+    assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))
