@@ -1,0 +1,263 @@
+"""Benchmark: response-replay attention fwd + response-only bwd at a 2,097,152-position
+resident prompt (one GPU).
+
+One step = one group of G = 8 members replayed serially (replay microbatch K = 1): for
+each member, rr_attn_fwd (chunk partials + exact merge), rr_attn_bwd (D, dQ partials +
+ordered reduction, reverse block walk for response dK/dV) and rr_grad_accum of dQ, dK, dV
+into position-aligned fp32 accumulators (zeroed at the start of the group).  All inputs
+are synthetic (seeded N(0,1), rounded to bf16) and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step; `roofline` is
+measured live for the kernel with the largest device time, from HIP events the library
+records around every launch in the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="bf16_full_P2097152_G8")
+    ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample rows (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_flops(w, R: int) -> dict:
+    """Algorithmic flops of each launch kind for one member of length R (d_qk = d_v = d).
+    dq_partials: S, dP and dQ over every visible pair; fwd_partials: S and PV over every
+    visible pair; dkdv: dK and dV over the response pairs (the S / dP it recomputes are
+    not counted)."""
+    d, Hq = w.d_qk, w.Hq
+    n_p, n_r = R * w.P, R * (R + 1) // 2
+    return {"fwd_partials": 4.0 * d * Hq * (n_p + n_r),
+            "dq_partials": 6.0 * d * Hq * (n_p + n_r),
+            "dkdv": 4.0 * d * Hq * n_r}
+
+
+def traffic_from_profiles(kernel: str, src_sha: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != src_sha:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch_for_bench_member_mean"])
+    except (KeyError, ValueError):
+        return None
+
+
+def source_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "resident_kv_response_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main() -> int:
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": a.gpus}))
+        return 2
+    import torch
+
+    from resident_kv_response_amd import configs, rr_attn as R, synth
+
+    w = configs.BY_NAME[a.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    lens = synth.response_lengths(w) if w.G > 1 else np.array([w.R])
+    Rmax = int(lens.max())
+
+    t0 = time.time()
+    res = synth.resident(w)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    k_p, v_p = up(res["k_p"]), up(res["v_p"])
+    members = []
+    host_m0 = None
+    for g, rg in enumerate(lens):
+        m = synth.member(w, g, R=int(rg))
+        if g == 0:
+            host_m0 = m
+        members.append({k: up(v)[None] for k, v in m.items()})
+    gen_s = time.time() - t0
+
+    kv = R.resident(k_p, v_p, version=1)
+    pmax = R.Problem(P=w.P, R_max=Rmax, Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v, chunk=w.chunk,
+                     block=w.block, tau=w.tau)
+    ws_f = R.workspace(pmax, R.RR_OP_FWD, dev)
+    ws_b = R.workspace(pmax, R.RR_OP_BWD, dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    o = torch.empty(Rmax, w.Hq, w.d_v, **f32)
+    lse = torch.empty(Rmax, w.Hq, **f32)
+    dq = torch.empty(Rmax, w.Hq, w.d_qk, **f32)
+    dk = torch.empty(Rmax, w.Hkv, w.d_qk, **f32)
+    dv = torch.empty(Rmax, w.Hkv, w.d_v, **f32)
+    acc = [torch.zeros(Rmax, w.Hq, w.d_qk, **f32), torch.zeros(Rmax, w.Hkv, w.d_qk, **f32),
+           torch.zeros(Rmax, w.Hkv, w.d_v, **f32)]
+    probs = [R.Problem(P=w.P, R_max=int(rg), Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v,
+                       chunk=w.chunk, block=w.block, tau=w.tau) for rg in lens]
+
+    def member_pass(g, win=None):
+        rg = int(lens[g])
+        m = members[g]
+        og, lg, dqg, dkg, dvg = o[:rg], lse[:rg], dq[:rg], dk[:rg], dv[:rg]
+        R.rr_attn_fwd(probs[g], kv, m["q"], m["k_r"], m["v_r"], [rg], o=og, lse=lg, ws=ws_f)
+        R.rr_attn_bwd(probs[g], kv, m["q"], m["k_r"], m["v_r"], [rg], og, lg, m["d_o"], dqg, dkg, dvg,
+                      ws=ws_b)
+        if win is not None:
+            R.rr_grad_accum(win, g, 1, [dqg, dkg, dvg])
+
+    def step():
+        for t in acc:
+            t.zero_()
+        win = R.Accum(acc, G=len(lens), version=1)
+        for g in range(len(lens)):
+            member_pass(g, win)
+        R.rr_accum_check_complete(win)
+
+    # parity gate on member 0 (sampled rows, one KV group) before any timing
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    member_pass(0)
+    torch.cuda.synchronize()
+    mem_g1 = torch.cuda.max_memory_allocated()
+    rows = synth.sample_rows(w.seed, int(lens[0]), a.cpu_rows, w.block) if a.cpu_rows > 0 else None
+    got = None
+    if rows is not None:
+        grp = w.Hq // w.Hkv
+        got = {"o": o[rows, :grp].double().cpu().numpy(), "dq": dq[rows, :grp].double().cpu().numpy()}
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    R.rr_profile_begin()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    prof = R.rr_profile_end()
+    mem_g8 = torch.cuda.max_memory_allocated()
+    ms_per_step = (t2 - t1) * 1e3 / a.steps
+
+    flops_step = 0.0
+    per_kernel_flops = {"fwd_partials": 0.0, "dq_partials": 0.0, "dkdv": 0.0}
+    for rg in lens:
+        kf = kernel_flops(w, int(rg))
+        flops_step += configs.flops_dense(w.Hq, w.d_qk, w.d_v, int(rg), w.P)["total"]
+        for k in per_kernel_flops:
+            per_kernel_flops[k] += kf[k]
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    tokens_s = float(lens.sum()) / (ms_per_step * 1e-3)
+
+    # dominant kernel by device time
+    dom = max(prof.items(), key=lambda kv_: kv_[1][1])
+    dom_name, (dom_launches, dom_ms) = dom[0], dom[1]
+    roof = None
+    if dom_name in per_kernel_flops:
+        launches_per_step = dom_launches / a.steps
+        flops_per_launch = per_kernel_flops[dom_name] / launches_per_step
+        avg_ms = dom_ms / dom_launches
+        achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+        src = {"fwd_partials": ["k_fwd_bf16.hip", "k_attn_tile.h", "k_common.h"],
+               "dq_partials": ["k_bwd_bf16.hip", "k_attn_tile.h", "k_common.h"],
+               "dkdv": ["k_bwd_bf16.hip", "k_attn_tile.h", "k_common.h"]}[dom_name]
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profiles(dom_name, source_sha(src)),
+                "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": flops_per_launch}
+    kernels = {k: {"launches_per_step": v[0] / a.steps, "ms_per_step": round(v[1] / a.steps, 3)}
+               for k, v in sorted(prof.items(), key=lambda kv_: -kv_[1][1])}
+    for k in per_kernel_flops:
+        if k in kernels:
+            kernels[k]["tflops"] = round(per_kernel_flops[k] / (kernels[k]["ms_per_step"] * 1e-3) / 1e12, 2)
+    if "lse_merge" in kernels:   # bytes: read n_parts partials (O and lse), write O and lse
+        nb = sum((w.n_chunks + 1) * int(rg) * w.Hq * (w.d_v + 1) * 4 + int(rg) * w.Hq * (w.d_v + 1) * 4
+                 for rg in lens)
+        kernels["lse_merge"]["gbs"] = round(nb / (kernels["lse_merge"]["ms_per_step"] * 1e-3) / 1e9, 1)
+
+    # CPU baseline: the oracle on the machine's host cores, bounded sample of member 0
+    cpu = None
+    parity = None
+    if rows is not None:
+        from oracle import dense
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            blas_threads = None
+        grp = w.Hq // w.Hkv
+        f = lambda x: synth.as_f64(x, w.dtype)
+        kp64, vp64 = f(res["k_p"][:, :1]), f(res["v_p"][:, :1])
+        qs, kr, vr, do = f(host_m0["q"][:, :grp]), f(host_m0["k_r"][:, :1]), f(host_m0["v_r"][:, :1]), \
+            f(host_m0["d_o"][:, :grp])
+        tc = time.perf_counter()
+        ro, _ = dense.attend(qs, kp64, vp64, kr, vr, w.tau, rows=rows)
+        rgr = dense.attend_bwd(qs, kp64, vp64, kr, vr, do, w.tau, rows=rows)
+        cpu_s = time.perf_counter() - tc
+        cpu_flops = sum(grp * 10.0 * w.d_qk * (w.P + int(r) + 1) for r in rows)
+        cores = len(os.sched_getaffinity(0))
+        cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": blas_threads or cores, "kind": "oracle",
+               "sample": f"member 0 (R={int(lens[0])}), {len(rows)} query rows {list(map(int, rows))}, "
+                         f"KV head 0 and its {grp} query heads, fwd + dQ over all {w.P} prompt keys "
+                         f"plus causal response keys; {cpu_s:.1f} s",
+               "host_cpus_affinity": cores, "host_cpu_count": os.cpu_count(),
+               "extrapolated_full_step_s": round(flops_step / (cpu_flops / cpu_s), 1)}
+        rel = lambda x, y: float(np.linalg.norm(x - y) / np.linalg.norm(y))
+        parity = {"rows": len(rows), "o_rel_l2": rel(got["o"], ro), "dq_rel_l2": rel(got["dq"], rgr["dq"]),
+                  "o_max_abs": float(np.abs(got["o"] - ro).max()),
+                  "dq_max_abs": float(np.abs(got["dq"] - rgr["dq"]).max())}
+        parity["pass"] = bool(parity["o_rel_l2"] <= 5e-3 and parity["dq_rel_l2"] <= 5e-3
+                              and parity["o_max_abs"] <= 2e-2 and parity["dq_max_abs"] <= 2e-2)
+
+    out = {
+        "metric": "response-replay attention fwd+bwd TFLOP/s + % bf16 MFMA peak at P=2M",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "P": w.P, "G": len(lens), "R_g": [int(x) for x in lens],
+                   "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk, "chunk": w.chunk, "block": w.block,
+                   "replay_microbatch": 1, "flops_per_step": flops_step},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(tokens_s, 1),
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
+        "peak_mem_bytes": {"after_1_member": int(mem_g1), "timed_G_groups": int(mem_g8)},
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if (parity is None or parity["pass"]) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())
