@@ -7,29 +7,145 @@
 // longstraw-2m-rl, section "Two incompatible architectures, same transaction").
 //
 // Rows: flattened m = r * grp + hh over the grp query heads that read KV head g, so one
-// K/V tile feeds grp heads.  4 waves x 64 rows; each wave keeps its Q fragments and its
+// K/V tile feeds all of them.  4 waves x 64 rows; each wave keeps its Q fragments and its
 // O^T accumulators (d x rows, fp32) in registers for the whole part.
 //
-// Per 64-key stage: K as [key][d] and V transposed as [d][key] in LDS (double-buffered;
-// the next stage's global loads are issued before the current stage's MFMAs).  Per
-// 32-key subtile and 32-row N-tile:  S^T = K Q^T (D/16 MFMAs), base-2 online softmax with
-// a lazy rescale (the reference maximum only moves when a row's maximum grows by more
-// than 2^8, keeping every p <= 256), P^T rounded to bf16, O^T += V^T P^T (D/16 MFMAs).
+// K/V stream: 128-key stages loaded straight from global memory into LDS (no register
+// staging), two buffers, the next stage's loads in flight while the current one is used.
+// Per 32-key subtile and 32-row N-tile: S^T = K Q^T (D/16 MFMAs, K row fragments),
+// base-2 online softmax with a lazy rescale (the reference maximum only moves when a
+// row's maximum grows by more than 2^8, so every p <= 256), P^T rounded to bf16 straight
+// from the C registers, O^T += V^T P^T (D/16 MFMAs, V^T fragments by transposing LDS
+// reads).  The next subtile's S^T MFMAs are issued before the current softmax so the
+// matrix cores and the vector ALUs work at the same time.
 #include "k_attn_tile.h"
+#include "k_lds.h"
 #include "kernels.h"
 
 namespace rr {
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest p between rescales
 
+#ifndef RR_FWD_WAVES
+#define RR_FWD_WAVES 8
+#endif
+#ifndef RR_FWD_NT
+#define RR_FWD_NT 1
+#endif
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void fwd_partials_bf16(
+struct FwdCfg {
+  static constexpr int WAVES = RR_FWD_WAVES;
+  static constexpr int NT = RR_FWD_NT;           // 32-row N-tiles per wave
+  static constexpr int ROWS_W = 32 * NT;
+  static constexpr int BM = WAVES * ROWS_W;      // query rows per workgroup
+  static constexpr int BN = 128;                 // keys per LDS stage
+  static constexpr int NSUB = BN / 32;
+  static constexpr int KS = D / 16, DT = D / 32;
+  static constexpr int TILE = BN * D * 2;        // bytes of one [BN][D] bf16 tile
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void scores_T(const char* Kt, int sub, const bf16x8 (&qf)[NT][D / 16],
+                                         f32x16 (&s)[NT]) {
+  constexpr int KS = D / 16;
+  bf16x8 kf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kf[ks] = frag_rows<D>(Kt, sub * 32, ks);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf[ks], qf[t][ks], s[t]);
+}
+
+template <bool MASK, int D, int NT>
+__device__ __forceinline__ void online_softmax(f32x16 (&s)[NT], const int (&lim)[NT], int rel,
+                                               float c2, float (&m_run)[NT], float (&l_run)[NT],
+                                               f32x16 (&acc)[NT][D / 32], bf16x8 (&pf)[NT][2]) {
+  constexpr int DT = D / 32;
+  const int hl = (threadIdx.x & 63) >> 5;
+  float m_new[NT];
+  bool grow = false;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (MASK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
+        if (key > lim[t]) s[t][i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[t][i]), s[t][i + 1]);
+    mx = fmaxf(mx, s[t][15]);
+    mx = pair_max(mx);
+    m_new[t] = fmaxf(m_run[t], mx * c2);
+    grow |= m_new[t] > m_run[t] + kRescaleThreshold;
+  }
+  if (__any(grow)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float alpha = fast_exp2(m_run[t] - m_new[t]);
+      l_run[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][dt][i] *= alpha;
+      m_run[t] = m_new[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[t][i], c2, -m_run[t]));
+    float ls = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ls += p[i];
+    l_run[t] += ls;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 u;
+      u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
+      u.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
+      u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
+      u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
+      pf[t][h2] = as_bf16x8(u);
+    }
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void pv_accumulate(const char* Vt, int sub, const bf16x8 (&pf)[NT][2],
+                                              f32x16 (&acc)[NT][D / 32]) {
+  constexpr int DT = D / 32;
+  bf16x8 vf[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = frag_trans<D>(Vt, sub * 32 + 16 * h2, 32 * dt);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf[dt][h2], pf[t][h2], acc[t][dt]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
     const uint16_t* __restrict__ v_r, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  using C = TileCfg<D>;
-  constexpr int STAGE = C::NORM_ELEMS + C::TRANS_ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  using C = FwdCfg<D>;
+  constexpr int NT = C::NT, KS = C::KS, DT = C::DT;
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * C::TILE];   // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * C::TILE];
 
   const TileWork w = decode_tile_work(g, C::BM);
   if (!w.ok) return;
@@ -40,7 +156,6 @@ __global__ __launch_bounds__(256, 1) void fwd_partials_bf16(
   const int r_top = (min(m_hi, w.m0 + C::BM) - 1) / g.grp;
   const int rl = g.r_len[w.k];
 
-  // keys of this part
   const bool resp = w.part >= g.n_chunks;
   int64_t key0, key1;
   if (!resp) {
@@ -54,15 +169,24 @@ __global__ __launch_bounds__(256, 1) void fwd_partials_bf16(
   const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
   const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
   const int n_keys = (r_first >= rl) ? 0 : (int)(key1 - key0);
-  const int n_tiles = (n_keys + C::BN - 1) / C::BN;
+  const int n_stages = (n_keys + C::BN - 1) / C::BN;
 
-  // this lane's rows: visibility limit (relative key index) and Q fragments
-  int lim[C::NT];
-  bool valid[C::NT];
-  int64_t orow[C::NT];
-  bf16x8 qf[C::NT][C::KS];
+  const int64_t sb = stride * 2;                  // bytes between consecutive keys
+  const uint16_t* kc = kb + key0 * stride;          // part-relative streams
+  const uint16_t* vc = vb + key0 * stride;
+  DirectLoad<D, C::BN, C::WAVES> dl;
+  dl.init(sb);
+  if (n_stages > 0) {
+    dl.issue(buf0, kc, 0, n_keys, sb);
+    dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
+  }
+
+  int lim[NT];
+  bool valid[NT];
+  int64_t orow[NT];
+  bf16x8 qf[NT][KS];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
+  for (int t = 0; t < NT; ++t) {
     const int m = w.m0 + wave * C::ROWS_W + t * 32 + col;
     const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
     valid[t] = m < m_hi && r < rl;
@@ -70,142 +194,77 @@ __global__ __launch_bounds__(256, 1) void fwd_partials_bf16(
     orow[t] = m < m_hi ? (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h : -1;
     const uint16_t* qrow = q + (((int64_t)w.k * g.R + r) * g.Hq + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       qf[t][ks] = as_bf16x8(valid[t] ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hl * 8)
                                      : make_uint4(0, 0, 0, 0));
   }
-  int wmin = min(lim[0], lim[C::NT - 1]), wmax = max(lim[0], lim[C::NT - 1]);
+  int wmin = min(lim[0], lim[NT - 1]), wmax = max(lim[0], lim[NT - 1]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     wmin = min(wmin, __shfl_xor(wmin, off, 64));
     wmax = max(wmax, __shfl_xor(wmax, off, 64));
   }
 
-  f32x16 acc[C::NT][C::DT];
-  float m_run[C::NT], l_run[C::NT];
+  f32x16 acc[NT][DT];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
+  for (int t = 0; t < NT; ++t) {
     m_run[t] = kNegBig;
     l_run[t] = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][dt][i] = 0.0f;
   }
 
-  RowPieces<D, C::PIECES_PER_THREAD> kreg;
-  QuadPieces<D, C::QUADS_PER_THREAD> vreg;
-  if (n_tiles > 0) {
-    load_pieces<D>(kreg, kb, key0, key0 + n_keys, stride);
-    load_quads<D>(vreg, vb, key0, key0 + n_keys, stride);
-    store_pieces<D>(kreg, lds);
-    store_quads_transposed<D>(vreg, lds + C::NORM_ELEMS);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) {
-      const int64_t nk0 = key0 + (int64_t)(it + 1) * C::BN;
-      load_pieces<D>(kreg, kb, nk0, key0 + n_keys, stride);
-      load_quads<D>(vreg, vb, nk0, key0 + n_keys, stride);
-    }
-    const uint16_t* Ks = lds + (it & 1) * STAGE;
-    const uint16_t* Vt = Ks + C::NORM_ELEMS;
-#pragma unroll
-    for (int sub = 0; sub < C::BN / 32; ++sub) {
-      const int rel = it * C::BN + sub * 32;
-      if (rel > wmax) continue;            // every row of this wave is past its last key
-      f32x16 s[C::NT];
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (sub * 32 + col) * C::ROW + ks * 16 + hl * 8));
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) s[t] = mfma32x32x16(a, qf[t][ks], s[t]);
-      }
-      const bool need_mask = rel + 31 > wmin;
-      bool grow = false;
-      float m_new[C::NT];
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[t][i] * g.c2;
-          if (need_mask) {
-            const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key > lim[t]) x = -INFINITY;
-          }
-          s[t][i] = x;
-          mx = fmaxf(mx, x);
-        }
-        mx = fmaxf(mx, partner32(mx));
-        m_new[t] = fmaxf(m_run[t], mx);
-        grow |= m_new[t] > m_run[t] + kRescaleThreshold;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
-          const float alpha = fast_exp2(m_run[t] - m_new[t]);
-          l_run[t] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[t][dt][i] *= alpha;
-          m_run[t] = m_new[t];
-        }
-      }
-      bf16x8 pf[C::NT][2];
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(s[t][i] - m_run[t]);
-          l_run[t] += p[i];
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint4 u;
-          u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
-          u.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
-          u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
-          u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
-          pf[t][h2] = as_bf16x8(u);
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 a = as_bf16x8(
-              *reinterpret_cast<const uint4*>(Vt + (dt * 32 + col) * C::TROW + sub * 32 + h2 * 16 + hl * 8));
-#pragma unroll
-          for (int t = 0; t < C::NT; ++t) acc[t][dt] = mfma32x32x16(a, pf[t][h2], acc[t][dt]);
-        }
-      }
-    }
-    if (it + 1 < n_tiles) {
-      uint16_t* nxt = lds + ((it + 1) & 1) * STAGE;
-      store_pieces<D>(kreg, nxt);
-      store_quads_transposed<D>(vreg, nxt + C::NORM_ELEMS);
-    }
+  // one stage: wait for its loads, prefetch the next stage into the other buffer, then
+  // four 32-key subtiles with the next subtile's scores issued ahead of the softmax
+  auto stage = [&](const char* cur, char* nxt, int it) {
+    wait_vmcnt0();
     __syncthreads();
+    if (it + 1 < n_stages) {
+      const int64_t nk0 = (int64_t)(it + 1) * C::BN;
+      dl.issue(nxt, kc, nk0, n_keys, sb);
+      dl.issue(nxt + C::TILE, vc, nk0, n_keys, sb);
+    }
+    const char* Kt = cur;
+    const char* Vt = cur + C::TILE;
+    const int rel0 = it * C::BN;
+    if (rel0 > wmax) return;
+    f32x16 s_cur[NT];
+    scores_T<D, NT>(Kt, 0, qf, s_cur);
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const int rel = rel0 + sub * 32;
+      const bool has_next = sub + 1 < C::NSUB && rel + 32 <= wmax;
+      f32x16 s_next[NT];
+      if (has_next) scores_T<D, NT>(Kt, sub + 1, qf, s_next);
+      bf16x8 pf[NT][2];
+      if (rel + 31 > wmin)
+        online_softmax<true, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
+      else
+        online_softmax<false, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
+      pv_accumulate<D, NT>(Vt, sub, pf, acc);
+      if (!has_next) break;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s_cur[t] = s_next[t];
+    }
+  };
+
+  for (int it = 0; it < n_stages; it += 2) {
+    stage(buf0, buf1, it);
+    if (it + 1 < n_stages) stage(buf1, buf0, it + 1);
   }
 
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-    const float l = l_run[t] + partner32(l_run[t]);
+  for (int t = 0; t < NT; ++t) {
+    const float l = pair_sum(l_run[t]);
     if (orow[t] < 0) continue;
     const bool live = valid[t] && l > 0.0f;
     const float inv = live ? 1.0f / l : 0.0f;
     float* dst = part_o + orow[t] * D;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d0 = dt * 32 + i4 * 8 + hl * 4;
@@ -218,9 +277,9 @@ __global__ __launch_bounds__(256, 1) void fwd_partials_bf16(
 }
 
 hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
-  const int64_t n = tile_work_count(g, TileCfg<128>::BM);
+  const int64_t n = tile_work_count(g, FwdCfg<128>::BM);
   if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)xcd_grid(n)), block(256);
+  const dim3 grid((unsigned)xcd_grid(n)), block(64 * FwdCfg<128>::WAVES);
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r;
   if (g.dqk == 64)

@@ -1,0 +1,131 @@
+// LDS staging for the bf16 MFMA attention kernels (gfx950): direct global->LDS loads of
+// row-major [rows][D] bf16 tiles with an XOR swizzle, and the two fragment reads the
+// kernels need from such a tile.
+//
+// Swizzle: a row is D/8 16-byte granules; logical granule g of row r is stored at
+// granule g ^ (r & 7).  Rows are not padded, so a wave-wide direct load (64 lanes x 16
+// bytes, stored at consecutive LDS addresses) fills whole rows, and the reads below touch
+// different banks for the rows a lane group reads together.
+//
+// Fragment reads (lane l, h = l / 32, wave64):
+//   row fragment     A[m][k] = T[row0 + l%32][16*ks + 8h .. +8]      one ds_read_b128
+//   transposed frag  A[m][k] = T[row(k)][col0 + l%32], 8 rows per lane  two ds_read_b64_tr_b16
+// ds_read_b64_tr_b16 semantics (gfx950): in each 16-lane group, result lane r, element j
+// is element (r % 4) of the 64-bit chunk addressed by lane 4j + r/4 of the group.  If lane
+// i of the group addresses T[base + i/4][c0 + 4(i%4) .. +4], result lane r gets
+// T[base + j][c0 + r] for j = 0..3: four consecutive rows of its own column.
+#pragma once
+
+#include "k_common.h"
+
+namespace rr {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int D>
+struct Swz {
+  static constexpr int G = D / 8;        // granules per row
+  static constexpr int ROW_BYTES = D * 2;
+  // byte offset of logical granule g of row r
+  static __device__ __forceinline__ int off(int r, int g) { return r * ROW_BYTES + ((g ^ (r & 7)) << 4); }
+};
+
+// Direct loads of a [N_ROWS][D] tile.  Row r of the tile comes from byte offset
+// r * stride_bytes of `src` (a wave-uniform base, so the load takes a scalar base plus a
+// 32-bit lane offset).  Each of the workgroup's waves issues PER_WAVE wave-wide loads of
+// 64 x 16 bytes, which land at consecutive LDS addresses.
+template <int D, int N_ROWS, int WAVES>
+struct DirectLoad {
+  static constexpr int G = D / 8;                       // granules per row
+  static constexpr int RPI = 64 / G;                    // rows per wave instruction
+  static constexpr int GRAN = N_ROWS * G;
+  static constexpr int PER_WAVE = GRAN / (64 * WAVES);
+  static_assert(GRAN % (64 * WAVES) == 0, "tile must split evenly over the waves");
+  static_assert(RPI == 4 || RPI == 8, "D must be 128 or 64");
+
+  uint32_t voff[2];     // lane byte offsets for even / odd instructions (row within the
+                        // instruction and swizzled granule)
+  int row0;             // first tile row of this wave
+
+  __device__ __forceinline__ void init(int64_t stride_bytes) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    row0 = wave * PER_WAVE * RPI;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int r = row0 + RPI * par + lane / G;
+      const int g = (lane % G) ^ (r & 7);
+      voff[par] = (uint32_t)((lane / G) * stride_bytes + g * 16);
+    }
+  }
+  // tile rows [0, N_ROWS) <- rows src_row0 .. of the stream; rows at or past row_end are
+  // redirected to row_end - 1 (their values are masked by the caller).  Requires
+  // src_row0 < row_end.
+  __device__ __forceinline__ void issue(char* tile, const uint16_t* stream, int64_t src_row0,
+                                        int64_t row_end, int64_t stride_bytes) const {
+    const int lane = threadIdx.x & 63;
+    const char* sbytes = reinterpret_cast<const char*>(stream);
+    const bool full = src_row0 + N_ROWS <= row_end;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int p0 = (row0 / RPI + i) * 64;           // first granule of this instruction
+      const int64_t r_first = src_row0 + row0 + RPI * i;
+      const char* gp;
+      if (full) {
+        gp = sbytes + r_first * stride_bytes + voff[i & 1];
+      } else {
+        const int r_lane = lane / G;
+        const int64_t row = min(r_first + r_lane, row_end - 1);
+        const uint32_t gran = voff[i & 1] - (uint32_t)(r_lane * stride_bytes);   // g * 16
+        gp = sbytes + row * stride_bytes + gran;
+      }
+      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(tile + p0 * 16), 16, 0, 0);
+    }
+  }
+};
+
+// Row fragment: lane holds T[row0 + l%32][16*ks + 8h .. +8].
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows(const char* tile, int row0, int ks) {
+  const int lane = threadIdx.x & 63;
+  const int r = row0 + (lane & 31);
+  const int g = 2 * ks + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + Swz<D>::off(r, g));
+}
+
+// Transposed fragment: A[m][k] = T[row(k)][col0 + l%32] with k-slots 0..3 <- rows
+// base + 4h + 0..3 and k-slots 4..7 <- rows base + 8 + 4h + 0..3 (h = l/32).  This is the
+// key order of the MFMA C layout, so the fragment pairs with P^T / dS^T taken straight
+// from the C registers of a 32x32 score tile.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_trans(const char* tile, int base, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
+  const int r = base + 4 * h + (i >> 2);
+  const int c = col0 + 16 * (grp & 1) + 4 * (i & 3);     // element column of this lane's chunk
+  const int g = c >> 3, within = (c & 7) * 2;
+  const char* p0 = tile + Swz<D>::off(r, g) + within;
+  const char* p1 = tile + Swz<D>::off(r + 8, g) + within;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// s_waitcnt vmcnt(0) leaving the other counters alone (gfx9 encoding).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// max of a value over lanes l and l ^ 32
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace rr
