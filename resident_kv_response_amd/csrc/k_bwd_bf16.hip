@@ -18,19 +18,80 @@
 // dV^T += dO^T P, dK^T += Q^T dS, then adds its result into dk_r / dv_r.  Launched once
 // per block, last block first.
 #include "k_attn_tile.h"
+#include "k_lds.h"
 #include "kernels.h"
 
 namespace rr {
 
+#ifndef RR_DQ_WAVES
+#define RR_DQ_WAVES 8
+#endif
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void dq_partials_bf16(
+struct DqCfg {
+  static constexpr int WAVES = RR_DQ_WAVES;
+  static constexpr int BM = WAVES * 32;          // query rows per workgroup (32 per wave)
+  static constexpr int BN = 128;                 // keys per LDS stage
+  static constexpr int NSUB = BN / 32;
+  static constexpr int KS = D / 16, DT = D / 32;
+  static constexpr int TILE = BN * D * 2;
+};
+
+// One 32-key subtile of the dQ accumulation for this wave's 32 rows.
+template <bool MASK, int D>
+__device__ __forceinline__ void dq_subtile(const char* Kt, const char* Vt, int sub, int rel, int lim,
+                                           float c2, float lse2, float dvv,
+                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&of)[D / 16],
+                                           f32x16 (&acc)[D / 32]) {
+  constexpr int KS = D / 16, DT = D / 32;
+  const int hl = (threadIdx.x & 63) >> 5;
+  f32x16 s, dp;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 ak = frag_rows<D>(Kt, sub * 32, ks);
+    const bf16x8 av = frag_rows<D>(Vt, sub * 32, ks);
+    s = mfma32x32x16(ak, qf[ks], s);
+    dp = mfma32x32x16(av, of[ks], dp);
+  }
+  float ds[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float p = fast_exp2(fmaf(s[i], c2, -lse2));
+    if (MASK) {
+      const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
+      if (key > lim) p = 0.0f;
+    }
+    ds[i] = p * (dp[i] - dvv);
+  }
+  bf16x8 dsf[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    uint4 u;
+    u.x = pack_bf16x2(ds[8 * h2 + 0], ds[8 * h2 + 1]);
+    u.y = pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]);
+    u.z = pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]);
+    u.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
+    dsf[h2] = as_bf16x8(u);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      acc[dt] = mfma32x32x16(frag_trans<D>(Kt, sub * 32 + 16 * h2, 32 * dt), dsf[h2], acc[dt]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
     const uint16_t* __restrict__ v_r, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ Dvec, float* __restrict__ dq_part) {
-  using C = TileCfg<D>;
-  constexpr int STAGE = 2 * C::NORM_ELEMS + C::TRANS_ELEMS;   // K, V plain + K transposed
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  using C = DqCfg<D>;
+  constexpr int KS = C::KS, DT = C::DT;
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * C::TILE];   // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * C::TILE];
 
   const TileWork w = decode_tile_work(g, C::BM);
   if (!w.ok) return;
@@ -54,145 +115,83 @@ __global__ __launch_bounds__(256, 1) void dq_partials_bf16(
   const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
   const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
   const int n_keys = (r_first >= rl) ? 0 : (int)(key1 - key0);
-  const int n_tiles = (n_keys + C::BN - 1) / C::BN;
-
-  int lim[C::NT];
-  bool valid[C::NT];
-  int64_t orow[C::NT];
-  float lse2[C::NT], dv_[C::NT];
-  bf16x8 qf[C::NT][C::KS], of[C::NT][C::KS];
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-    const int m = w.m0 + wave * C::ROWS_W + t * 32 + col;
-    const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
-    valid[t] = m < m_hi && r < rl;
-    lim[t] = resp ? min(r, n_keys - 1) : n_keys - 1;
-    const int64_t row = ((int64_t)w.k * g.R + r) * g.Hq + h;
-    orow[t] = m < m_hi ? ((int64_t)w.part * g.K * g.R * g.Hq + row) : -1;
-    lse2[t] = valid[t] ? lse[row] * kLog2e : INFINITY;
-    dv_[t] = valid[t] ? Dvec[row] : 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      qf[t][ks] = as_bf16x8(valid[t] ? *reinterpret_cast<const uint4*>(q + row * D + ks * 16 + hl * 8)
-                                     : make_uint4(0, 0, 0, 0));
-      of[t][ks] = as_bf16x8(valid[t] ? *reinterpret_cast<const uint4*>(d_o + row * D + ks * 16 + hl * 8)
-                                     : make_uint4(0, 0, 0, 0));
-    }
+  const int n_stages = (n_keys + C::BN - 1) / C::BN;
+  const int64_t sb = stride * 2;
+  const uint16_t* kc = kb + key0 * stride;
+  const uint16_t* vc = vb + key0 * stride;
+  DirectLoad<D, C::BN, C::WAVES> dl;
+  dl.init(sb);
+  if (n_stages > 0) {
+    dl.issue(buf0, kc, 0, n_keys, sb);
+    dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
   }
-  int wmin = min(lim[0], lim[C::NT - 1]), wmax = max(lim[0], lim[C::NT - 1]);
+
+  const int m = w.m0 + wave * 32 + col;
+  const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
+  const bool valid = m < m_hi && r < rl;
+  const int lim = resp ? min(r, n_keys - 1) : n_keys - 1;
+  const int64_t row = ((int64_t)w.k * g.R + r) * g.Hq + h;
+  const int64_t orow = m < m_hi ? ((int64_t)w.part * g.K * g.R * g.Hq + row) : -1;
+  const float lse2 = valid ? lse[row] * kLog2e : INFINITY;
+  const float dvv = valid ? Dvec[row] : 0.0f;
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(q + row * D + ks * 16 + hl * 8)
+                             : make_uint4(0, 0, 0, 0));
+    of[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(d_o + row * D + ks * 16 + hl * 8)
+                             : make_uint4(0, 0, 0, 0));
+  }
+  int wmin = lim, wmax = lim;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     wmin = min(wmin, __shfl_xor(wmin, off, 64));
     wmax = max(wmax, __shfl_xor(wmax, off, 64));
   }
 
-  f32x16 acc[C::NT][C::DT];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][dt][i] = 0.0f;
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
 
-  QuadPieces<D, C::QUADS_PER_THREAD> kreg;
-  RowPieces<D, C::PIECES_PER_THREAD> vreg;
-  if (n_tiles > 0) {
-    load_quads<D>(kreg, kb, key0, key0 + n_keys, stride);
-    load_pieces<D>(vreg, vb, key0, key0 + n_keys, stride);
-    store_quads_plain<D>(kreg, lds);
-    store_pieces<D>(vreg, lds + C::NORM_ELEMS);
-    store_quads_transposed<D>(kreg, lds + 2 * C::NORM_ELEMS);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) {
-      const int64_t nk0 = key0 + (int64_t)(it + 1) * C::BN;
-      load_quads<D>(kreg, kb, nk0, key0 + n_keys, stride);
-      load_pieces<D>(vreg, vb, nk0, key0 + n_keys, stride);
-    }
-    const uint16_t* Ks = lds + (it & 1) * STAGE;
-    const uint16_t* Vs = Ks + C::NORM_ELEMS;
-    const uint16_t* Kt = Ks + 2 * C::NORM_ELEMS;
-#pragma unroll
-    for (int sub = 0; sub < C::BN / 32; ++sub) {
-      const int rel = it * C::BN + sub * 32;
-      if (rel > wmax) continue;
-      f32x16 s[C::NT], dp[C::NT];
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[t][i] = dp[t][i] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int off = (sub * 32 + col) * C::ROW + ks * 16 + hl * 8;
-        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + off));
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + off));
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
-          s[t] = mfma32x32x16(ak, qf[t][ks], s[t]);
-          dp[t] = mfma32x32x16(av, of[t][ks], dp[t]);
-        }
-      }
-      const bool need_mask = rel + 31 > wmin;
-      bf16x8 dsf[C::NT][2];
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        float ds[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(s[t][i] * g.c2 - lse2[t]);
-          if (need_mask) {
-            const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key > lim[t]) p = 0.0f;
-          }
-          ds[i] = p * (dp[t][i] - dv_[t]);
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint4 u;
-          u.x = pack_bf16x2(ds[8 * h2 + 0], ds[8 * h2 + 1]);
-          u.y = pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]);
-          u.z = pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]);
-          u.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
-          dsf[t][h2] = as_bf16x8(u);
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 a = as_bf16x8(
-              *reinterpret_cast<const uint4*>(Kt + (dt * 32 + col) * C::TROW + sub * 32 + h2 * 16 + hl * 8));
-#pragma unroll
-          for (int t = 0; t < C::NT; ++t) acc[t][dt] = mfma32x32x16(a, dsf[t][h2], acc[t][dt]);
-        }
-      }
-    }
-    if (it + 1 < n_tiles) {
-      uint16_t* nxt = lds + ((it + 1) & 1) * STAGE;
-      store_quads_plain<D>(kreg, nxt);
-      store_pieces<D>(vreg, nxt + C::NORM_ELEMS);
-      store_quads_transposed<D>(kreg, nxt + 2 * C::NORM_ELEMS);
-    }
+  auto stage = [&](const char* cur, char* nxt, int it) {
+    wait_vmcnt0();
     __syncthreads();
+    if (it + 1 < n_stages) {
+      const int64_t nk0 = (int64_t)(it + 1) * C::BN;
+      dl.issue(nxt, kc, nk0, n_keys, sb);
+      dl.issue(nxt + C::TILE, vc, nk0, n_keys, sb);
+    }
+    const char* Kt = cur;
+    const char* Vt = cur + C::TILE;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const int rel = it * C::BN + sub * 32;
+      if (rel > wmax) break;
+      if (rel + 31 > wmin)
+        dq_subtile<true, D>(Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+      else
+        dq_subtile<false, D>(Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+    }
+  };
+  for (int it = 0; it < n_stages; it += 2) {
+    stage(buf0, buf1, it);
+    if (it + 1 < n_stages) stage(buf1, buf0, it + 1);
   }
 
+  if (orow < 0) return;
+  const float sc = valid ? g.tau : 0.0f;
+  float* dst = dq_part + orow * D;
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-    if (orow[t] < 0) continue;
-    const float sc = valid[t] ? g.tau : 0.0f;
-    float* dst = dq_part + orow[t] * D;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = dt * 32 + i4 * 8 + hl * 4;
-        *reinterpret_cast<float4*>(dst + d0) =
-            make_float4(acc[t][dt][4 * i4 + 0] * sc, acc[t][dt][4 * i4 + 1] * sc,
-                        acc[t][dt][4 * i4 + 2] * sc, acc[t][dt][4 * i4 + 3] * sc);
-      }
-  }
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = dt * 32 + i4 * 8 + hl * 4;
+      *reinterpret_cast<float4*>(dst + d0) =
+          make_float4(acc[dt][4 * i4 + 0] * sc, acc[dt][4 * i4 + 1] * sc, acc[dt][4 * i4 + 2] * sc,
+                      acc[dt][4 * i4 + 3] * sc);
+    }
 }
 
 // ---- response dK / dV --------------------------------------------------------------------
@@ -437,9 +436,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
 }
 
 hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
-  const int64_t n = tile_work_count(g, TileCfg<128>::BM);
+  const int64_t n = tile_work_count(g, DqCfg<128>::BM);
   if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)xcd_grid(n)), block(256);
+  const dim3 grid((unsigned)xcd_grid(n)), block(64 * DqCfg<128>::WAVES);
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r, *dO = (const uint16_t*)a.d_o;
   if (g.dqk == 64)
