@@ -39,7 +39,8 @@ struct DqCfg {
 
 // One 32-key subtile of the dQ accumulation for this wave's 32 rows.
 template <bool MASK, int D>
-__device__ __forceinline__ void dq_subtile(const char* Kt, const char* Vt, int sub, int rel, int lim,
+__device__ __forceinline__ void dq_subtile(const Frag<D>& fr, const char* Kt, const char* Vt, int sub,
+                                           int rel, int lim,
                                            float c2, float lse2, float dvv,
                                            const bf16x8 (&qf)[D / 16], const bf16x8 (&of)[D / 16],
                                            f32x16 (&acc)[D / 32]) {
@@ -48,13 +49,15 @@ __device__ __forceinline__ void dq_subtile(const char* Kt, const char* Vt, int s
   f32x16 s, dp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+  prio_mfma();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 ak = frag_rows<D>(Kt, sub * 32, ks);
-    const bf16x8 av = frag_rows<D>(Vt, sub * 32, ks);
+    const bf16x8 ak = fr.row(Kt, sub, ks);
+    const bf16x8 av = fr.row(Vt, sub, ks);
     s = mfma32x32x16(ak, qf[ks], s);
     dp = mfma32x32x16(av, of[ks], dp);
   }
+  prio_valu();
   float ds[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -75,11 +78,13 @@ __device__ __forceinline__ void dq_subtile(const char* Kt, const char* Vt, int s
     u.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
     dsf[h2] = as_bf16x8(u);
   }
+  prio_mfma();
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
-      acc[dt] = mfma32x32x16(frag_trans<D>(Kt, sub * 32 + 16 * h2, 32 * dt), dsf[h2], acc[dt]);
+      acc[dt] = mfma32x32x16(fr.trans_frag(Kt, sub, h2, dt), dsf[h2], acc[dt]);
+  prio_valu();
 }
 
 template <int D>
@@ -125,6 +130,8 @@ __global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
     dl.issue(buf0, kc, 0, n_keys, sb);
     dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
   }
+  Frag<D> fr;
+  fr.init();
 
   const int m = w.m0 + wave * 32 + col;
   const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
@@ -170,9 +177,9 @@ __global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
       const int rel = it * C::BN + sub * 32;
       if (rel > wmax) break;
       if (rel + 31 > wmin)
-        dq_subtile<true, D>(Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+        dq_subtile<true, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
       else
-        dq_subtile<false, D>(Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+        dq_subtile<false, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
     }
   };
   for (int it = 0; it < n_stages; it += 2) {

@@ -22,13 +22,27 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Round-to-nearest-even fp32 pair -> packed bf16x2 (v_cvt_pk_bf16_f32 on gfx950).
+// Round-to-nearest-even fp32 pair -> packed bf16x2: one v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  uint16_t ua = __builtin_bit_cast(uint16_t, a);
-  uint16_t ub = __builtin_bit_cast(uint16_t, b);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Wave priority around matrix-core blocks: with two waves per SIMD, the wave that has
+// MFMAs to issue goes first, and the other wave's vector work fills the matrix core's
+// busy cycles.  The scheduling barriers keep the compiler from moving instructions
+// across the priority changes.
+__device__ __forceinline__ void prio_mfma() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void prio_valu() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // 16-byte vector <-> 8 bf16 MFMA operand.

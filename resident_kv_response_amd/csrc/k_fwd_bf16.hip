@@ -46,20 +46,22 @@ struct FwdCfg {
 };
 
 template <int D, int NT>
-__device__ __forceinline__ void scores_T(const char* Kt, int sub, const bf16x8 (&qf)[NT][D / 16],
-                                         f32x16 (&s)[NT]) {
+__device__ __forceinline__ void scores_T(const Frag<D>& fr, const char* Kt, int sub,
+                                         const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
   constexpr int KS = D / 16;
   bf16x8 kf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kf[ks] = frag_rows<D>(Kt, sub * 32, ks);
+  for (int ks = 0; ks < KS; ++ks) kf[ks] = fr.row(Kt, sub, ks);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+  prio_mfma();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf[ks], qf[t][ks], s[t]);
+  prio_valu();
 }
 
 template <bool MASK, int D, int NT>
@@ -121,20 +123,22 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[NT], const int (&lim)
 }
 
 template <int D, int NT>
-__device__ __forceinline__ void pv_accumulate(const char* Vt, int sub, const bf16x8 (&pf)[NT][2],
-                                              f32x16 (&acc)[NT][D / 32]) {
+__device__ __forceinline__ void pv_accumulate(const Frag<D>& fr, const char* Vt, int sub,
+                                              const bf16x8 (&pf)[NT][2], f32x16 (&acc)[NT][D / 32]) {
   constexpr int DT = D / 32;
   bf16x8 vf[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = frag_trans<D>(Vt, sub * 32 + 16 * h2, 32 * dt);
+    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = fr.trans_frag(Vt, sub, h2, dt);
+  prio_mfma();
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf[dt][h2], pf[t][h2], acc[t][dt]);
+  prio_valu();
 }
 
 template <int D>
@@ -176,6 +180,8 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
   const uint16_t* vc = vb + key0 * stride;
   DirectLoad<D, C::BN, C::WAVES> dl;
   dl.init(sb);
+  Frag<D> fr;
+  fr.init();
   if (n_stages > 0) {
     dl.issue(buf0, kc, 0, n_keys, sb);
     dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
@@ -232,19 +238,19 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
     const int rel0 = it * C::BN;
     if (rel0 > wmax) return;
     f32x16 s_cur[NT];
-    scores_T<D, NT>(Kt, 0, qf, s_cur);
+    scores_T<D, NT>(fr, Kt, 0, qf, s_cur);
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub) {
       const int rel = rel0 + sub * 32;
       const bool has_next = sub + 1 < C::NSUB && rel + 32 <= wmax;
       f32x16 s_next[NT];
-      if (has_next) scores_T<D, NT>(Kt, sub + 1, qf, s_next);
+      if (has_next) scores_T<D, NT>(fr, Kt, sub + 1, qf, s_next);
       bf16x8 pf[NT][2];
       if (rel + 31 > wmin)
         online_softmax<true, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
       else
         online_softmax<false, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
-      pv_accumulate<D, NT>(Vt, sub, pf, acc);
+      pv_accumulate<D, NT>(fr, Vt, sub, pf, acc);
       if (!has_next) break;
 #pragma unroll
       for (int t = 0; t < NT; ++t) s_cur[t] = s_next[t];

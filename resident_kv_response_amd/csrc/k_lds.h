@@ -3,9 +3,12 @@
 // kernels need from such a tile.
 //
 // Swizzle: a row is D/8 16-byte granules; logical granule g of row r is stored at
-// granule g ^ (r & 7).  Rows are not padded, so a wave-wide direct load (64 lanes x 16
-// bytes, stored at consecutive LDS addresses) fills whole rows, and the reads below touch
-// different banks for the rows a lane group reads together.
+// granule g ^ f(r).  Rows are not padded, so a wave-wide direct load (64 lanes x 16 bytes,
+// stored at consecutive LDS addresses) fills whole rows.  With D = 128 a row spans all 64
+// banks, and f(r) = ((r & 3) << 2) | ((r >> 2) & 3) is a bijection on r mod 16: the 16
+// consecutive rows of a 128-bit row-fragment read land on 16 different granules, and the
+// four consecutive rows x four granules of a half-wave transposing read cover all 16
+// granules once.  With D = 64 two rows share the 64 banks and f(r) = (r >> 1) & 7.
 //
 // Fragment reads (lane l, h = l / 32, wave64):
 //   row fragment     A[m][k] = T[row0 + l%32][16*ks + 8h .. +8]      one ds_read_b128
@@ -28,8 +31,11 @@ template <int D>
 struct Swz {
   static constexpr int G = D / 8;        // granules per row
   static constexpr int ROW_BYTES = D * 2;
+  static __device__ __forceinline__ int f(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
+  }
   // byte offset of logical granule g of row r
-  static __device__ __forceinline__ int off(int r, int g) { return r * ROW_BYTES + ((g ^ (r & 7)) << 4); }
+  static __device__ __forceinline__ int off(int r, int g) { return r * ROW_BYTES + ((g ^ f(r)) << 4); }
 };
 
 // Direct loads of a [N_ROWS][D] tile.  Row r of the tile comes from byte offset
@@ -44,18 +50,19 @@ struct DirectLoad {
   static constexpr int PER_WAVE = GRAN / (64 * WAVES);
   static_assert(GRAN % (64 * WAVES) == 0, "tile must split evenly over the waves");
   static_assert(RPI == 4 || RPI == 8, "D must be 128 or 64");
+  static_assert((PER_WAVE * RPI) % 16 == 0, "each wave's first row must be a multiple of 16");
 
-  uint32_t voff[2];     // lane byte offsets for even / odd instructions (row within the
-                        // instruction and swizzled granule)
+  uint32_t voff[4];     // lane byte offsets by instruction index mod 4 (row within the
+                        // instruction and swizzled granule; the swizzle depends on r mod 16)
   int row0;             // first tile row of this wave
 
   __device__ __forceinline__ void init(int64_t stride_bytes) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     row0 = wave * PER_WAVE * RPI;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
+    for (int par = 0; par < 4; ++par) {
       const int r = row0 + RPI * par + lane / G;
-      const int g = (lane % G) ^ (r & 7);
+      const int g = (lane % G) ^ Swz<D>::f(r);
       voff[par] = (uint32_t)((lane / G) * stride_bytes + g * 16);
     }
   }
@@ -73,11 +80,11 @@ struct DirectLoad {
       const int64_t r_first = src_row0 + row0 + RPI * i;
       const char* gp;
       if (full) {
-        gp = sbytes + r_first * stride_bytes + voff[i & 1];
+        gp = sbytes + r_first * stride_bytes + voff[i & 3];
       } else {
         const int r_lane = lane / G;
         const int64_t row = min(r_first + r_lane, row_end - 1);
-        const uint32_t gran = voff[i & 1] - (uint32_t)(r_lane * stride_bytes);   // g * 16
+        const uint32_t gran = voff[i & 3] - (uint32_t)(r_lane * stride_bytes);   // g * 16
         gp = sbytes + row * stride_bytes + gran;
       }
       __builtin_amdgcn_global_load_lds(gp, (lds_void*)(tile + p0 * 16), 16, 0, 0);
@@ -85,34 +92,53 @@ struct DirectLoad {
   }
 };
 
-// Row fragment: lane holds T[row0 + l%32][16*ks + 8h .. +8].
+// Fragment reads from a swizzled [rows][D] tile.  Every read address is a per-lane
+// offset computed once (the swizzle depends only on the row mod 16, and the subtile and
+// half-subtile row offsets used below are multiples of 16 rows) plus a compile-time
+// offset, so the reads need no address arithmetic in the loop.
 template <int D>
-__device__ __forceinline__ bf16x8 frag_rows(const char* tile, int row0, int ks) {
-  const int lane = threadIdx.x & 63;
-  const int r = row0 + (lane & 31);
-  const int g = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + Swz<D>::off(r, g));
-}
+struct Frag {
+  static constexpr int KS = D / 16, DT = D / 32, ROW = D * 2;
+  uint32_t rows[KS];        // row fragment, k-step ks, subtile 0
+  uint32_t trans[DT][2];    // transposed fragment, d-tile dt, rows +0 / +8, subtile 0
 
-// Transposed fragment: A[m][k] = T[row(k)][col0 + l%32] with k-slots 0..3 <- rows
-// base + 4h + 0..3 and k-slots 4..7 <- rows base + 8 + 4h + 0..3 (h = l/32).  This is the
-// key order of the MFMA C layout, so the fragment pairs with P^T / dS^T taken straight
-// from the C registers of a 32x32 score tile.
-template <int D>
-__device__ __forceinline__ bf16x8 frag_trans(const char* tile, int base, int col0) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
-  const int r = base + 4 * h + (i >> 2);
-  const int c = col0 + 16 * (grp & 1) + 4 * (i & 3);     // element column of this lane's chunk
-  const int g = c >> 3, within = (c & 7) * 2;
-  const char* p0 = tile + Swz<D>::off(r, g) + within;
-  const char* p1 = tile + Swz<D>::off(r + 8, g) + within;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int r = lane & 31;
+      rows[ks] = (uint32_t)(r * ROW + (((2 * ks + h) ^ Swz<D>::f(r)) << 4));
+    }
+    const int i = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * h + (i >> 2) + 8 * hi;
+        const int c = 32 * dt + 16 * (grp & 1) + 4 * (i & 3);   // element column of the chunk
+        trans[dt][hi] = (uint32_t)(r * ROW + (((c >> 3) ^ Swz<D>::f(r)) << 4) + (c & 7) * 2);
+      }
+  }
+
+  // Row fragment: lane holds T[32*sub + l%32][16*ks + 8h .. +8].
+  __device__ __forceinline__ bf16x8 row(const char* tile, int sub, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(tile + rows[ks] + sub * 32 * ROW);
+  }
+
+  // Transposed fragment: A[m][k] = T[row(k)][32*dt + l%32] with k-slots 0..3 <- rows
+  // 32*sub + 16*h2 + 4h + 0..3 and k-slots 4..7 <- rows 32*sub + 16*h2 + 8 + 4h + 0..3
+  // (h = l/32).  This is the key order of the MFMA C layout, so the fragment pairs with
+  // P^T / dS^T taken straight from the C registers of a 32x32 score tile.
+  __device__ __forceinline__ bf16x8 trans_frag(const char* tile, int sub, int h2, int dt) const {
+    const int rb = (sub * 32 + 16 * h2) * ROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + trans[dt][0] + rb));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + trans[dt][1] + rb));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
 
 // s_waitcnt vmcnt(0) leaving the other counters alone (gfx9 encoding).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
