@@ -51,10 +51,10 @@ def kernel_flops(w, R: int) -> dict:
             "dkdv": 4.0 * d * Hq * n_r}
 
 
-def traffic_from_profiles(kernel: str, src_sha: str):
+def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -68,6 +68,13 @@ def traffic_from_profiles(kernel: str, src_sha: str):
         return float(fields["hbm_bytes_per_launch_for_bench_member_mean"])
     except (KeyError, ValueError):
         return None
+
+
+KERNEL_SOURCES = {
+    "fwd_partials": ["k_fwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "dq_partials": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "dkdv": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+}
 
 
 def source_sha(files) -> str:
@@ -189,12 +196,10 @@ def main() -> int:
         flops_per_launch = per_kernel_flops[dom_name] / launches_per_step
         avg_ms = dom_ms / dom_launches
         achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
-        src = {"fwd_partials": ["k_fwd_bf16.hip", "k_attn_tile.h", "k_common.h"],
-               "dq_partials": ["k_bwd_bf16.hip", "k_attn_tile.h", "k_common.h"],
-               "dkdv": ["k_bwd_bf16.hip", "k_attn_tile.h", "k_common.h"]}[dom_name]
+        src = KERNEL_SOURCES[dom_name]
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_profiles(dom_name, source_sha(src)),
+                "traffic": traffic_from_profiles(dom_name, w.name, source_sha(src)),
                 "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": flops_per_launch}
     kernels = {k: {"launches_per_step": v[0] / a.steps, "ms_per_step": round(v[1] / a.steps, 3)}
                for k, v in sorted(prof.items(), key=lambda kv_: -kv_[1][1])}
