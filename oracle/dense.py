@@ -87,16 +87,16 @@ def attend(q, k_p, v_p, k_r, v_r, tau: float, rows: Optional[Sequence[int]] = No
     lse = np.zeros((rows.size, Hq))
     probs = np.zeros((rows.size, Hq, P + R)) if return_probs else None
     pos = {int(r): n for n, r in enumerate(rows)}
-    for h in range(Hq):
-        g = kv_head(h, Hq, Hkv)
-        for rb in _row_batches(rows, P + R):
+    for rb in _row_batches(rows, P + R):
+        at = np.array([pos[int(r)] for r in rb])
+        for g in range(Hkv):
             keys, vals = _visible(k_p, v_p, k_r, v_r, g, int(rb.max()))
-            p, l = _softmax_rows(_scores(q[rb, h, :], keys, rb, P, tau))
-            at = np.array([pos[int(r)] for r in rb])
-            o[at, h, :] = p @ vals
-            lse[at, h] = l
-            if return_probs:
-                probs[at, h, :p.shape[1]] = p
+            for h in (h for h in range(Hq) if kv_head(h, Hq, Hkv) == g):
+                p, l = _softmax_rows(_scores(q[rb, h, :], keys, rb, P, tau))
+                o[at, h, :] = p @ vals
+                lse[at, h] = l
+                if return_probs:
+                    probs[at, h, :p.shape[1]] = p
     return (o, lse, probs) if return_probs else (o, lse)
 
 
@@ -123,24 +123,24 @@ def attend_bwd(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Optional[Sequence[i
         dk_p = np.zeros((P, Hkv, d_qk))
         dv_p = np.zeros((P, Hkv, d_v))
     pos = {int(r): n for n, r in enumerate(rows)}
-    for h in range(Hq):
-        g = kv_head(h, Hq, Hkv)
-        for rb in _row_batches(rows, P + R):
-            last = int(rb.max())
+    for rb in _row_batches(rows, P + R):
+        last = int(rb.max())
+        at = np.array([pos[int(r)] for r in rb])
+        for g in range(Hkv):
             keys, vals = _visible(k_p, v_p, k_r, v_r, g, last)
-            qh, doh = q[rb, h, :], d_o[rb, h, :]
-            p, _ = _softmax_rows(_scores(qh, keys, rb, P, tau))
-            o = p @ vals
-            D = np.sum(doh * o, axis=1)
-            dp = doh @ vals.T
-            ds = p * (dp - D[:, None])
-            at = np.array([pos[int(r)] for r in rb])
-            dq[at, h, :] = tau * (ds @ keys)
-            dk_r[:last + 1, g, :] += tau * (ds[:, P:].T @ qh)
-            dv_r[:last + 1, g, :] += p[:, P:].T @ doh
-            if full_sequence:
-                dk_p[:, g, :] += tau * (ds[:, :P].T @ qh)
-                dv_p[:, g, :] += p[:, :P].T @ doh
+            for h in (h for h in range(Hq) if kv_head(h, Hq, Hkv) == g):
+                qh, doh = q[rb, h, :], d_o[rb, h, :]
+                p, _ = _softmax_rows(_scores(qh, keys, rb, P, tau))
+                o = p @ vals
+                D = np.sum(doh * o, axis=1)
+                dp = doh @ vals.T
+                ds = p * (dp - D[:, None])
+                dq[at, h, :] = tau * (ds @ keys)
+                dk_r[:last + 1, g, :] += tau * (ds[:, P:].T @ qh)
+                dv_r[:last + 1, g, :] += p[:, P:].T @ doh
+                if full_sequence:
+                    dk_p[:, g, :] += tau * (ds[:, :P].T @ qh)
+                    dv_p[:, g, :] += p[:, :P].T @ doh
     out = {"dq": dq, "dk_r": dk_r, "dv_r": dv_r}
     if full_sequence:
         out.update(dk_p=dk_p, dv_p=dv_p)
