@@ -81,6 +81,13 @@ extern "C" {
 #define RR_OP_BWD 1           /* workspace query for rr_attn_bwd                      */
 
 #define RR_MAX_K     64       /* responses per replay microbatch                      */
+
+/* rr_problem.flags */
+#define RR_FLAG_SHARD_NO_RESPONSE 1  /* this call holds one shard of the prompt and another
+                                        shard owns the response's own keys: the forward
+                                        writes the response part as empty (lse = -inf),
+                                        the backward forms dq over this shard's prompt keys
+                                        only and no dk_r / dv_r (they may be NULL)        */
 #define RR_MAX_ACC    8       /* buffers per accumulation window                      */
 
 /* Problem description shared by rr_attn_fwd / rr_attn_bwd / rr_workspace_bytes. */
@@ -100,6 +107,7 @@ typedef struct rr_problem {
   int32_t latent;   /* 0 = GQA K/V pages; 1 = latent rows (K = row, V = first d_v dims) */
   int32_t dtype;    /* RR_F32 or RR_BF16                                                */
   float   tau;      /* softmax scale, finite and > 0                                    */
+  int32_t flags;    /* RR_FLAG_* bits; 0 for a whole prompt on one device               */
 } rr_problem;
 
 /* Resident prompt state (prompt-group lifetime).  Read-only to the library. */

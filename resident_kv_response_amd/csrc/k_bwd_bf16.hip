@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
   const int64_t stride = (int64_t)g.Hkv * D;
   const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
   const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
-  const int n_keys = (r_first >= rl) ? 0 : (int)(key1 - key0);
+  const int n_keys = (r_first >= rl || (resp && !g.resp_keys)) ? 0 : (int)(key1 - key0);
   const int n_stages = (n_keys + C::BN - 1) / C::BN;
   const int64_t sb = stride * 2;
   const uint16_t* kc = kb + key0 * stride;

@@ -30,7 +30,7 @@ __device__ __forceinline__ PartRange part_range(const Geom& g, int part, int k, 
     pr.resp = false;
   } else {
     pr.key0 = 0;
-    pr.key1 = min(g.r_len[k], r_top + 1);
+    pr.key1 = g.resp_keys ? min(g.r_len[k], r_top + 1) : 0;
     pr.resp = true;
   }
   return pr;

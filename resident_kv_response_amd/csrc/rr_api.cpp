@@ -175,6 +175,7 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   if ((e = timed("dq_reduce", s, [&] { return launch_dq_reduce(g, dq_part, dq, accumulate, s); })))
     return hip_fail(e, "dq_reduce");
   const int key_top = g.row_hi;   // response keys reachable from the launch's rows
+  if (!g.resp_keys) return RR_OK;  // another shard owns the response keys and their grads
   if (!accumulate) {
     if ((e = timed("zero_rows", s, [&] {
            hipError_t e1 = launch_zero_rows(dk_r, p->K, p->R_max, 0, key_top, kv_row, s);

@@ -22,6 +22,8 @@ struct Geom {
   int32_t row_hi;
   float tau;          // softmax scale
   float c2;           // tau * log2(e): scores in base-2 units
+  int32_t resp_keys;  // 1: the response's own causal keys form the last part; 0: another
+                      // prompt shard owns them and the last part is empty
   int32_t r_len[RR_MAX_K];
 };
 

@@ -42,6 +42,7 @@ int validate_problem(const rr_problem* p) {
   if (p->dtype != RR_F32 && p->dtype != RR_BF16)
     return set_error(RR_E_SHAPE, "dtype must be RR_F32 or RR_BF16 (got %d)", p->dtype);
   if (p->topk < 0) return set_error(RR_E_SHAPE, "topk must be >= 0");
+  if (p->flags & ~RR_FLAG_SHARD_NO_RESPONSE) return set_error(RR_E_SHAPE, "unknown flags 0x%x", p->flags);
   if (p->latent) {
     return set_error(RR_E_UNSUPPORTED, "latent pages are not supported by this build");
   }
@@ -137,7 +138,8 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
   if ((rc = check_resident(p, kv))) return rc;
   if (!q || !k_r || !v_r || !o || !lse || !d_o)
     return set_error(RR_E_NULL, "q / k_r / v_r / o / lse / d_o is NULL");
-  if (!dq || !dk_r || !dv_r) return set_error(RR_E_NULL, "dq / dk_r / dv_r is NULL");
+  const bool owns_resp = !(p->flags & RR_FLAG_SHARD_NO_RESPONSE);
+  if (!dq || (owns_resp && (!dk_r || !dv_r))) return set_error(RR_E_NULL, "dq / dk_r / dv_r is NULL");
   if ((rc = check_r_len(p, r_len))) return rc;
   if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
   if ((rc = check_aligned("q / k_r / v_r / k_p / v_p / o / d_o / dq / dk_r / dv_r",
@@ -208,6 +210,7 @@ Geom make_geom(const rr_problem* p, const int32_t* r_len) {
   g.row_hi = p->R_max;
   g.tau = p->tau;
   g.c2 = (float)(p->tau * 1.4426950408889634);
+  g.resp_keys = (p->flags & RR_FLAG_SHARD_NO_RESPONSE) ? 0 : 1;
   for (int k = 0; k < p->K; ++k) g.r_len[k] = r_len[k];
   return g;
 }

@@ -23,6 +23,7 @@ RR_E_RANGE, RR_E_DUPLICATE, RR_E_STALE, RR_E_MISSING, RR_E_HIP = -5, -6, -7, -8,
 RR_F32, RR_BF16 = 0, 1
 RR_OP_FWD, RR_OP_BWD = 0, 1
 RR_MAX_K, RR_MAX_ACC = 64, 8
+RR_FLAG_SHARD_NO_RESPONSE = 1
 
 EXPORTS = ["rr_workspace_bytes", "rr_num_parts", "rr_attn_fwd", "rr_lse_merge", "rr_attn_bwd",
            "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
@@ -40,7 +41,7 @@ class CProblem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("latent", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("tau", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("tau", ctypes.c_float), ("flags", ctypes.c_int32)]
 
 
 class CResident(ctypes.Structure):
@@ -119,11 +120,13 @@ class Problem:
     topk: int = 0
     idx_dim: int = 0
     latent: int = 0
+    flags: int = 0
 
     def c(self) -> CProblem:
         return CProblem(P=self.P, chunk=self.chunk, R_max=self.R_max, K=self.K, Hq=self.Hq,
                         Hkv=self.Hkv, d_qk=self.d_qk, d_v=self.d_v, block=self.block, topk=self.topk,
-                        idx_dim=self.idx_dim, latent=self.latent, dtype=self.dtype, tau=self.tau)
+                        idx_dim=self.idx_dim, latent=self.latent, dtype=self.dtype, tau=self.tau,
+                        flags=self.flags)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -83,26 +83,29 @@ def test_f32_varlen_microbatch():
     _run_and_check(w, [90, 33, 0], R_max=96, chunk=256, block=32)
 
 
-@pytest.mark.parametrize("cfg", ["GQA_P128K", "SHARE_P256K"])
+@pytest.mark.parametrize("cfg", ["GQA_P128K", "SHARE_P256K", "FULL_P2M"])
 def test_full_size_sampled_rows(cfg):
     """Full-size configurations: every output of the GPU path is produced; O, lse and dQ of
     seeded sampled rows (block boundaries included) are compared with the oracle, and
     dK/dV of the last response keys, whose gradients only rows near the end reach."""
     from tests import _gpu as G
     w = getattr(configs, cfg)
-    res, mem = _inputs(w, [w.R])
-    st = G.stack_members(mem, w.R)
-    prob = G.problem(w.P, w.R, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
-    print(f"[parity] {w.name} full size", flush=True)
-    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [w.R]).fwd().bwd().numpy()
-    rows = synth.sample_rows(w.seed, w.R, 24, w.block)
-    tail = np.arange(w.R - 8, w.R)
+    # the 2M group: its first member, at its seeded length
+    Rg = int(synth.response_lengths(w)[0]) if w.G > 1 else w.R
+    res, mem = _inputs(w, [Rg])
+    st = G.stack_members(mem, Rg)
+    prob = G.problem(w.P, Rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+    print(f"[parity] {w.name} full size, R={Rg}", flush=True)
+    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [Rg]).fwd().bwd().numpy()
+    n_rows, n_tail = (24, 8) if w.P <= 262144 else (10, 4)
+    rows = synth.sample_rows(w.seed, Rg, n_rows, w.block)
+    tail = np.arange(Rg - n_tail, Rg)
     rows = np.union1d(rows, tail)
-    ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, 0, w.R, w.tau, rows=rows)
+    ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, 0, Rg, w.tau, rows=rows)
     assert_bf16_close("o", got["o"][0][rows], ref["o"])
     assert_bf16_close("dq", got["dq"][0][rows], ref["dq"])
     assert np.max(np.abs(got["lse"][0][rows] - ref["lse"])) <= 2e-2
-    # response keys j >= R-8 receive gradient only from rows >= R-8, all included above
-    assert_bf16_close("dk_r tail", got["dk"][0][w.R - 8:], ref["dk_r"][w.R - 8:])
-    assert_bf16_close("dv_r tail", got["dv"][0][w.R - 8:], ref["dv_r"][w.R - 8:])
+    # response keys j >= R-n_tail receive gradient only from rows >= R-n_tail, all included
+    assert_bf16_close("dk_r tail", got["dk"][0][Rg - n_tail:], ref["dk_r"][Rg - n_tail:])
+    assert_bf16_close("dv_r tail", got["dv"][0][Rg - n_tail:], ref["dv_r"][Rg - n_tail:])
     assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))
