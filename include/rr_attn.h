@@ -144,7 +144,18 @@ int32_t rr_num_parts(const rr_problem* p);
  *   part_lse  rr_num_parts); with part_lse [n_parts][K][R][Hq] fp32.  Exported
  *             partials make the per-chunk statistics available to an external merge.
  *   topk_idx  topk > 0: output [K][R][topk] int32, the selected prompt positions of
- *             each row in ascending order; else NULL
+ *             each row in ascending order (-1 in padding rows); else NULL
+ *
+ * Latent-page top-k variant (latent = 1).  Source: ai.thesatyajit.com/articles/
+ * longstraw-2m-rl, section "Two incompatible architectures, same transaction" (GLM
+ * instantiation: MLA latent pages of 512 + 64 dims and resident index keys from which
+ * the sparse selection is rebuilt).  Row i of response k scores every prompt position j
+ * by sigma = q_idx . k_idx_j (fp32), keeps the topk largest (equal scores: the lower
+ * position first), and attends, for each of the 64 heads, over those latent rows plus
+ * response rows 0..i (key = the 576-wide row, value = its first 512 dims).  Built for
+ * bf16, Hq = 64, Hkv = 1, d_qk = 576, d_v = 512, idx_dim = 128, topk a multiple of 32 in
+ * [32, P], R_max a multiple of 8, flags = 0, o and lse required, no partial export; the
+ * workspace holds the fp32 scores, K * R_max * P * 4 bytes.
  *   ws        workspace of rr_workspace_bytes(p, RR_OP_FWD) bytes (may be NULL when 0)
  */
 int rr_attn_fwd(const rr_problem* p, const rr_resident* kv,
@@ -185,7 +196,9 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
  *
  *   o, lse      the forward's fp32 outputs for these rows (global statistics; a caller
  *               holding one shard of the prompt passes the merged ones)
- *   topk_idx    topk > 0: the forward's selection [K][R][topk]; else NULL
+ *   topk_idx    topk > 0: the forward's selection [K][R][topk]; else NULL.  Entries
+ *               outside [0, P) are clamped into it (no fault; the gradients are then
+ *               those of the clamped selection).
  *   accumulate  0: gradients are written (=) to every row the call touches;
  *               1: they are added (+=)
  *   block_idx   -1: whole response: dq of every row, then dk_r/dv_r by walking blocks

@@ -50,10 +50,10 @@ struct DirectLoad {
   static constexpr int PER_WAVE = GRAN / (64 * WAVES);
   static_assert(GRAN % (64 * WAVES) == 0, "tile must split evenly over the waves");
   static_assert(RPI == 4 || RPI == 8, "D must be 128 or 64");
-  static_assert((PER_WAVE * RPI) % 16 == 0, "each wave's first row must be a multiple of 16");
 
   uint32_t voff[4];     // lane byte offsets by instruction index mod 4 (row within the
-                        // instruction and swizzled granule; the swizzle depends on r mod 16)
+                        // instruction and swizzled granule): the swizzle depends on the row
+                        // mod 16 and 4 instructions advance 4 * RPI rows, a multiple of 16
   int row0;             // first tile row of this wave
 
   __device__ __forceinline__ void init(int64_t stride_bytes) {
@@ -124,6 +124,27 @@ struct Frag {
   // Row fragment: lane holds T[32*sub + l%32][16*ks + 8h .. +8].
   __device__ __forceinline__ bf16x8 row(const char* tile, int sub, int ks) const {
     return *reinterpret_cast<const bf16x8*>(tile + rows[ks] + sub * 32 * ROW);
+  }
+
+  // Lane offsets (rows +0 / +8) of the transposed fragment at a run-time column offset
+  // col0 (a multiple of 32), for callers whose column tile is not a compile-time index.
+  static __device__ __forceinline__ void trans_offsets(int col0, uint32_t (&off)[2]) {
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, i = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 4 * h + (i >> 2) + 8 * hi;
+      const int c = col0 + 16 * (grp & 1) + 4 * (i & 3);
+      off[hi] = (uint32_t)(r * ROW + (((c >> 3) ^ Swz<D>::f(r)) << 4) + (c & 7) * 2);
+    }
+  }
+  static __device__ __forceinline__ bf16x8 trans_at(const char* tile, const uint32_t (&off)[2], int sub, int h2) {
+    const int rb = (sub * 32 + 16 * h2) * ROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off[0] + rb));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off[1] + rb));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
   }
 
   // Transposed fragment: A[m][k] = T[row(k)][32*dt + l%32] with k-slots 0..3 <- rows

@@ -1,0 +1,507 @@
+// Latent-page sparse attention on MFMA (gfx950).
+//
+// Source: ai.thesatyajit.com/articles/longstraw-2m-rl, section "Two incompatible
+// architectures, same transaction" (GLM instantiation): resident MLA latent pages of
+// 512 + 64 dims, every head reading the same latent row, attention over the sparse
+// selection of prompt positions plus the response's own causal rows, and the
+// response-only backward.  Key = the whole 576-wide latent row, value = its first 512
+// dims; 64 query heads share each row.
+//
+// sparse_fwd: one workgroup (4 waves) per query row.  Keys are the row's top-k prompt
+// rows followed by response rows 0..i, gathered 32 at a time straight into LDS.  Wave w
+// contracts dims [144w, 144w + 144) of the scores for all 64 heads; the four partial
+// score tiles are exchanged through LDS and summed in a fixed order, so every wave holds
+// the same scores and runs the same online softmax; wave w then accumulates the output
+// for value dims [128w, 128w + 128).
+//
+// sparse_dq: the same structure for the backward: partial scores and partial dP = dO V^T
+// (wave w: value dims [128w, 128w+128)), exchanged and summed; dS = P (dP - D); dQ^T for
+// the wave's share of the 18 32-wide dim tiles.  For response keys it also writes P and
+// dS (bf16) of every (row, head, key) pair, from which xty_gemm forms dK_r and dV_r.
+//
+// xty_gemm: C[j][d] (+)= alpha sum_{(i,h): i >= j} X[i][h][j] Y[i][h][d], the response-key
+// gradients dK_r = tau dS^T Q and dV_r = P^T dO, with both operands read by transposing
+// LDS reads from row-major tiles loaded straight into LDS.
+#include "k_lds.h"
+#include "kernels.h"
+
+namespace rr {
+
+constexpr int kLatD = 576, kLatDV = 512, kLatH = 64;
+
+// Latent tile: rows of 576 bf16 (72 granules); logical granule g of row r stored at
+// (g & ~7) | ((g & 7) ^ f(r)).  f(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3) makes the 16
+// consecutive rows of a row-fragment read and the 4 rows x 4 granules of a half-wave
+// transposing read land on distinct banks (a row is 1152 bytes, so even and odd rows
+// occupy different bank halves).
+struct Lat {
+  static constexpr int G = 72, ROW = 1152;
+  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+  static __device__ __forceinline__ int phys(int g, int r) { return (g & ~7) | ((g & 7) ^ f(r)); }
+  static __device__ __forceinline__ int off(int r, int g) { return r * ROW + (phys(g, r) << 4); }
+};
+constexpr int kLatKeys = 32;
+constexpr int kLatTile = kLatKeys * Lat::ROW;        // 36,864 bytes
+constexpr int kLatInstr = kLatKeys * Lat::G / 64;    // 36 wave-wide loads per tile
+
+// Gather keys [t0, t0 + 32) of a row's key list into `tile`: key t < n_sel is prompt row
+// sel[t], key t >= n_sel is response row t - n_sel; keys at or past n_keys are
+// redirected to key n_keys - 1 (masked by the caller).  A selected position outside
+// [0, P) is clamped into it, so a corrupt index list cannot address memory outside the
+// resident pages.  4 waves, 9 loads each.
+__device__ __forceinline__ void gather_tile(char* tile, const uint16_t* latent_p, int64_t P,
+                                            const uint16_t* latent_rk, const int32_t* sel,
+                                            int n_sel, int n_keys, int t0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < kLatInstr / 4; ++u) {
+    const int n = wave * (kLatInstr / 4) + u;
+    const int p = 64 * n + lane;
+    const int r = p / Lat::G, ph = p % Lat::G;
+    const int g = (ph & ~7) | ((ph & 7) ^ Lat::f(r));
+    const int t = min(t0 + r, n_keys - 1);
+    const int64_t sp = t < n_sel ? min(max((int64_t)sel[t], (int64_t)0), P - 1) : 0;
+    const uint16_t* rowp = t < n_sel ? latent_p + sp * kLatD : latent_rk + (int64_t)(t - n_sel) * kLatD;
+    __builtin_amdgcn_global_load_lds(rowp + g * 8, (lds_void*)(tile + n * 1024), 16, 0, 0);
+  }
+}
+
+// Row fragment of a latent tile: A[m][k] = T[l%32][16*ks + 8h .. +8].
+__device__ __forceinline__ bf16x8 lat_row(const char* tile, int ks) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const bf16x8*>(tile + Lat::off(lane & 31, 2 * ks + (lane >> 5)));
+}
+
+// Transposed fragment of a latent tile: A[m][k] = T[row(k)][col0 + l%32], k-slots
+// 0..3 <- rows 16*h2 + 4h + 0..3, 4..7 <- rows 16*h2 + 8 + 4h + 0..3 (the MFMA C layout's
+// key order).
+__device__ __forceinline__ bf16x8 lat_trans(const char* tile, int h2, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
+  const int r = 16 * h2 + 4 * h + (i >> 2);
+  const int c = col0 + 16 * (grp & 1) + 4 * (i & 3);
+  const int within = (c & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + Lat::off(r, c >> 3) + within));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + Lat::off(r + 8, c >> 3) + within));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Exchange of per-wave partial 32x32 tiles: xch[w][j][lane] holds registers 4j..4j+3 of
+// lane `lane` of wave w.
+struct Xch {
+  float4 v[4][4][64];
+};
+
+__device__ __forceinline__ void xch_put(Xch& x, const f32x16& p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x.v[wave][j][lane] = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+}
+
+// Sum of the four partials in wave order (identical in every wave).
+__device__ __forceinline__ void xch_sum(const Xch& x, f32x16& s) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float4 a = x.v[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 b = x.v[w][j][lane];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    s[4 * j] = a.x;
+    s[4 * j + 1] = a.y;
+    s[4 * j + 2] = a.z;
+    s[4 * j + 3] = a.w;
+  }
+}
+
+constexpr float kLatRescale = 8.0f;
+
+// One workgroup = one query row and one tile of 32 heads (blockIdx.x = 2 * row + tile).
+__global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ latent_p,
+                                                     const uint16_t* __restrict__ latent_r,
+                                                     const int32_t* __restrict__ sel_idx,
+                                                     float* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) char kv0[kLatTile];
+  __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
+  __shared__ __attribute__((aligned(16))) Xch xch;
+  const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
+  const int k = row / g.R, i = row % g.R;
+  if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int64_t hrow0 = (int64_t)row * kLatH + 32 * ht;   // (k, i, first head of the tile)
+  if (i >= g.r_len[k]) {
+    for (int e = threadIdx.x; e < 32 * kLatDV; e += 256) o[hrow0 * kLatDV + e] = 0.0f;
+    if (threadIdx.x < 32) lse[hrow0 + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const int n_keys = topk + i + 1;
+  const int n_tiles = (n_keys + kLatKeys - 1) / kLatKeys;
+  const int32_t* sel = sel_idx + (int64_t)row * topk;
+  const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
+  gather_tile(kv0, latent_p, g.P, latent_rk, sel, topk, n_keys, 0);
+
+  // Q fragments of this wave's 9 k-steps of the score contraction
+  bf16x8 qf[9];
+  const uint16_t* qrow = q + (hrow0 + col) * kLatD;
+#pragma unroll
+  for (int s = 0; s < 9; ++s)
+    qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * (9 * wave + s) + 8 * hl));
+  f32x16 acc[4];
+  float m_run = kNegBig, l_run = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+
+  auto tile_step = [&](const char* cur, char* nxt, int t) {
+    wait_vmcnt0();
+    __syncthreads();
+    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, g.P, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    f32x16 sp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sp[e] = 0.0f;
+    prio_mfma();
+#pragma unroll
+    for (int s = 0; s < 9; ++s) sp = mfma32x32x16(lat_row(cur, 9 * wave + s), qf[s], sp);
+    prio_valu();
+    xch_put(xch, sp);
+    __syncthreads();
+    f32x16 sc;
+    xch_sum(xch, sc);
+    const int rel = t * kLatKeys;
+    if (rel + kLatKeys > n_keys) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = rel + (e >> 2) * 8 + hl * 4 + (e & 3);
+        if (key >= n_keys) sc[e] = -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m_run, mx * g.c2);
+    if (__any(m_new > m_run + kLatRescale)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m_run = m_new;
+    }
+    float p[16], ls = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(sc[e], g.c2, -m_run));
+      ls += p[e];
+    }
+    l_run += ls;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 uu;
+      uu.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
+      uu.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
+      uu.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
+      uu.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
+      pf[h2] = as_bf16x8(uu);
+    }
+    prio_mfma();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 128 * wave + 32 * dt), pf[h2], acc[dt]);
+    prio_valu();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(kv0, kv1, t);
+    if (t + 1 < n_tiles) tile_step(kv1, kv0, t + 1);
+  }
+
+  const float l = pair_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* dst = o + (hrow0 + col) * kLatDV + 128 * wave;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = 32 * dt + 8 * i4 + 4 * hl;
+      *reinterpret_cast<float4*>(dst + d0) = make_float4(acc[dt][4 * i4] * inv, acc[dt][4 * i4 + 1] * inv,
+                                                         acc[dt][4 * i4 + 2] * inv, acc[dt][4 * i4 + 3] * inv);
+    }
+  if (wave == 0 && hl == 0) lse[hrow0 + col] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// dQ of one query row and head tile, and the response pairs' P and dS.  pds layout:
+// [K][R][64][R] bf16 (row, head, key); for row i the keys j in
+// [0, min(R, round_up(i + 1, 128))) are written, zeros for j > i.
+__global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint16_t* __restrict__ q,
+                                                    const uint16_t* __restrict__ latent_p,
+                                                    const uint16_t* __restrict__ latent_r,
+                                                    const int32_t* __restrict__ sel_idx,
+                                                    const uint16_t* __restrict__ d_o,
+                                                    const float* __restrict__ lse,
+                                                    const float* __restrict__ Dvec,
+                                                    float* __restrict__ dq, uint16_t* __restrict__ p_r,
+                                                    uint16_t* __restrict__ ds_r, int accumulate) {
+  __shared__ __attribute__((aligned(1024))) char kv0[kLatTile];
+  __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
+  __shared__ __attribute__((aligned(16))) Xch xs;
+  __shared__ __attribute__((aligned(16))) Xch xp;
+  const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
+  const int k = row / g.R, i = row % g.R;
+  if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int64_t hrow0 = (int64_t)row * kLatH + 32 * ht;
+  if (i >= g.r_len[k]) {
+    if (!accumulate)
+      for (int e = threadIdx.x; e < 32 * kLatD; e += 256) dq[hrow0 * kLatD + e] = 0.0f;
+    return;
+  }
+  const int64_t pds_row = hrow0 * g.R;                // element offset of (k, i, first head, key 0)
+  const int jz_end = min(g.R, ((i + 1 + 127) / 128) * 128);
+  const int nz = jz_end - i - 1;                       // causal remainder of the last 128-key group
+  for (int e = threadIdx.x; e < 32 * nz; e += 256) {
+    const int64_t at = pds_row + (int64_t)(e / nz) * g.R + i + 1 + e % nz;
+    p_r[at] = 0;
+    ds_r[at] = 0;
+  }
+  const int n_keys = topk + i + 1;
+  const int n_tiles = (n_keys + kLatKeys - 1) / kLatKeys;
+  const int32_t* sel = sel_idx + (int64_t)row * topk;
+  const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
+  gather_tile(kv0, latent_p, g.P, latent_rk, sel, topk, n_keys, 0);
+
+  bf16x8 qf[9], of[8];
+  const int64_t hr = hrow0 + col;
+#pragma unroll
+  for (int s = 0; s < 9; ++s)
+    qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q + hr * kLatD + 16 * (9 * wave + s) + 8 * hl));
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    of[s] = as_bf16x8(*reinterpret_cast<const uint4*>(d_o + hr * kLatDV + 16 * (8 * wave + s) + 8 * hl));
+  const float lse2 = lse[hr] * kLog2e;
+  const float dvv = Dvec[hr];
+  // this wave's dQ dim tiles: 18 tiles of 32 split 5, 5, 4, 4
+  const int dt_lo = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
+  const int n_dt = wave < 2 ? 5 : 4;
+  f32x16 acc[5];
+#pragma unroll
+  for (int dt = 0; dt < 5; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+  uint16_t* p_row = p_r + pds_row + (int64_t)col * g.R;
+  uint16_t* ds_row = ds_r + pds_row + (int64_t)col * g.R;
+
+  auto tile_step = [&](const char* cur, char* nxt, int t) {
+    wait_vmcnt0();
+    __syncthreads();
+    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, g.P, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    f32x16 sp, dpp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sp[e] = dpp[e] = 0.0f;
+    prio_mfma();
+#pragma unroll
+    for (int s = 0; s < 9; ++s) sp = mfma32x32x16(lat_row(cur, 9 * wave + s), qf[s], sp);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dpp = mfma32x32x16(lat_row(cur, 8 * wave + s), of[s], dpp);  // value dims
+    prio_valu();
+    xch_put(xs, sp);
+    xch_put(xp, dpp);
+    __syncthreads();
+    f32x16 sc, dp;
+    xch_sum(xs, sc);
+    xch_sum(xp, dp);
+    const int rel = t * kLatKeys;
+    float p[16], ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = rel + (e >> 2) * 8 + hl * 4 + (e & 3);
+      p[e] = key < n_keys ? fast_exp2(fmaf(sc[e], g.c2, -lse2)) : 0.0f;
+      ds[e] = p[e] * (dp[e] - dvv);
+    }
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 uu;
+      uu.x = pack_bf16x2(ds[8 * h2 + 0], ds[8 * h2 + 1]);
+      uu.y = pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]);
+      uu.z = pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]);
+      uu.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
+      dsf[h2] = as_bf16x8(uu);
+    }
+    // response keys: P and dS of (row i, head, key j) for the dK_r / dV_r contraction
+    if (wave == 0 && rel + kLatKeys > topk) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int key0 = rel + e4 * 8 + hl * 4;       // 4 consecutive keys
+        if (key0 >= topk && key0 < n_keys) {
+          const int j = key0 - topk;                  // keys past i carry p = dS = 0
+          uint2 pv, dv;
+          pv.x = pack_bf16x2(p[4 * e4], p[4 * e4 + 1]);
+          pv.y = pack_bf16x2(p[4 * e4 + 2], p[4 * e4 + 3]);
+          dv.x = pack_bf16x2(ds[4 * e4], ds[4 * e4 + 1]);
+          dv.y = pack_bf16x2(ds[4 * e4 + 2], ds[4 * e4 + 3]);
+          *reinterpret_cast<uint2*>(p_row + j) = pv;     // j + 3 < jz_end: R_max % 4 == 0
+          *reinterpret_cast<uint2*>(ds_row + j) = dv;
+        }
+      }
+    }
+    prio_mfma();
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt) {
+      if (dt < n_dt) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 32 * (dt_lo + dt)), dsf[h2], acc[dt]);
+      }
+    }
+    prio_valu();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(kv0, kv1, t);
+    if (t + 1 < n_tiles) tile_step(kv1, kv0, t + 1);
+  }
+
+  float* dst = dq + hr * kLatD;
+#pragma unroll
+  for (int dt = 0; dt < 5; ++dt) {
+    if (dt < n_dt) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = 32 * (dt_lo + dt) + 8 * i4 + 4 * hl;
+        float4 v = make_float4(acc[dt][4 * i4] * g.tau, acc[dt][4 * i4 + 1] * g.tau,
+                               acc[dt][4 * i4 + 2] * g.tau, acc[dt][4 * i4 + 3] * g.tau);
+        if (accumulate) {
+          const float4 y = *reinterpret_cast<const float4*>(dst + d0);
+          v.x += y.x;
+          v.y += y.y;
+          v.z += y.z;
+          v.w += y.w;
+        }
+        *reinterpret_cast<float4*>(dst + d0) = v;
+      }
+    }
+  }
+}
+
+// C[k][j][d] (+)= alpha * sum over rows i in [max(row_lo, j0), row_hi) and heads h of
+// X[k][i][h][j] * Y[k][i][h][d].  Workgroup tile: 128 keys j x 64 dims d (4 waves x 32
+// keys); inner dimension m = (i, h) in steps of 32 rows.
+__global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ X,
+                                                   const uint16_t* __restrict__ Y, int ldY, int n_d,
+                                                   float* __restrict__ C, int ldC, int R, int K,
+                                                   int row_lo, int row_hi, int j_hi, float alpha,
+                                                   int accumulate, Geom g) {
+  __shared__ __attribute__((aligned(1024))) char xb0[32 * 128 * 2];
+  __shared__ __attribute__((aligned(1024))) char yb0[32 * 64 * 2];
+  __shared__ __attribute__((aligned(1024))) char xb1[32 * 128 * 2];
+  __shared__ __attribute__((aligned(1024))) char yb1[32 * 64 * 2];
+  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 63) / 64;
+  int64_t idx = blockIdx.x;
+  const int dt = (int)(idx % n_dt);
+  idx /= n_dt;
+  const int jt = (int)(idx % n_jt);
+  const int k = (int)(idx / n_jt);
+  if (k >= K) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int j0 = jt * 128, d0 = dt * 64;
+  const int rl = g.r_len[k];
+  const int i_lo = max(row_lo, j0), i_hi = min(row_hi, rl);
+  const int64_t m_lo = (int64_t)i_lo * kLatH, m_hi = (int64_t)i_hi * kLatH;
+  const int n_steps = m_hi > m_lo ? (int)((m_hi - m_lo) / 32) : 0;   // kLatH is a multiple of 32
+  const uint16_t* xs = X + ((int64_t)k * R * kLatH + m_lo) * R + j0;
+  const uint16_t* ys = Y + ((int64_t)k * R * kLatH + m_lo) * ldY + d0;
+  DirectLoad<128, 32, 4> dlx;
+  DirectLoad<64, 32, 4> dly;
+  dlx.init((int64_t)R * 2);
+  dly.init((int64_t)ldY * 2);
+  uint32_t xoff[2];                       // X^T fragment: key columns 32*wave .. +32
+  Frag<128>::trans_offsets(32 * wave, xoff);
+  Frag<64> fy;
+  fy.init();
+  f32x16 acc[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
+  if (n_steps > 0) {
+    dlx.issue(xb0, xs, 0, 32, (int64_t)R * 2);
+    dly.issue(yb0, ys, 0, 32, (int64_t)ldY * 2);
+  }
+  auto step = [&](const char* xc, const char* yc, char* xn, char* yn, int st) {
+    wait_vmcnt0();
+    __syncthreads();
+    if (st + 1 < n_steps) {
+      dlx.issue(xn, xs + (int64_t)(st + 1) * 32 * R, 0, 32, (int64_t)R * 2);
+      dly.issue(yn, ys + (int64_t)(st + 1) * 32 * ldY, 0, 32, (int64_t)ldY * 2);
+    }
+    prio_mfma();
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 a = Frag<128>::trans_at(xc, xoff, 0, h2);   // X^T: keys 32*wave .. +32
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[n] = mfma32x32x16(a, fy.trans_frag(yc, 0, h2, n), acc[n]);
+    }
+    prio_valu();
+  };
+  for (int st = 0; st < n_steps; st += 2) {
+    step(xb0, yb0, xb1, yb1, st);
+    if (st + 1 < n_steps) step(xb1, yb1, xb0, yb0, st + 1);
+  }
+  // C layout: lane = dim column, registers = key rows
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int d = d0 + 32 * n + col;
+    if (d >= n_d) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + 32 * wave + (e >> 2) * 8 + 4 * hl + (e & 3);
+      if (j >= j_hi || j >= rl) continue;
+      float* dst = C + ((int64_t)k * R + j) * ldC + d;
+      *dst = (accumulate ? *dst : 0.0f) + alpha * acc[n][e];
+    }
+  }
+}
+
+hipError_t launch_sparse_fwd(const Geom& g, int topk, const void* q, const void* latent_p,
+                             const void* latent_r, const int32_t* sel, float* o, float* lse,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(sparse_fwd, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
+                     (const uint16_t*)q, (const uint16_t*)latent_p, (const uint16_t*)latent_r, sel,
+                     o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* latent_p,
+                            const void* latent_r, const int32_t* sel, const void* d_o,
+                            const float* lse, const float* Dvec, float* dq, uint16_t* p_r,
+                            uint16_t* ds_r, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(sparse_dq, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
+                     (const uint16_t*)q, (const uint16_t*)latent_p, (const uint16_t*)latent_r, sel,
+                     (const uint16_t*)d_o, lse, Dvec, dq, p_r, ds_r, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, float* C, int ldC,
+                      const Geom& g, int row_lo, int row_hi, int j_hi, float alpha, int accumulate,
+                      hipStream_t s) {
+  if (j_hi <= 0) return hipSuccess;
+  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 63) / 64;
+  hipLaunchKernelGGL(xty_gemm, dim3((unsigned)(g.K * n_jt * n_dt)), dim3(256), 0, s, X, Y, ldY, n_d, C,
+                     ldC, g.R, g.K, row_lo, row_hi, j_hi, alpha, accumulate, g);
+  return hipGetLastError();
+}
+
+}  // namespace rr

@@ -52,6 +52,22 @@ hipError_t launch_dkdv(const Geom& g, int dtype, const AttnPtrs& a, int key_hi, 
 hipError_t launch_zero_rows(float* x, int K, int R, int lo, int hi, int64_t row_elems,
                             hipStream_t s);
 
+// Latent-page sparse variant (k_topk.hip, k_sparse.hip).
+hipError_t launch_index_scores(const float* q_idx, const float* k_idx, float* sigma, int rows,
+                               int64_t P, hipStream_t s);
+hipError_t launch_topk(const float* sigma, int64_t P, int k, const Geom& g, int32_t* idx_out,
+                       hipStream_t s);
+hipError_t launch_sparse_fwd(const Geom& g, int topk, const void* q, const void* latent_p,
+                             const void* latent_r, const int32_t* sel, float* o, float* lse,
+                             hipStream_t s);
+hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* latent_p,
+                            const void* latent_r, const int32_t* sel, const void* d_o,
+                            const float* lse, const float* Dvec, float* dq, uint16_t* p_r,
+                            uint16_t* ds_r, int accumulate, hipStream_t s);
+hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, float* C, int ldC,
+                      const Geom& g, int row_lo, int row_hi, int j_hi, float alpha, int accumulate,
+                      hipStream_t s);
+
 // acc[e] += scale * g[e], e < n.
 hipError_t launch_axpy(float* acc, const float* g, int64_t n, float scale, hipStream_t s);
 

@@ -81,6 +81,56 @@ float* carve(void* base, size_t offset) {
 
 }  // namespace
 
+// Latent-page backward: D, then per-row dQ (which also writes the response pairs' P and dS),
+// then dK_r = tau dS^T Q and dV_r = P^T dO over the query rows of each block, last block
+// first.
+int latent_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+               const int32_t* r_len, const int32_t* topk_idx, const float* o, const float* lse,
+               const void* d_o, float* dq, float* dk_r, float* dv_r, int32_t accumulate,
+               int32_t block_idx, void* ws, hipStream_t s) {
+  Geom g = make_geom(p, r_len);
+  const size_t rows = (size_t)p->K * p->R_max * p->Hq;
+  float* Dvec = carve(ws, 0);
+  uint16_t* p_r = reinterpret_cast<uint16_t*>(carve(ws, align_up(rows * sizeof(float), 256)));
+  uint16_t* ds_r = reinterpret_cast<uint16_t*>(carve(ws, align_up(rows * sizeof(float), 256) + ws_pds_bytes(p)));
+  const int nb = (p->R_max + p->block - 1) / p->block;
+  if (block_idx >= 0) {
+    g.row_lo = block_idx * p->block;
+    g.row_hi = std::min(p->R_max, g.row_lo + p->block);
+  }
+  hipError_t e;
+  if ((e = timed("bwd_pre", s, [&] { return launch_bwd_pre(g, p->dtype, o, d_o, Dvec, s); })))
+    return hip_fail(e, "bwd_pre");
+  if ((e = timed("sparse_dq", s, [&] {
+         return launch_sparse_dq(g, p->topk, q, kv->k_p, k_r, topk_idx, d_o, lse, Dvec, dq, p_r, ds_r,
+                                 accumulate, s);
+       })))
+    return hip_fail(e, "sparse_dq");
+  if (!accumulate) {
+    if ((e = timed("zero_rows", s, [&] {
+           hipError_t e1 = launch_zero_rows(dk_r, p->K, p->R_max, 0, g.row_hi, p->d_qk, s);
+           return e1 != hipSuccess ? e1 : launch_zero_rows(dv_r, p->K, p->R_max, 0, g.row_hi, p->d_v, s);
+         })))
+      return hip_fail(e, "zero_rows");
+  }
+  const int b_hi = block_idx >= 0 ? block_idx : nb - 1;
+  const int b_lo = block_idx >= 0 ? block_idx : 0;
+  for (int b = b_hi; b >= b_lo; --b) {   // reverse block walk
+    const int lo = b * p->block, hi = std::min(p->R_max, lo + p->block);
+    if ((e = timed("xty_dk", s, [&] {
+           return launch_xty(ds_r, static_cast<const uint16_t*>(q), p->d_qk, p->d_qk, dk_r, p->d_qk, g, lo,
+                             hi, hi, p->tau, 1, s);
+         })))
+      return hip_fail(e, "xty_dk");
+    if ((e = timed("xty_dv", s, [&] {
+           return launch_xty(p_r, static_cast<const uint16_t*>(d_o), p->d_v, p->d_v, dv_r, p->d_v, g, lo,
+                             hi, hi, 1.0f, 1, s);
+         })))
+      return hip_fail(e, "xty_dv");
+  }
+  return RR_OK;
+}
+
 }  // namespace rr
 
 using namespace rr;
@@ -98,6 +148,21 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
+  if (p->latent) {
+    // index scores -> exact top-k per row -> attention over the selection + causal rows
+    float* sigma = carve(ws, 0);
+    hipError_t e = timed("index_scores", s, [&] {
+      return launch_index_scores(q_idx, kv->k_idx, sigma, p->K * p->R_max, p->P, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "index_scores");
+    if ((e = timed("topk_select", s, [&] { return launch_topk(sigma, p->P, p->topk, g, topk_idx, s); })))
+      return hip_fail(e, "topk_select");
+    if ((e = timed("sparse_fwd", s, [&] {
+           return launch_sparse_fwd(g, p->topk, q, kv->k_p, k_r, topk_idx, o, lse, s);
+         })))
+      return hip_fail(e, "sparse_fwd");
+    return RR_OK;
+  }
   float* po = part_o;
   float* pl = part_lse;
   if (!po) {
@@ -147,6 +212,8 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
+  if (p->latent) return latent_bwd(p, kv, q, k_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r,
+                                   accumulate, block_idx, ws, s);
   float* Dvec = carve(ws, 0);
   float* dq_part = carve(ws, align_up(rows * sizeof(float), 256));
   AttnPtrs a{};

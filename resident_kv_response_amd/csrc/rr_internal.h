@@ -35,6 +35,7 @@ int64_t n_chunks_of(const rr_problem* p);
 int32_t n_parts_of(const rr_problem* p);
 size_t ws_fwd_bytes(const rr_problem* p, bool exported);
 size_t ws_bwd_bytes(const rr_problem* p);
+size_t ws_pds_bytes(const rr_problem* p);
 int validate_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
                  const void* v_r, const int32_t* r_len, const float* q_idx, const float* o,
                  const float* lse, const float* part_o, const float* part_lse,

@@ -44,7 +44,17 @@ int validate_problem(const rr_problem* p) {
   if (p->topk < 0) return set_error(RR_E_SHAPE, "topk must be >= 0");
   if (p->flags & ~RR_FLAG_SHARD_NO_RESPONSE) return set_error(RR_E_SHAPE, "unknown flags 0x%x", p->flags);
   if (p->latent) {
-    return set_error(RR_E_UNSUPPORTED, "latent pages are not supported by this build");
+    if (p->dtype != RR_BF16) return set_error(RR_E_UNSUPPORTED, "latent pages need bf16 inputs");
+    if (p->d_qk != 576 || p->d_v != 512 || p->Hkv != 1 || p->Hq != 64)
+      return set_error(RR_E_UNSUPPORTED, "latent pages are built for d_qk=576, d_v=512, Hkv=1, Hq=64 "
+                       "(got %d, %d, %d, %d)", p->d_qk, p->d_v, p->Hkv, p->Hq);
+    if (p->topk < 32 || p->topk % 32 != 0 || p->topk > p->P)
+      return set_error(RR_E_SHAPE, "latent top-k must be a multiple of 32 in [32, P] (got %d)", p->topk);
+    if (p->idx_dim != 128) return set_error(RR_E_UNSUPPORTED, "index keys must be 128 wide (got %d)", p->idx_dim);
+    if (p->R_max % 8 != 0) return set_error(RR_E_SHAPE, "latent pages need R_max %% 8 == 0");
+    if (p->flags) return set_error(RR_E_UNSUPPORTED, "shard flags are not built for latent pages");
+    if ((int64_t)p->K * p->R_max > (1 << 20)) return set_error(RR_E_SHAPE, "K*R_max too large");
+    return RR_OK;
   }
   if (p->topk != 0)
     return set_error(RR_E_UNSUPPORTED, "top-k selection needs latent pages");
@@ -74,13 +84,20 @@ static int check_aligned(const char* what, std::initializer_list<const void*> pt
 static size_t rows_total(const rr_problem* p) { return (size_t)p->K * p->R_max * p->Hq; }
 
 size_t ws_fwd_bytes(const rr_problem* p, bool exported) {
+  if (p->latent) return align_up((size_t)p->K * p->R_max * (size_t)p->P * sizeof(float), 256);
   if (exported) return 0;
   const size_t n = (size_t)n_parts_of(p) * rows_total(p);
   return align_up(n * p->d_v * sizeof(float), 256) + align_up(n * sizeof(float), 256);
 }
 
+size_t ws_pds_bytes(const rr_problem* p) {
+  // response-pair P or dS, [K][R][Hq][R] bf16, plus one 128-key row segment of padding
+  return align_up(((size_t)p->K * p->R_max * p->Hq * p->R_max + 128) * sizeof(uint16_t), 256);
+}
+
 size_t ws_bwd_bytes(const rr_problem* p) {
   const size_t rows = rows_total(p);
+  if (p->latent) return align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p);
   return align_up(rows * sizeof(float), 256) +
          align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256);
 }
@@ -95,7 +112,7 @@ static int check_r_len(const rr_problem* p, const int32_t* r_len) {
 
 static int check_resident(const rr_problem* p, const rr_resident* kv) {
   if (!kv) return set_error(RR_E_NULL, "resident is NULL");
-  if (!kv->k_p || !kv->v_p) return set_error(RR_E_NULL, "resident k_p / v_p is NULL");
+  if (!kv->k_p || (!kv->v_p && !p->latent)) return set_error(RR_E_NULL, "resident k_p / v_p is NULL");
   if (kv->P != p->P)
     return set_error(RR_E_SHAPE, "resident P (%lld) != problem P (%lld)", (long long)kv->P,
                      (long long)p->P);
@@ -107,12 +124,22 @@ int validate_fwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
                  const float* lse, const float* part_o, const float* part_lse,
                  const int32_t* topk_idx, const void* ws, size_t ws_bytes) {
   (void)q_idx;
-  (void)topk_idx;
   int rc = validate_problem(p);
   if (rc) return rc;
   if ((rc = check_resident(p, kv))) return rc;
-  if (!q || !k_r || !v_r) return set_error(RR_E_NULL, "q / k_r / v_r is NULL");
+  if (!q || !k_r || (!v_r && !p->latent)) return set_error(RR_E_NULL, "q / k_r / v_r is NULL");
   if ((rc = check_r_len(p, r_len))) return rc;
+  if (p->latent) {
+    if (!q_idx || !kv->k_idx || !topk_idx) return set_error(RR_E_NULL, "q_idx / k_idx / topk_idx is NULL");
+    if (!o || !lse) return set_error(RR_E_NULL, "o and lse are required for latent pages");
+    if (part_o || part_lse) return set_error(RR_E_UNSUPPORTED, "partials export is not built for latent pages");
+    if ((rc = check_aligned("q / k_r / latent / q_idx / k_idx / o", {q, k_r, kv->k_p, q_idx, kv->k_idx, o})))
+      return rc;
+    const size_t need = ws_fwd_bytes(p, false);
+    if (!ws || ws_bytes < need)
+      return set_error(RR_E_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes, ws ? "" : ", NULL");
+    return RR_OK;
+  }
   if ((o == nullptr) != (lse == nullptr))
     return set_error(RR_E_NULL, "o and lse must both be given or both be NULL");
   if ((part_o == nullptr) != (part_lse == nullptr))
@@ -132,12 +159,12 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
                  const float* o, const float* lse, const void* d_o, const float* dq,
                  const float* dk_r, const float* dv_r, int32_t accumulate, int32_t block_idx,
                  const void* ws, size_t ws_bytes) {
-  (void)topk_idx;
   int rc = validate_problem(p);
   if (rc) return rc;
   if ((rc = check_resident(p, kv))) return rc;
-  if (!q || !k_r || !v_r || !o || !lse || !d_o)
+  if (!q || !k_r || (!v_r && !p->latent) || !o || !lse || !d_o)
     return set_error(RR_E_NULL, "q / k_r / v_r / o / lse / d_o is NULL");
+  if (p->latent && !topk_idx) return set_error(RR_E_NULL, "topk_idx is NULL");
   const bool owns_resp = !(p->flags & RR_FLAG_SHARD_NO_RESPONSE);
   if (!dq || (owns_resp && (!dk_r || !dv_r))) return set_error(RR_E_NULL, "dq / dk_r / dv_r is NULL");
   if ((rc = check_r_len(p, r_len))) return rc;

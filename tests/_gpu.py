@@ -84,3 +84,47 @@ def oracle_member(dense, dtype, k_p, v_p, stacked, kk, rl, tau, rows=None, grads
     if grads:
         out.update(dense.attend_bwd(q, kp, vp, kr, vr, do, tau, rows=rows))
     return out
+
+
+class LatentRun:
+    """Device copies of a latent-page problem (one or more responses) and its outputs."""
+
+    def __init__(self, prob, latent_p, k_idx, q, latent_r, q_idx, d_o, r_len):
+        self.p, self.r_len = prob, [int(x) for x in r_len]
+        self.latent_p = to_dev(latent_p, "bf16")
+        self.k_idx = to_dev(k_idx, "f32")
+        self.q, self.latent_r, self.d_o = to_dev(q, "bf16"), to_dev(latent_r, "bf16"), to_dev(d_o, "bf16")
+        self.q_idx = to_dev(q_idx, "f32")
+        self.kv = R.resident(self.latent_p, None, version=0, k_idx=self.k_idx)
+        K, Rm = prob.K, prob.R_max
+        f = dict(device=DEV, dtype=torch.float32)
+        self.o = torch.full((K, Rm, prob.Hq, prob.d_v), float("nan"), **f)
+        self.lse = torch.full((K, Rm, prob.Hq), float("nan"), **f)
+        self.idx = torch.full((K, Rm, prob.topk), -7, device=DEV, dtype=torch.int32)
+        self.dq = torch.full((K, Rm, prob.Hq, prob.d_qk), float("nan"), **f)
+        self.dk = torch.full((K, Rm, prob.d_qk), float("nan"), **f)
+        self.dv = torch.full((K, Rm, prob.d_v), float("nan"), **f)
+        self.ws_f = R.workspace(prob, R.RR_OP_FWD, DEV)
+        self.ws_b = R.workspace(prob, R.RR_OP_BWD, DEV)
+
+    def fwd(self):
+        R.rr_attn_fwd(self.p, self.kv, self.q, self.latent_r, None, self.r_len, o=self.o, lse=self.lse,
+                      q_idx=self.q_idx, topk_idx=self.idx, ws=self.ws_f)
+        return self
+
+    def bwd(self, accumulate=0, block_idx=-1):
+        R.rr_attn_bwd(self.p, self.kv, self.q, self.latent_r, None, self.r_len, self.o, self.lse,
+                      self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate, block_idx=block_idx,
+                      topk_idx=self.idx, ws=self.ws_b)
+        return self
+
+    def numpy(self):
+        torch.cuda.synchronize()
+        out = {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
+        out["idx"] = self.idx.cpu().numpy()
+        return out
+
+
+def latent_problem(P, R_max, topk, block, K=1):
+    return R.Problem(P=P, R_max=R_max, Hq=64, Hkv=1, d_qk=576, d_v=512, chunk=P, block=block,
+                     tau=float(1.0 / np.sqrt(576)), dtype=R.RR_BF16, K=K, topk=topk, idx_dim=128, latent=1)
