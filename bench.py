@@ -7,6 +7,10 @@ ordered reduction, reverse block walk for response dK/dV) and rr_grad_accum of d
 into position-aligned fp32 accumulators (zeroed at the start of the group).  All inputs
 are synthetic (seeded N(0,1), rounded to bf16) and resident in HBM before timing starts.
 
+With --workload bf16_latent_P1048576_R4096_top2048 a step is one response of the
+latent-page top-k variant: fp32 index scores, exact top-2048 selection, sparse attention
+forward and response-only backward (64 heads sharing 576-wide latent rows).
+
 Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step; `roofline` is
 measured live for the kernel with the largest device time, from HIP events the library
 records around every launch in the timed region.
@@ -26,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -90,11 +95,19 @@ def main() -> int:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
         return 2
+    from resident_kv_response_amd import configs
+
+    w = configs.BY_NAME[a.workload]
+    if w.latent:
+        return run_latent(a, w)
+    return run_dense(a, w)
+
+
+def run_dense(a, w) -> int:
     import torch
 
     from resident_kv_response_amd import configs, rr_attn as R, synth
 
-    w = configs.BY_NAME[a.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     lens = synth.response_lengths(w) if w.G > 1 else np.array([w.R])
@@ -259,6 +272,199 @@ def main() -> int:
         "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
         "peak_mem_bytes": {"after_1_member": int(mem_g1), "timed_G_groups": int(mem_g8)},
         "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if (parity is None or parity["pass"]) else 1
+
+
+LATENT_SOURCES = {
+    "index_scores": ["k_topk.hip", "k_common.h"],
+    "topk_select": ["k_topk.hip", "k_common.h"],
+    "sparse_fwd": ["k_sparse.hip", "k_lds.h", "k_common.h"],
+    "sparse_dq": ["k_sparse.hip", "k_lds.h", "k_common.h"],
+    "xty_dk": ["k_sparse.hip", "k_lds.h", "k_common.h"],
+    "xty_dv": ["k_sparse.hip", "k_lds.h", "k_common.h"],
+}
+
+
+def latent_kernel_model(w, R: int) -> dict:
+    """Algorithmic flops / HBM bytes of each launch kind for one response of length R of
+    the latent-page variant.  Bytes count each selected latent row once per query row
+    (the gather), every other operand once; response rows re-read by later query rows
+    are not counted (they are a few MB and stay in cache)."""
+    H, dk, dv, P, k, di = w.Hq, w.d_qk, w.d_v, w.P, w.topk, w.idx_dim
+    n_p, n_r = R * k, R * (R + 1) // 2
+    row = dk * 2
+    q_b, do_b = R * H * dk * 2, R * H * dv * 2
+    return {
+        "index_scores": {"flops": 2.0 * di * R * P, "peak": PEAK_F32_TFLOPS,
+                         "bytes": P * di * 4 + R * di * 4 + R * P * 4},
+        "topk_select": {"flops": 0.0, "peak": None, "bytes": R * P * 4 + R * k * 4},
+        "sparse_fwd": {"flops": H * (2.0 * dk + 2.0 * dv) * (n_p + n_r), "peak": PEAK_BF16_TFLOPS,
+                       "bytes": n_p * row + R * row + q_b + R * H * (dv + 1) * 4 + R * k * 4},
+        "sparse_dq": {"flops": H * (4.0 * dk + 2.0 * dv) * (n_p + n_r), "peak": PEAK_BF16_TFLOPS,
+                      "bytes": n_p * row + R * row + q_b + do_b + R * H * dk * 4 + 2 * H * n_r * 2},
+        "xty_dk": {"flops": H * 2.0 * dk * n_r, "peak": PEAK_BF16_TFLOPS,
+                   "bytes": H * n_r * 2 + q_b + R * dk * 4},
+        "xty_dv": {"flops": H * 2.0 * dv * n_r, "peak": PEAK_BF16_TFLOPS,
+                   "bytes": H * n_r * 2 + do_b + R * dv * 4},
+    }
+
+
+def roofline_entry(name, model, launches_per_step, avg_ms, traffic):
+    """The bound with the longer ideal time decides: MFMA (flops / peak) or HBM (bytes /
+    8 TB/s)."""
+    t_f = model["flops"] / (model["peak"] * 1e12) if model["peak"] else 0.0
+    t_b = model["bytes"] / (PEAK_HBM_GBS * 1e9)
+    per = 1.0 / launches_per_step
+    if t_f >= t_b:
+        ach = model["flops"] * per / (avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": name, "achieved": round(ach, 2), "peak": model["peak"],
+                "unit": "TFLOP/s", "frac": round(ach / model["peak"], 4), "traffic": traffic,
+                "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": model["flops"] * per,
+                "algorithmic_bytes_per_launch": model["bytes"] * per}
+    ach = model["bytes"] * per / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": name, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "avg_launch_ms": round(avg_ms, 4), "algorithmic_bytes_per_launch": model["bytes"] * per,
+            "flops_per_launch": model["flops"] * per}
+
+
+def run_latent(a, w) -> int:
+    import torch
+
+    from resident_kv_response_amd import configs, rr_attn as R, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    Rr = w.R
+    t0 = time.time()
+    res = synth.resident(w)
+    m0 = synth.member(w, 0)
+
+    def up(x, dt="bf16"):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    lat_p, k_idx = up(res["latent_p"]), up(res["k_idx"], "f32")
+    q, lat_r, d_o = up(m0["q"])[None], up(m0["latent_r"])[None], up(m0["d_o"])[None]
+    q_idx = up(m0["q_idx"], "f32")[None]
+    gen_s = time.time() - t0
+    kv = R.resident(lat_p, None, version=1, k_idx=k_idx)
+    prob = R.Problem(P=w.P, R_max=Rr, Hq=w.Hq, Hkv=1, d_qk=w.d_qk, d_v=w.d_v, chunk=w.chunk,
+                     block=w.block, tau=w.tau, dtype=R.RR_BF16, K=1, topk=w.topk, idx_dim=w.idx_dim,
+                     latent=1)
+    ws_f = R.workspace(prob, R.RR_OP_FWD, dev)
+    ws_b = R.workspace(prob, R.RR_OP_BWD, dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    o = torch.empty(1, Rr, w.Hq, w.d_v, **f32)
+    lse = torch.empty(1, Rr, w.Hq, **f32)
+    idx = torch.empty(1, Rr, w.topk, device=dev, dtype=torch.int32)
+    dq = torch.empty(1, Rr, w.Hq, w.d_qk, **f32)
+    dk = torch.empty(1, Rr, w.d_qk, **f32)
+    dv = torch.empty(1, Rr, w.d_v, **f32)
+
+    def step():
+        R.rr_attn_fwd(prob, kv, q, lat_r, None, [Rr], o=o, lse=lse, q_idx=q_idx, topk_idx=idx, ws=ws_f)
+        R.rr_attn_bwd(prob, kv, q, lat_r, None, [Rr], o, lse, d_o, dq, dk, dv, topk_idx=idx, ws=ws_b)
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    step()
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w.seed, Rr, a.cpu_rows, w.block) if a.cpu_rows > 0 else None
+    got = None
+    if rows is not None:
+        got = {"o": o[0, rows].double().cpu().numpy(), "dq": dq[0, rows].double().cpu().numpy(),
+               "idx": idx[0, rows].cpu().numpy()}
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    R.rr_profile_begin()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    prof = R.rr_profile_end()
+    peak_mem = torch.cuda.max_memory_allocated()
+    ms_per_step = (t2 - t1) * 1e3 / a.steps
+
+    flops_step = configs.flops_dense(w.Hq, w.d_qk, w.d_v, Rr, w.topk)["total"]
+    index_flops = 2.0 * w.idx_dim * Rr * w.P
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    model = latent_kernel_model(w, Rr)
+    dom_name, (dom_launches, dom_ms) = max(prof.items(), key=lambda kv_: kv_[1][1])
+    roof = None
+    if dom_name in model:
+        roof = roofline_entry(dom_name, model[dom_name], dom_launches / a.steps, dom_ms / dom_launches,
+                              traffic_from_profiles(dom_name, w.name, source_sha(LATENT_SOURCES[dom_name])))
+    kernels = {}
+    for k, v in sorted(prof.items(), key=lambda kv_: -kv_[1][1]):
+        e = {"launches_per_step": v[0] / a.steps, "ms_per_step": round(v[1] / a.steps, 3)}
+        if k in model:
+            t = v[1] / a.steps * 1e-3
+            if model[k]["flops"]:
+                e["tflops"] = round(model[k]["flops"] / t / 1e12, 2)
+            e["gbs"] = round(model[k]["bytes"] / t / 1e9, 1)
+        kernels[k] = e
+
+    cpu = parity = None
+    if rows is not None:
+        from oracle import sparse
+        f = lambda x: synth.as_f64(x, "bf16")
+        tc = time.perf_counter()
+        sig = sparse.index_scores(m0["q_idx"][rows], res["k_idx"])
+        sel = np.zeros((Rr, w.topk), dtype=np.int64)
+        sel[rows] = sparse.topk_select(sig, w.topk)
+        lp, qq, lr, do = f(res["latent_p"]), f(m0["q"]), f(m0["latent_r"]), f(m0["d_o"])
+        ro, _ = sparse.sparse_attend(qq, lp, lr, sel, w.tau, w.d_v, rows=rows)
+        rgr = sparse.sparse_attend_bwd(qq, lp, lr, sel, do, w.tau, w.d_v, rows=rows)
+        cpu_s = time.perf_counter() - tc
+        # the same attention flops per row as the GPU value counts (the index scoring's
+        # time is included, its flops are not, on both sides)
+        H, dqk, dvv = w.Hq, w.d_qk, w.d_v
+        cpu_flops = sum(H * ((2.0 * dqk + 2.0 * dvv) * (w.topk + int(r) + 1) + (4.0 * dqk + 2.0 * dvv) * w.topk
+                             + (6.0 * dqk + 4.0 * dvv) * (int(r) + 1)) for r in rows)
+        cores = len(os.sched_getaffinity(0))
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            blas_threads = None
+        cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": blas_threads or cores, "kind": "oracle",
+               "sample": f"{len(rows)} query rows {list(map(int, rows))} of the R={Rr} response: index "
+                         f"scores over all {w.P} positions, top-{w.topk}, sparse attention fwd + bwd "
+                         f"(64 heads); {cpu_s:.1f} s incl. widening the inputs to fp64",
+               "host_cpus_affinity": cores, "host_cpu_count": os.cpu_count(),
+               "extrapolated_full_step_s": round(flops_step / (cpu_flops / cpu_s), 1)}
+        same = [n for n, r in enumerate(rows) if np.array_equal(got["idx"][n], sel[r])]
+        rel = lambda x, y: float(np.linalg.norm(x - y) / np.linalg.norm(y))
+        parity = {"rows": len(rows), "rows_with_identical_selection": len(same)}
+        if same:
+            s_ = np.array(same)
+            parity.update({"o_rel_l2": rel(got["o"][s_], ro[s_]), "dq_rel_l2": rel(got["dq"][s_], rgr["dq"][s_]),
+                           "o_max_abs": float(np.abs(got["o"][s_] - ro[s_]).max()),
+                           "dq_max_abs": float(np.abs(got["dq"][s_] - rgr["dq"][s_]).max())})
+        parity["pass"] = bool(len(same) >= len(rows) // 2 and parity.get("o_rel_l2", 1) <= 5e-3
+                              and parity.get("dq_rel_l2", 1) <= 5e-3 and parity.get("o_max_abs", 1) <= 2e-2
+                              and parity.get("dq_max_abs", 1) <= 2e-2)
+
+    out = {
+        "metric": "response-replay attention fwd+bwd TFLOP/s + % bf16 MFMA peak (latent top-k variant)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "P": w.P, "R": Rr, "Hq": w.Hq, "latent": [w.d_v, w.d_qk - w.d_v],
+                   "topk": w.topk, "idx_dim": w.idx_dim, "block": w.block,
+                   "attention_flops_per_step": flops_step, "index_flops_fp32_per_step": index_flops},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(Rr / (ms_per_step * 1e-3), 1),
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
+        "peak_mem_bytes": int(peak_mem), "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)
     return 0 if (parity is None or parity["pass"]) else 1

@@ -53,4 +53,30 @@ Geom make_geom(const rr_problem* p, const int32_t* r_len);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Plan of the per-row top-k selection over P fp32 scores (k_topk.hip).  Fast path: a
+// sample of kTopkSample scores gives a threshold expected to keep about 3k positions
+// (at least 32 sample ranks above it); one pass keeps the positions at or above it as
+// candidates (at most `cap`), and the exact k-th largest is selected among them.  A row
+// whose candidate count falls outside [k, cap] takes the exact full-row path instead.
+constexpr int kTopkSample = 8192;
+constexpr int kTopkSortMax = 4096;
+struct TopkPlan {
+  int fast;            // 1: sample + candidate path available for this (P, k)
+  int sample_rank;     // descending rank in the sample that sets the threshold
+  int cap;             // candidate slots per row
+  int64_t ld;          // score row stride (P rounded up to a multiple of 4)
+};
+inline TopkPlan topk_plan(int64_t P, int k) {
+  TopkPlan t{};
+  t.ld = (P + 3) / 4 * 4;
+  const int64_t rs = (3 * (int64_t)k * kTopkSample + P - 1) / P;
+  t.sample_rank = (int)(rs < 32 ? 32 : rs);
+  t.fast = P >= 8 * (int64_t)kTopkSample && k <= kTopkSortMax && t.sample_rank <= kTopkSample / 4;
+  if (t.fast) {
+    const int64_t expect = (int64_t)t.sample_rank * P / kTopkSample;   // candidates expected
+    t.cap = (int)((2 * expect + 1024 + 255) / 256 * 256);
+  }
+  return t;
+}
+
 }  // namespace rr

@@ -84,7 +84,13 @@ static int check_aligned(const char* what, std::initializer_list<const void*> pt
 static size_t rows_total(const rr_problem* p) { return (size_t)p->K * p->R_max * p->Hq; }
 
 size_t ws_fwd_bytes(const rr_problem* p, bool exported) {
-  if (p->latent) return align_up((size_t)p->K * p->R_max * (size_t)p->P * sizeof(float), 256);
+  if (p->latent) {
+    // fp32 index scores [K*R][ld], then candidate keys and positions [K*R][cap] each
+    const TopkPlan t = topk_plan(p->P, p->topk);
+    const size_t rows = (size_t)p->K * p->R_max;
+    return align_up(rows * (size_t)t.ld * sizeof(float), 256) +
+           (t.fast ? 2 * align_up(rows * (size_t)t.cap * sizeof(uint32_t), 256) : 0);
+  }
   if (exported) return 0;
   const size_t n = (size_t)n_parts_of(p) * rows_total(p);
   return align_up(n * p->d_v * sizeof(float), 256) + align_up(n * sizeof(float), 256);
@@ -133,7 +139,7 @@ int validate_fwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
     if (!q_idx || !kv->k_idx || !topk_idx) return set_error(RR_E_NULL, "q_idx / k_idx / topk_idx is NULL");
     if (!o || !lse) return set_error(RR_E_NULL, "o and lse are required for latent pages");
     if (part_o || part_lse) return set_error(RR_E_UNSUPPORTED, "partials export is not built for latent pages");
-    if ((rc = check_aligned("q / k_r / latent / q_idx / k_idx / o", {q, k_r, kv->k_p, q_idx, kv->k_idx, o})))
+    if ((rc = check_aligned("q / k_r / latent / q_idx / k_idx / o / ws", {q, k_r, kv->k_p, q_idx, kv->k_idx, o, ws})))
       return rc;
     const size_t need = ws_fwd_bytes(p, false);
     if (!ws || ws_bytes < need)
@@ -169,8 +175,8 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
   if (!dq || (owns_resp && (!dk_r || !dv_r))) return set_error(RR_E_NULL, "dq / dk_r / dv_r is NULL");
   if ((rc = check_r_len(p, r_len))) return rc;
   if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
-  if ((rc = check_aligned("q / k_r / v_r / k_p / v_p / o / d_o / dq / dk_r / dv_r",
-                          {q, k_r, v_r, kv->k_p, kv->v_p, o, d_o, dq, dk_r, dv_r})))
+  if ((rc = check_aligned("q / k_r / v_r / k_p / v_p / o / d_o / dq / dk_r / dv_r / ws",
+                          {q, k_r, v_r, kv->k_p, kv->v_p, o, d_o, dq, dk_r, dv_r, ws})))
     return rc;
   const int32_t nb = (p->R_max + p->block - 1) / p->block;
   if (block_idx < -1 || block_idx >= nb)

@@ -67,6 +67,50 @@ def test_sparse_exact_selection_every_element(P, R, topk, block):
     assert_bf16_close("dv_r", got["dv"][0], gr["dv_r"])
 
 
+def test_sparse_exact_selection_large_rows_with_ties():
+    """Rows long enough for the sampled-threshold path; integer index data puts hundreds of
+    positions on the k-th largest score, so the tie rule decides part of every row."""
+    P, R, topk = 131072, 64, 2048
+    d = _data(8100, P, R, integer_index=True)
+    print(f"[sparse] large rows P={P} R={R} topk={topk}", flush=True)
+    got = _run(d, P, R, topk, 32)
+    sel, sig, o, lse, gr = _oracle(d, topk)
+    kth = np.sort(sig, axis=1)[:, -topk]
+    assert np.min(np.sum(sig == kth[:, None], axis=1)) > 1      # ties at the threshold exist
+    np.testing.assert_array_equal(got["idx"][0], sel)
+    assert_bf16_close("o", got["o"][0], o)
+    assert_bf16_close("dq", got["dq"][0], gr["dq"])
+    assert_bf16_close("dk_r", got["dk"][0], gr["dk_r"])
+
+
+def _structured_index(kind, P, R, seed):
+    """Index data whose scores are small exact integers with a chosen structure."""
+    g = np.random.default_rng(seed)
+    q_idx = np.zeros((R, 128), dtype=np.float32)
+    q_idx[:, 0] = 1.0
+    k_idx = np.zeros((P, 128), dtype=np.float32)
+    if kind == "increasing":          # score = position: the top k are the last k positions
+        k_idx[:, 0] = np.arange(P, dtype=np.float32)
+        q_idx[1::2, 0] = -1.0         # odd rows: decreasing, the top k are the first k
+    elif kind == "constant":          # every score equal: the k lowest positions
+        k_idx[:, 0] = 5.0
+    elif kind == "two_levels":        # 10% of positions score 1, far more than k tied at T
+        k_idx[:, 0] = (g.random(P) < 0.1).astype(np.float32)
+    return q_idx, k_idx
+
+
+@pytest.mark.parametrize("kind", ["increasing", "constant", "two_levels"])
+def test_sparse_selection_structured_scores(kind):
+    P, R, topk = 131072, 8, 2048
+    d = _data(8200, P, R, integer_index=True)
+    d["q_idx"], d["k_idx"] = _structured_index(kind, P, R, 8201)
+    print(f"[sparse] structured scores {kind}", flush=True)
+    got = _run(d, P, R, topk, 8)
+    sel, sig, o, lse, gr = _oracle(d, topk)
+    np.testing.assert_array_equal(got["idx"][0], sel)
+    assert_bf16_close("o", got["o"][0], o)
+
+
 def test_sparse_latent_full_size_sampled_rows():
     w = configs.LATENT_P1M
     res = synth.resident(w)
