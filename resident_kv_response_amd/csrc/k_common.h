@@ -45,6 +45,15 @@ __device__ __forceinline__ void prio_valu() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier(mask, count, sync_id): a
+// sequence of such calls at the end of a basic block asks the scheduler to order the
+// block's instructions in that pattern (e.g. one MFMA, then a few vector ops, repeated),
+// so that a wave keeps issuing vector work while its matrix-core operations run.
+#define RR_SG_MFMA 0x008
+#define RR_SG_VALU 0x002
+#define RR_SG_DS_READ 0x100
+#define RR_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
 // 16-byte vector <-> 8 bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 

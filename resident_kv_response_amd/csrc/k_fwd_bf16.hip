@@ -141,6 +141,141 @@ __device__ __forceinline__ void pv_accumulate(const Frag<D>& fr, const char* Vt,
   prio_valu();
 }
 
+// Softmax of one unmasked 32-key subtile (one 32-row N-tile): P^T as bf16 MFMA operands
+// in pf, and alpha, the factor the accumulators must be scaled by when the reference
+// maximum moved (returned wave-uniform flag; alpha = 1 otherwise).  Branch-free, so it
+// can share a basic block with the MFMAs it is scheduled against.
+__device__ __forceinline__ bool softmax_plain(const f32x16& s, float c2, float& m_run, float& l_run,
+                                              float& alpha, bf16x8 (&pf)[2]) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+  mx = fmaxf(mx, s[15]);
+  mx = pair_max(mx);
+  const float m_new = fmaxf(m_run, mx * c2);
+  const bool grow = __any(m_new > m_run + kRescaleThreshold);
+  const float m_use = grow ? m_new : m_run;
+  alpha = fast_exp2(m_run - m_use);
+  m_run = m_use;
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], c2, -m_use));
+  float ls = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ls += p[i];
+  l_run = fmaf(l_run, alpha, ls);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    uint4 u;
+    u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
+    u.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
+    u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
+    u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
+    pf[h2] = as_bf16x8(u);
+  }
+  return grow;
+}
+
+template <int D>
+__device__ __forceinline__ void scale_acc(f32x16 (&acc)[D / 32], float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+}
+
+// S^T of subtile `sub` for the wave's NT N-tiles: each K row fragment is read once and
+// feeds NT MFMAs.
+template <int D, int NT>
+__device__ __forceinline__ void mma_scores(const Frag<D>& fr, const char* Kt, int sub,
+                                           const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = fr.row(Kt, sub, ks);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf[ks], qf[t][ks], s[t]);
+}
+
+// O^T += V^T P^T of subtile `sub` for the wave's NT N-tiles (each V^T fragment feeds NT
+// MFMAs).
+template <int D, int NT>
+__device__ __forceinline__ void mma_pv(const Frag<D>& fr, const char* Vt, int sub, const bf16x8 (&pf)[NT][2],
+                                       f32x16 (&acc)[NT][D / 32]) {
+  bf16x8 vf[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = fr.trans_frag(Vt, sub, h2, dt);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf[dt][h2], pf[t][h2], acc[t][dt]);
+}
+
+// Softmax of the NT tiles of one subtile; true when any reference maximum moved (the
+// accumulators of tile t must then be scaled by alpha[t], which is 1 for tiles that did
+// not move).
+template <int NT>
+__device__ __forceinline__ bool softmax_tiles(const f32x16 (&s)[NT], float c2, float (&m_run)[NT],
+                                              float (&l_run)[NT], float (&alpha)[NT], bf16x8 (&pf)[NT][2]) {
+  bool grow = false;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) grow |= softmax_plain(s[t], c2, m_run[t], l_run[t], alpha[t], pf[t]);
+  return grow;
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void scale_tiles(f32x16 (&acc)[NT][D / 32], const float (&alpha)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) scale_acc<D>(acc[t], alpha[t]);
+}
+
+// Schedules of the pipelined stage's basic blocks: (D/16) K-fragment reads and D/16 * NT
+// MFMAs per S^T, (D/8) V^T reads and D/16 * NT MFMAs per PV.  Operand reads run a few
+// MFMAs ahead of their use (not all up front, which would hold every fragment in
+// registers at once), and each MFMA is followed by a share of the softmax's vector work.
+template <int D, int NT>
+__device__ __forceinline__ void sched_s_softmax() {      // S(j+1) with softmax(j)
+  constexpr int NM = D / 16 * NT;
+  RR_SCHED_GROUP(RR_SG_DS_READ, 4);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    RR_SCHED_GROUP(RR_SG_MFMA, 1);
+    if (i % NT == NT - 1 && i / NT < D / 16 - 4) RR_SCHED_GROUP(RR_SG_DS_READ, 1);
+    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 9 : 7);
+  }
+}
+template <int D, int NT>
+__device__ __forceinline__ void sched_s_pv_softmax() {   // S(j+1) and PV(j-1) with softmax(j)
+  constexpr int NM = D / 8 * NT, READS = D / 16 - 4 + D / 8, PER = NT == 1 ? 2 : 1;
+  RR_SCHED_GROUP(RR_SG_DS_READ, 4);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    RR_SCHED_GROUP(RR_SG_MFMA, 1);
+    if (i < READS / PER) RR_SCHED_GROUP(RR_SG_DS_READ, PER);
+    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 5 : 4);
+  }
+}
+template <int D, int NT>
+__device__ __forceinline__ void sched_pv_softmax() {     // PV(j-1) with softmax(j)
+  constexpr int NM = D / 16 * NT, READS = D / 8 - 6, PER = NT == 1 ? 2 : 1;
+  RR_SCHED_GROUP(RR_SG_DS_READ, 6);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    RR_SCHED_GROUP(RR_SG_MFMA, 1);
+    if (i < READS / PER) RR_SCHED_GROUP(RR_SG_DS_READ, PER);
+    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 9 : 8);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
@@ -237,6 +372,34 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
     const char* Vt = cur + C::TILE;
     const int rel0 = it * C::BN;
     if (rel0 > wmax) return;
+    if (C::NSUB == 4 && rel0 + C::BN - 1 <= wmin) {
+      // every key of the stage is visible to every row of the wave: software-pipelined
+      // subtiles, S(j+1) and PV(j-1) on the matrix cores while the softmax of j runs
+      f32x16 sa[NT], sb[NT];
+      bf16x8 pa[NT][2], pb[NT][2];
+      float alpha[NT];
+      mma_scores<D, NT>(fr, Kt, 0, qf, sa);
+      mma_scores<D, NT>(fr, Kt, 1, qf, sb);
+      bool grow = softmax_tiles<NT>(sa, g.c2, m_run, l_run, alpha, pa);
+      sched_s_softmax<D, NT>();
+      if (grow) scale_tiles<D, NT>(acc, alpha);
+      mma_scores<D, NT>(fr, Kt, 2, qf, sa);
+      mma_pv<D, NT>(fr, Vt, 0, pa, acc);
+      grow = softmax_tiles<NT>(sb, g.c2, m_run, l_run, alpha, pb);
+      sched_s_pv_softmax<D, NT>();
+      if (grow) scale_tiles<D, NT>(acc, alpha);
+      mma_scores<D, NT>(fr, Kt, 3, qf, sb);
+      mma_pv<D, NT>(fr, Vt, 1, pb, acc);
+      grow = softmax_tiles<NT>(sa, g.c2, m_run, l_run, alpha, pa);
+      sched_s_pv_softmax<D, NT>();
+      if (grow) scale_tiles<D, NT>(acc, alpha);
+      mma_pv<D, NT>(fr, Vt, 2, pa, acc);
+      grow = softmax_tiles<NT>(sb, g.c2, m_run, l_run, alpha, pb);
+      sched_pv_softmax<D, NT>();
+      if (grow) scale_tiles<D, NT>(acc, alpha);
+      mma_pv<D, NT>(fr, Vt, 3, pb, acc);
+      return;
+    }
     f32x16 s_cur[NT];
     scores_T<D, NT>(fr, Kt, 0, qf, s_cur);
 #pragma unroll
