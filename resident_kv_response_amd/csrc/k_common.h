@@ -30,6 +30,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Sum of the 8 bf16 values of two packed MFMA operands (x + (lo + hi) per pair, fp32),
+// by v_dot2c_f32_bf16 against (1, 1): half the instructions of 16 fp32 adds, and the sum
+// is that of exactly the rounded values the MFMA consumes.
+__device__ __forceinline__ float sum_bf16x8(uint4 u, float x) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.x), one, x, false);
+  x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one, x, false);
+  x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one, x, false);
+  x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one, x, false);
+  return x;
+}
+
 // Wave priority around matrix-core blocks: with two waves per SIMD, the wave that has
 // MFMAs to issue goes first, and the other wave's vector work fills the matrix core's
 // busy cycles.  The scheduling barriers keep the compiler from moving instructions

@@ -15,7 +15,8 @@
 // Per 32-key subtile and 32-row N-tile: S^T = K Q^T (D/16 MFMAs, K row fragments),
 // base-2 online softmax with a lazy rescale (the reference maximum only moves when a
 // row's maximum grows by more than 2^8, so every p <= 256), P^T rounded to bf16 straight
-// from the C registers, O^T += V^T P^T (D/16 MFMAs, V^T fragments by transposing LDS
+// from the C registers (the running sum l adds up those rounded values, so the
+// normaliser is the sum of exactly the weights the PV product uses), O^T += V^T P^T (D/16 MFMAs, V^T fragments by transposing LDS
 // reads).  The next subtile's S^T MFMAs are issued before the current softmax so the
 // matrix cores and the vector ALUs work at the same time.
 #include "k_attn_tile.h"
@@ -108,9 +109,6 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[NT], const int (&lim)
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[t][i], c2, -m_run[t]));
     float ls = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ls += p[i];
-    l_run[t] += ls;
-#pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       uint4 u;
       u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
@@ -118,7 +116,9 @@ __device__ __forceinline__ void online_softmax(f32x16 (&s)[NT], const int (&lim)
       u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
       u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
       pf[t][h2] = as_bf16x8(u);
+      ls = sum_bf16x8(u, ls);
     }
+    l_run[t] += ls;
   }
 }
 
@@ -162,9 +162,6 @@ __device__ __forceinline__ bool softmax_plain(const f32x16& s, float c2, float& 
   for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], c2, -m_use));
   float ls = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) ls += p[i];
-  l_run = fmaf(l_run, alpha, ls);
-#pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     uint4 u;
     u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
@@ -172,7 +169,9 @@ __device__ __forceinline__ bool softmax_plain(const f32x16& s, float c2, float& 
     u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
     u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
     pf[h2] = as_bf16x8(u);
+    ls = sum_bf16x8(u, ls);
   }
+  l_run = fmaf(l_run, alpha, ls);
   return grow;
 }
 
