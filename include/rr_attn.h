@@ -154,7 +154,7 @@ int32_t rr_num_parts(const rr_problem* p);
  * position first), and attends, for each of the 64 heads, over those latent rows plus
  * response rows 0..i (key = the 576-wide row, value = its first 512 dims).  Built for
  * bf16, Hq = 64, Hkv = 1, d_qk = 576, d_v = 512, idx_dim = 128, topk a multiple of 32 in
- * [32, P], R_max a multiple of 8, flags = 0, o and lse required, no partial export; the
+ * [32, min(P, 4096)], R_max a multiple of 8, flags = 0, o and lse required, no partial export; the
  * workspace holds the fp32 scores, K * R_max * P * 4 bytes.
  *   ws        workspace of rr_workspace_bytes(p, RR_OP_FWD) bytes (may be NULL when 0)
  */

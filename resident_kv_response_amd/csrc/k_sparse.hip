@@ -43,13 +43,15 @@ struct Lat {
 constexpr int kLatKeys = 32;
 constexpr int kLatTile = kLatKeys * Lat::ROW;        // 36,864 bytes
 constexpr int kLatInstr = kLatKeys * Lat::G / 64;    // 36 wave-wide loads per tile
+constexpr int kLatSelMax = 4096;                     // largest top-k the kernels stage in LDS
 
 // Gather keys [t0, t0 + 32) of a row's key list into `tile`: key t < n_sel is prompt row
 // sel[t], key t >= n_sel is response row t - n_sel; keys at or past n_keys are
-// redirected to key n_keys - 1 (masked by the caller).  A selected position outside
-// [0, P) is clamped into it, so a corrupt index list cannot address memory outside the
-// resident pages.  4 waves, 9 loads each.
-__device__ __forceinline__ void gather_tile(char* tile, const uint16_t* latent_p, int64_t P,
+// redirected to key n_keys - 1 (masked by the caller).  `sel` is the row's selection in
+// LDS, already clamped into [0, P): reading it there keeps the gathers free of waits on
+// global loads (vmcnt drains in issue order, so waiting on a global index load would
+// also wait on every gather in flight).  4 waves, 9 loads each.
+__device__ __forceinline__ void gather_tile(char* tile, const uint16_t* latent_p,
                                             const uint16_t* latent_rk, const int32_t* sel,
                                             int n_sel, int n_keys, int t0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -60,10 +62,19 @@ __device__ __forceinline__ void gather_tile(char* tile, const uint16_t* latent_p
     const int r = p / Lat::G, ph = p % Lat::G;
     const int g = (ph & ~7) | ((ph & 7) ^ Lat::f(r));
     const int t = min(t0 + r, n_keys - 1);
-    const int64_t sp = t < n_sel ? min(max((int64_t)sel[t], (int64_t)0), P - 1) : 0;
-    const uint16_t* rowp = t < n_sel ? latent_p + sp * kLatD : latent_rk + (int64_t)(t - n_sel) * kLatD;
+    const uint16_t* rowp = t < n_sel ? latent_p + (int64_t)sel[t] * kLatD : latent_rk + (int64_t)(t - n_sel) * kLatD;
     __builtin_amdgcn_global_load_lds(rowp + g * 8, (lds_void*)(tile + n * 1024), 16, 0, 0);
   }
+}
+
+// The row's selected positions, clamped into [0, P) so that a corrupt index list cannot
+// address memory outside the resident pages, staged in LDS (ends with a barrier).
+__device__ __forceinline__ void stage_selection(int32_t* sel_lds, const int32_t* sel, int n_sel, int64_t P) {
+  for (int t = threadIdx.x; t < n_sel; t += blockDim.x) {
+    const int64_t v = sel[t];
+    sel_lds[t] = (int32_t)(v < 0 ? 0 : (v >= P ? P - 1 : v));
+  }
+  __syncthreads();
 }
 
 // Row fragment of a latent tile: A[m][k] = T[l%32][16*ks + 8h .. +8].
@@ -132,6 +143,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
   __shared__ __attribute__((aligned(1024))) char kv0[kLatTile];
   __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
   __shared__ __attribute__((aligned(16))) Xch xch;
+  __shared__ int32_t sel_lds[kLatSelMax];
   const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
   const int k = row / g.R, i = row % g.R;
   if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
@@ -145,9 +157,10 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
   }
   const int n_keys = topk + i + 1;
   const int n_tiles = (n_keys + kLatKeys - 1) / kLatKeys;
-  const int32_t* sel = sel_idx + (int64_t)row * topk;
   const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
-  gather_tile(kv0, latent_p, g.P, latent_rk, sel, topk, n_keys, 0);
+  stage_selection(sel_lds, sel_idx + (int64_t)row * topk, topk, g.P);
+  const int32_t* sel = sel_lds;
+  gather_tile(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
 
   // Q fragments of this wave's 9 k-steps of the score contraction
   bf16x8 qf[9];
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
   auto tile_step = [&](const char* cur, char* nxt, int t) {
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, g.P, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
     f32x16 sp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = 0.0f;
@@ -258,6 +271,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
   __shared__ __attribute__((aligned(16))) Xch xs;
   __shared__ __attribute__((aligned(16))) Xch xp;
+  __shared__ int32_t sel_lds[kLatSelMax];
   const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
   const int k = row / g.R, i = row % g.R;
   if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
@@ -279,9 +293,10 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   }
   const int n_keys = topk + i + 1;
   const int n_tiles = (n_keys + kLatKeys - 1) / kLatKeys;
-  const int32_t* sel = sel_idx + (int64_t)row * topk;
   const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
-  gather_tile(kv0, latent_p, g.P, latent_rk, sel, topk, n_keys, 0);
+  stage_selection(sel_lds, sel_idx + (int64_t)row * topk, topk, g.P);
+  const int32_t* sel = sel_lds;
+  gather_tile(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
 
   bf16x8 qf[9], of[8];
   const int64_t hr = hrow0 + col;
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   auto tile_step = [&](const char* cur, char* nxt, int t) {
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, g.P, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
     f32x16 sp, dpp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = dpp[e] = 0.0f;

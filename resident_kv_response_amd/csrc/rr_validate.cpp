@@ -48,8 +48,9 @@ int validate_problem(const rr_problem* p) {
     if (p->d_qk != 576 || p->d_v != 512 || p->Hkv != 1 || p->Hq != 64)
       return set_error(RR_E_UNSUPPORTED, "latent pages are built for d_qk=576, d_v=512, Hkv=1, Hq=64 "
                        "(got %d, %d, %d, %d)", p->d_qk, p->d_v, p->Hkv, p->Hq);
-    if (p->topk < 32 || p->topk % 32 != 0 || p->topk > p->P)
-      return set_error(RR_E_SHAPE, "latent top-k must be a multiple of 32 in [32, P] (got %d)", p->topk);
+    if (p->topk < 32 || p->topk % 32 != 0 || p->topk > p->P || p->topk > 4096)
+      return set_error(RR_E_SHAPE, "latent top-k must be a multiple of 32 in [32, min(P, 4096)] (got %d)",
+                       p->topk);
     if (p->idx_dim != 128) return set_error(RR_E_UNSUPPORTED, "index keys must be 128 wide (got %d)", p->idx_dim);
     if (p->R_max % 8 != 0) return set_error(RR_E_SHAPE, "latent pages need R_max %% 8 == 0");
     if (p->flags) return set_error(RR_E_UNSUPPORTED, "shard flags are not built for latent pages");

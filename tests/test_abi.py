@@ -153,3 +153,59 @@ def test_accumulator_hazards_are_rejected_before_launch():
     for g in range(8):
         seen[g] = 1
     assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_OK
+
+
+def _latent(**kw):
+    base = dict(P=1048576, R_max=4096, Hq=64, Hkv=1, d_qk=576, d_v=512, chunk=65536, block=2048,
+                tau=1.0 / 24.0, dtype=R.RR_BF16, topk=2048, idx_dim=128, latent=1)
+    base.update(kw)
+    return R.Problem(**base)
+
+
+def _latent_fwd(p, q_idx=FAKE, k_idx=FAKE, topk_idx=FAKE, ws=FAKE, ws_bytes=1 << 40, part_o=None):
+    L = R.lib()
+    kv = R.CResident(k_p=FAKE, v_p=None, k_idx=k_idx, P=p.P, version=0)
+    cp = p.c()
+    arr = (ctypes.c_int32 * 1)(min(p.R_max, 8))
+    rc = L.rr_attn_fwd(ctypes.byref(cp), ctypes.byref(kv), FAKE, FAKE, None, arr, q_idx, FAKE, FAKE, part_o,
+                       FAKE if part_o else None, topk_idx, ws, ws_bytes, None)
+    return rc, L.rr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dtype=R.RR_F32), R.RR_E_UNSUPPORTED, "bf16"),
+    (dict(Hq=32), R.RR_E_UNSUPPORTED, "Hq=64"),
+    (dict(d_qk=512), R.RR_E_UNSUPPORTED, "d_qk=576"),
+    (dict(topk=2000), R.RR_E_SHAPE, "multiple of 32"),
+    (dict(topk=0), R.RR_E_SHAPE, "multiple of 32"),
+    (dict(topk=8192), R.RR_E_SHAPE, "4096"),
+    (dict(P=1000, topk=1024), R.RR_E_SHAPE, "multiple of 32"),
+    (dict(idx_dim=64), R.RR_E_UNSUPPORTED, "128 wide"),
+    (dict(R_max=4092), R.RR_E_SHAPE, "R_max"),
+    (dict(flags=R.RR_FLAG_SHARD_NO_RESPONSE), R.RR_E_UNSUPPORTED, "shard"),
+])
+def test_latent_problem_limits(kw, code, frag):
+    rc, msg = _latent_fwd(_latent(**kw))
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_latent_fwd_arguments_and_workspace():
+    p = _latent()
+    assert _latent_fwd(p, q_idx=None)[0] == R.RR_E_NULL
+    assert _latent_fwd(p, k_idx=None)[0] == R.RR_E_NULL
+    assert _latent_fwd(p, topk_idx=None)[0] == R.RR_E_NULL
+    assert _latent_fwd(p, part_o=FAKE)[0] == R.RR_E_UNSUPPORTED
+    assert _latent_fwd(p, ws=FAKE + 8)[0] == R.RR_E_SHAPE            # misaligned workspace
+    need = R.rr_workspace_bytes(p, R.RR_OP_FWD)
+    assert _latent_fwd(p, ws_bytes=need - 1)[0] == R.RR_E_WORKSPACE
+    # scores [K*R][ld] fp32, then candidate keys and positions [K*R][cap] (sampled-threshold
+    # path: cap = 2 * expected candidates + 1024, expected = rank * P / 8192, rank = 3k*8192/P)
+    up = lambda x: -(-x // 256) * 256
+    rank = max(32, -(-3 * 2048 * 8192 // 1048576))
+    cap = up(2 * (rank * 1048576 // 8192) + 1024)
+    assert need == up(4096 * 1048576 * 4) + 2 * up(4096 * cap * 4)
+    # backward: D, then P and dS of the response pairs [K][R][64][R] bf16 (+ one padded segment)
+    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == up(4096 * 64 * 4) + 2 * up((4096 * 64 * 4096 + 128) * 2)
+    # small rows use the exact full-row path and need no candidate buffers
+    small = _latent(P=3000, R_max=96, topk=256)
+    assert R.rr_workspace_bytes(small, R.RR_OP_FWD) == up(96 * 3000 * 4)
