@@ -11,7 +11,8 @@
 // to the caller's workspace with row stride ld.  A wave owns 32 query rows (their q_idx
 // fragments stay in registers) and streams 32-key tiles of k_idx straight from global
 // memory; lanes 0-31 contract index dims 0..63 and lanes 32-63 dims 64..127, so each
-// lane's operand is one contiguous 256-byte half row.
+// lane's operand is one contiguous 256-byte half row; the next tile's keys load while the
+// current tile's 64 MFMAs run.
 //
 // topk_select: one workgroup per query row; scores are mapped to order-preserving
 // unsigned keys.  Fast path (large rows): the key of a fixed descending rank in a sample
@@ -60,11 +61,13 @@ __global__ __launch_bounds__(256) void index_scores_f32(const float* __restrict_
     }
   }
   const int64_t kt_end = min(n_kt, kt0 + key_tiles_per_wg);
-  for (int64_t kt = kt0; kt < kt_end; ++kt) {
+  const bool full_rows = row0 + 32 <= rows;
+  // B fragments of key tile kt: k_idx[kt*32 + col][64h + s], s = 0..63 (a 256-byte half
+  // row per lane); keys past P are redirected to P - 1 and not stored
+  auto load_keys = [&](int64_t kt, float (&kb)[64]) {
     const int64_t key = kt * 32 + col;
     const int64_t kk = key < P ? key : P - 1;
     const float4* src = reinterpret_cast<const float4*>(k_idx + kk * kIdxDim + 64 * h);
-    float kb[64];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float4 x = src[v];
@@ -73,18 +76,35 @@ __global__ __launch_bounds__(256) void index_scores_f32(const float* __restrict_
       kb[4 * v + 2] = x.z;
       kb[4 * v + 3] = x.w;
     }
+  };
+  // scores of tile kt from kb while the next tile's keys load into kn
+  auto tile = [&](int64_t kt, const float (&kb)[64], float (&kn)[64]) {
+    if (kt + 1 < kt_end) load_keys(kt + 1, kn);
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int s = 0; s < 64; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s], kb[s], acc, 0, 0, 0);
+    const int64_t key = kt * 32 + col;
     if (key < P) {
+      float* dst = sigma + (int64_t)row0 * ld + key;
+      if (full_rows) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = row0 + (i >> 2) * 8 + 4 * h + (i & 3);
-        if (r < rows) sigma[(int64_t)r * ld + key] = acc[i];
+        for (int i = 0; i < 16; ++i) dst[(int64_t)((i >> 2) * 8 + 4 * h + (i & 3)) * ld] = acc[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i >> 2) * 8 + 4 * h + (i & 3);
+          if (row0 + r < rows) dst[(int64_t)r * ld] = acc[i];
+        }
       }
     }
+  };
+  float ka[64], kb2[64];
+  if (kt0 < kt_end) load_keys(kt0, ka);
+  for (int64_t kt = kt0; kt < kt_end; kt += 2) {
+    tile(kt, ka, kb2);
+    if (kt + 1 < kt_end) tile(kt + 1, kb2, ka);
   }
 }
 
