@@ -19,9 +19,11 @@
 // the wave's share of the 18 32-wide dim tiles.  For response keys it also writes P and
 // dS (bf16) of every (row, head, key) pair, from which xty_gemm forms dK_r and dV_r.
 //
-// xty_gemm: C[j][d] (+)= alpha sum_{(i,h): i >= j} X[i][h][j] Y[i][h][d], the response-key
-// gradients dK_r = tau dS^T Q and dV_r = P^T dO, with both operands read by transposing
-// LDS reads from row-major tiles loaded straight into LDS.
+// xty_gemm / xty_reduce: C[j][d] += alpha sum_{(i,h): i >= j} X[i][h][j] Y[i][h][d], the
+// response-key gradients dK_r = tau dS^T Q and dV_r = P^T dO, with both operands read by
+// transposing LDS reads from row-major tiles loaded straight into LDS.  The rows are split
+// into chunks (one workgroup per chunk, key tile and dim tile) and the chunk partials are
+// added in chunk order, so the sums are deterministic.
 #include "k_lds.h"
 #include "kernels.h"
 
@@ -410,14 +412,23 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   }
 }
 
-// C[k][j][d] (+)= alpha * sum over rows i in [max(row_lo, j0), row_hi) and heads h of
+// Rows of chunk c that the key tile starting at j0 sums over: [max(row_lo, c*cr, j0),
+// min(row_hi, (c+1)*cr, r_len)).  Rows below j0 are skipped (their P / dS are zero for
+// every key of the tile); the same rule decides, in xty_reduce, which partials exist.
+__device__ __forceinline__ void xty_rows(int c, int cr, int row_lo, int row_hi, int j0, int rl, int& i_lo,
+                                         int& i_hi) {
+  i_lo = max(max(row_lo, c * cr), j0);
+  i_hi = min(min(row_hi, (c + 1) * cr), rl);
+}
+
+// part[c][k][j][d] = sum over rows i of chunk c (xty_rows) and heads h of
 // X[k][i][h][j] * Y[k][i][h][d].  Workgroup tile: 128 keys j x 64 dims d (4 waves x 32
-// keys); inner dimension m = (i, h) in steps of 32 rows.
-__global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ X,
+// keys); inner dimension m = (i, h) in steps of 32.  Workgroups whose chunk has no rows
+// for their key tile return at once and write nothing.
+__global__ __launch_bounds__(256, 2) void xty_gemm(const uint16_t* __restrict__ X,
                                                    const uint16_t* __restrict__ Y, int ldY, int n_d,
-                                                   float* __restrict__ C, int ldC, int R, int K,
-                                                   int row_lo, int row_hi, int j_hi, float alpha,
-                                                   int accumulate, Geom g) {
+                                                   float* __restrict__ part, int R, int K, int row_lo,
+                                                   int row_hi, int j_hi, int cr, Geom g) {
   __shared__ __attribute__((aligned(1024))) char xb0[32 * 128 * 2];
   __shared__ __attribute__((aligned(1024))) char yb0[32 * 64 * 2];
   __shared__ __attribute__((aligned(1024))) char xb1[32 * 128 * 2];
@@ -427,15 +438,18 @@ __global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ 
   const int dt = (int)(idx % n_dt);
   idx /= n_dt;
   const int jt = (int)(idx % n_jt);
-  const int k = (int)(idx / n_jt);
-  if (k >= K) return;
+  idx /= n_jt;
+  const int k = (int)(idx % K);
+  const int c = (int)(idx / K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const int j0 = jt * 128, d0 = dt * 64;
   const int rl = g.r_len[k];
-  const int i_lo = max(row_lo, j0), i_hi = min(row_hi, rl);
+  int i_lo, i_hi;
+  xty_rows(c, cr, row_lo, row_hi, j0, rl, i_lo, i_hi);
+  if (i_hi <= i_lo) return;
   const int64_t m_lo = (int64_t)i_lo * kLatH, m_hi = (int64_t)i_hi * kLatH;
-  const int n_steps = m_hi > m_lo ? (int)((m_hi - m_lo) / 32) : 0;   // kLatH is a multiple of 32
+  const int n_steps = (int)((m_hi - m_lo) / 32);   // kLatH is a multiple of 32
   const uint16_t* xs = X + ((int64_t)k * R * kLatH + m_lo) * R + j0;
   const uint16_t* ys = Y + ((int64_t)k * R * kLatH + m_lo) * ldY + d0;
   DirectLoad<128, 32, 4> dlx;
@@ -451,10 +465,8 @@ __global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ 
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
-  if (n_steps > 0) {
-    dlx.issue(xb0, xs, 0, 32, (int64_t)R * 2);
-    dly.issue(yb0, ys, 0, 32, (int64_t)ldY * 2);
-  }
+  dlx.issue(xb0, xs, 0, 32, (int64_t)R * 2);
+  dly.issue(yb0, ys, 0, 32, (int64_t)ldY * 2);
   auto step = [&](const char* xc, const char* yc, char* xn, char* yn, int st) {
     wait_vmcnt0();
     __syncthreads();
@@ -476,6 +488,7 @@ __global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ 
     if (st + 1 < n_steps) step(xb1, yb1, xb0, yb0, st + 1);
   }
   // C layout: lane = dim column, registers = key rows
+  float* pc = part + ((int64_t)c * K + k) * R * n_d;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int d = d0 + 32 * n + col;
@@ -484,10 +497,44 @@ __global__ __launch_bounds__(256, 1) void xty_gemm(const uint16_t* __restrict__ 
     for (int e = 0; e < 16; ++e) {
       const int j = j0 + 32 * wave + (e >> 2) * 8 + 4 * hl + (e & 3);
       if (j >= j_hi || j >= rl) continue;
-      float* dst = C + ((int64_t)k * R + j) * ldC + d;
-      *dst = (accumulate ? *dst : 0.0f) + alpha * acc[n][e];
+      pc[(int64_t)j * n_d + d] = acc[n][e];
     }
   }
+}
+
+// C[k][j][d] += alpha * sum over chunks c (in order) of part[c][k][j][d], for the chunks
+// that had rows for j's key tile; j < min(j_hi, r_len[k]).  One thread per 4 dims.
+__global__ __launch_bounds__(256) void xty_reduce(const float* __restrict__ part, float* __restrict__ C,
+                                                  int ldC, int n_d, int R, int K, int row_lo, int row_hi,
+                                                  int j_hi, int cr, int n_chunks, float alpha, Geom g) {
+  const int n_d4 = n_d / 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_k = (int64_t)j_hi * n_d4;
+  if (t >= per_k * K) return;
+  const int k = (int)(t / per_k);
+  const int64_t r = t % per_k;
+  const int j = (int)(r / n_d4), d = 4 * (int)(r % n_d4);
+  const int rl = g.r_len[k];
+  if (j >= rl) return;
+  const int j0 = j / 128 * 128;
+  float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int c = 0; c < n_chunks; ++c) {
+    int i_lo, i_hi;
+    xty_rows(c, cr, row_lo, row_hi, j0, rl, i_lo, i_hi);
+    if (i_hi <= i_lo) continue;
+    const float4 v = *reinterpret_cast<const float4*>(part + (((int64_t)c * K + k) * R + j) * n_d + d);
+    sum.x += v.x;
+    sum.y += v.y;
+    sum.z += v.z;
+    sum.w += v.w;
+  }
+  float4* dst = reinterpret_cast<float4*>(C + ((int64_t)k * R + j) * ldC + d);
+  float4 y = *dst;
+  y.x += alpha * sum.x;
+  y.y += alpha * sum.y;
+  y.z += alpha * sum.z;
+  y.w += alpha * sum.w;
+  *dst = y;
 }
 
 hipError_t launch_sparse_fwd(const Geom& g, int topk, const void* q, const void* latent_p,
@@ -510,12 +557,18 @@ hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* 
 }
 
 hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, float* C, int ldC,
-                      const Geom& g, int row_lo, int row_hi, int j_hi, float alpha, int accumulate,
+                      float* part, const Geom& g, int row_lo, int row_hi, int j_hi, float alpha,
                       hipStream_t s) {
   if (j_hi <= 0) return hipSuccess;
+  const int cr = xty_chunk_rows(g.R), n_chunks = xty_n_chunks(g.R);
   const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 63) / 64;
-  hipLaunchKernelGGL(xty_gemm, dim3((unsigned)(g.K * n_jt * n_dt)), dim3(256), 0, s, X, Y, ldY, n_d, C,
-                     ldC, g.R, g.K, row_lo, row_hi, j_hi, alpha, accumulate, g);
+  hipLaunchKernelGGL(xty_gemm, dim3((unsigned)((int64_t)n_chunks * g.K * n_jt * n_dt)), dim3(256), 0, s, X, Y,
+                     ldY, n_d, part, g.R, g.K, row_lo, row_hi, j_hi, cr, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)g.K * j_hi * (n_d / 4);
+  hipLaunchKernelGGL(xty_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, C, ldC, n_d, g.R,
+                     g.K, row_lo, row_hi, j_hi, cr, n_chunks, alpha, g);
   return hipGetLastError();
 }
 

@@ -64,8 +64,11 @@ hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* 
                             const void* latent_r, const int32_t* sel, const void* d_o,
                             const float* lse, const float* Dvec, float* dq, uint16_t* p_r,
                             uint16_t* ds_r, int accumulate, hipStream_t s);
+// C[k][j][d] += alpha * sum over rows i in [max(row_lo, tile start), row_hi) and heads h of
+// X[k][i][h][j] * Y[k][i][h][d] for j < min(j_hi, r_len[k]); `part` is the workspace of
+// chunk partials ([xty_n_chunks][K][R][n_d] fp32), summed into C in chunk order.
 hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, float* C, int ldC,
-                      const Geom& g, int row_lo, int row_hi, int j_hi, float alpha, int accumulate,
+                      float* part, const Geom& g, int row_lo, int row_hi, int j_hi, float alpha,
                       hipStream_t s);
 
 // acc[e] += scale * g[e], e < n.

@@ -93,6 +93,7 @@ int latent_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const 
   float* Dvec = carve(ws, 0);
   uint16_t* p_r = reinterpret_cast<uint16_t*>(carve(ws, align_up(rows * sizeof(float), 256)));
   uint16_t* ds_r = reinterpret_cast<uint16_t*>(carve(ws, align_up(rows * sizeof(float), 256) + ws_pds_bytes(p)));
+  float* part = carve(ws, align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p));
   const int nb = (p->R_max + p->block - 1) / p->block;
   if (block_idx >= 0) {
     g.row_lo = block_idx * p->block;
@@ -118,13 +119,13 @@ int latent_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const 
   for (int b = b_hi; b >= b_lo; --b) {   // reverse block walk
     const int lo = b * p->block, hi = std::min(p->R_max, lo + p->block);
     if ((e = timed("xty_dk", s, [&] {
-           return launch_xty(ds_r, static_cast<const uint16_t*>(q), p->d_qk, p->d_qk, dk_r, p->d_qk, g, lo,
-                             hi, hi, p->tau, 1, s);
+           return launch_xty(ds_r, static_cast<const uint16_t*>(q), p->d_qk, p->d_qk, dk_r, p->d_qk, part, g,
+                             lo, hi, hi, p->tau, s);
          })))
       return hip_fail(e, "xty_dk");
     if ((e = timed("xty_dv", s, [&] {
-           return launch_xty(p_r, static_cast<const uint16_t*>(d_o), p->d_v, p->d_v, dv_r, p->d_v, g, lo,
-                             hi, hi, 1.0f, 1, s);
+           return launch_xty(p_r, static_cast<const uint16_t*>(d_o), p->d_v, p->d_v, dv_r, p->d_v, part, g,
+                             lo, hi, hi, 1.0f, s);
          })))
       return hip_fail(e, "xty_dv");
   }

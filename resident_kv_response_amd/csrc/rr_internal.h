@@ -53,6 +53,19 @@ Geom make_geom(const rr_problem* p, const int32_t* r_len);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Row chunks of the latent response-pair GEMM (dK_r, dV_r): the response rows are split
+// into at most 16 chunks of at least 256 rows; each chunk's partial product is written to
+// the workspace and the partials are summed in chunk order.
+inline int xty_chunk_rows(int R_max) {
+  const int n = (R_max + 255) / 256;
+  const int n_chunks = n < 16 ? n : 16;
+  return (R_max + n_chunks - 1) / n_chunks;
+}
+inline int xty_n_chunks(int R_max) {
+  const int cr = xty_chunk_rows(R_max);
+  return (R_max + cr - 1) / cr;
+}
+
 // Plan of the per-row top-k selection over P fp32 scores (k_topk.hip).  Fast path: a
 // sample of kTopkSample scores gives a threshold expected to keep about 3k positions
 // (at least 32 sample ranks above it); one pass keeps the positions at or above it as

@@ -104,7 +104,9 @@ size_t ws_pds_bytes(const rr_problem* p) {
 
 size_t ws_bwd_bytes(const rr_problem* p) {
   const size_t rows = rows_total(p);
-  if (p->latent) return align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p);
+  if (p->latent)   // D, P and dS of the response pairs, chunk partials of dK_r / dV_r
+    return align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p) +
+           align_up((size_t)xty_n_chunks(p->R_max) * p->K * p->R_max * p->d_qk * sizeof(float), 256);
   return align_up(rows * sizeof(float), 256) +
          align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256);
 }

@@ -204,8 +204,10 @@ def test_latent_fwd_arguments_and_workspace():
     rank = max(32, -(-3 * 2048 * 8192 // 1048576))
     cap = up(2 * (rank * 1048576 // 8192) + 1024)
     assert need == up(4096 * 1048576 * 4) + 2 * up(4096 * cap * 4)
-    # backward: D, then P and dS of the response pairs [K][R][64][R] bf16 (+ one padded segment)
-    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == up(4096 * 64 * 4) + 2 * up((4096 * 64 * 4096 + 128) * 2)
+    # backward: D, then P and dS of the response pairs [K][R][64][R] bf16 (+ one padded
+    # segment), then the dK_r / dV_r chunk partials [16 chunks of 256 rows][K][R][576] fp32
+    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == (up(4096 * 64 * 4) + 2 * up((4096 * 64 * 4096 + 128) * 2)
+                                                   + up(16 * 4096 * 576 * 4))
     # small rows use the exact full-row path and need no candidate buffers
     small = _latent(P=3000, R_max=96, topk=256)
     assert R.rr_workspace_bytes(small, R.RR_OP_FWD) == up(96 * 3000 * 4)
