@@ -157,3 +157,60 @@ def test_sparse_deterministic():
     b = _run(d, P, R, topk, 32)
     for key in ("idx", "o", "lse", "dq", "dk", "dv"):
         assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_sparse_varlen_microbatch():
+    """Two responses in one call (K = 2), one shorter than R_max: the valid rows of each
+    match the oracle exactly in selection and to the bf16 bounds in values; padding rows
+    get O = 0, lse = -inf, selection -1 and zero gradients."""
+    from tests import _gpu as G
+    P, Rm, topk, lens = 3000, 64, 256, (64, 37)
+    ds = [_data(8400 + n, P, Rm, integer_index=True) for n in range(2)]
+    base = ds[0]
+    stack = lambda key: np.stack([d[key] for d in ds])
+    prob = G.latent_problem(P, Rm, topk, 32, K=2)
+    run = G.LatentRun(prob, base["latent_p"], base["k_idx"], stack("q"), stack("latent_r"), stack("q_idx"),
+                      stack("d_o"), lens)
+    print("[sparse] varlen microbatch", flush=True)
+    got = run.fwd().bwd().numpy()
+    for kk, rl in enumerate(lens):
+        d = dict(latent_p=base["latent_p"], k_idx=base["k_idx"], q=ds[kk]["q"][:rl],
+                 latent_r=ds[kk]["latent_r"][:rl], q_idx=ds[kk]["q_idx"][:rl], d_o=ds[kk]["d_o"][:rl])
+        sel, sig, o, lse, gr = _oracle(d, topk)
+        np.testing.assert_array_equal(got["idx"][kk][:rl], sel)
+        assert_bf16_close(f"o[{kk}]", got["o"][kk][:rl], o)
+        assert_bf16_close(f"dq[{kk}]", got["dq"][kk][:rl], gr["dq"])
+        assert_bf16_close(f"dk_r[{kk}]", got["dk"][kk][:rl], gr["dk_r"])
+        assert_bf16_close(f"dv_r[{kk}]", got["dv"][kk][:rl], gr["dv_r"])
+        if rl < Rm:
+            assert np.all(got["idx"][kk][rl:] == -1)
+            assert np.all(got["o"][kk][rl:] == 0) and np.all(np.isneginf(got["lse"][kk][rl:]))
+            for key in ("dq", "dk", "dv"):
+                assert np.all(got[key][kk][rl:] == 0), key
+
+
+def test_sparse_caller_driven_reverse_walk():
+    """The backward driven one block at a time (last block first, accumulating) equals the
+    whole walk bit for bit, and after the call for block b the dK_r / dV_r rows of block b
+    already hold their final values."""
+    import torch
+    from tests import _gpu as G
+    P, R, topk, block = 3000, 96, 256, 32
+    d = _data(8500, P, R, integer_index=False)
+    prob = G.latent_problem(P, R, topk, block)
+    run = G.LatentRun(prob, d["latent_p"], d["k_idx"], d["q"][None], d["latent_r"][None], d["q_idx"][None],
+                      d["d_o"][None], [R])
+    print("[sparse] caller-driven walk", flush=True)
+    full = run.fwd().bwd().numpy()
+    for t in (run.dq, run.dk, run.dv):
+        t.zero_()
+    nb = (R + block - 1) // block
+    for b in reversed(range(nb)):
+        run.bwd(accumulate=1, block_idx=b)
+        torch.cuda.synchronize()
+        lo, hi = b * block, min(R, (b + 1) * block)
+        assert np.array_equal(run.dk[0, lo:hi].double().cpu().numpy(), full["dk"][0, lo:hi]), b
+        assert np.array_equal(run.dv[0, lo:hi].double().cpu().numpy(), full["dv"][0, lo:hi]), b
+    walked = run.numpy()
+    for key in ("dq", "dk", "dv"):
+        assert np.array_equal(walked[key], full[key]), key
