@@ -7,8 +7,9 @@
 // response-only backward.  Key = the whole 576-wide latent row, value = its first 512
 // dims; 64 query heads share each row.
 //
-// sparse_fwd: one workgroup (4 waves) per query row.  Keys are the row's top-k prompt
-// rows followed by response rows 0..i, gathered 32 at a time straight into LDS.  Wave w
+// sparse_fwd: one workgroup (8 waves) per query row, both 32-head tiles sharing each
+// gathered tile.  Keys are the row's top-k prompt rows followed by response rows 0..i,
+// gathered 32 at a time straight into LDS.  Wave w
 // contracts dims [144w, 144w + 144) of the scores for all 64 heads; the four partial
 // score tiles are exchanged through LDS and summed in a fixed order, so every wave holds
 // the same scores and runs the same online softmax; wave w then accumulates the output
@@ -52,14 +53,16 @@ constexpr int kLatSelMax = 4096;                     // largest top-k the kernel
 // redirected to key n_keys - 1 (masked by the caller).  `sel` is the row's selection in
 // LDS, already clamped into [0, P): reading it there keeps the gathers free of waits on
 // global loads (vmcnt drains in issue order, so waiting on a global index load would
-// also wait on every gather in flight).  4 waves, 9 loads each.
+// also wait on every gather in flight).  The 36 wave-wide loads are dealt over NW waves.
+template <int NW = 4>
 __device__ __forceinline__ void gather_tile(char* tile, const uint16_t* latent_p,
                                             const uint16_t* latent_rk, const int32_t* sel,
                                             int n_sel, int n_keys, int t0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int u = 0; u < kLatInstr / 4; ++u) {
-    const int n = wave * (kLatInstr / 4) + u;
+  for (int u = 0; u < (kLatInstr + NW - 1) / NW; ++u) {
+    const int n = u * NW + wave;           // wave-wide load n fills LDS bytes [1024 n, 1024 n + 1024)
+    if (kLatInstr % NW != 0 && n >= kLatInstr) break;
     const int p = 64 * n + lane;
     const int r = p / Lat::G, ph = p % Lat::G;
     const int g = (ph & ~7) | ((ph & 7) ^ Lat::f(r));
@@ -107,10 +110,10 @@ struct Xch {
   float4 v[4][4][64];
 };
 
-__device__ __forceinline__ void xch_put(Xch& x, const f32x16& p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void xch_put(Xch& x, const f32x16& p, int slot) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x.v[wave][j][lane] = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+  for (int j = 0; j < 4; ++j) x.v[slot][j][lane] = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
 }
 
 // Sum of the four partials in wave order (identical in every wave).
@@ -136,25 +139,31 @@ __device__ __forceinline__ void xch_sum(const Xch& x, f32x16& s) {
 
 constexpr float kLatRescale = 8.0f;
 
-// One workgroup = one query row and one tile of 32 heads (blockIdx.x = 2 * row + tile).
-__global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ latent_p,
-                                                     const uint16_t* __restrict__ latent_r,
-                                                     const int32_t* __restrict__ sel_idx,
-                                                     float* __restrict__ o, float* __restrict__ lse) {
+// One workgroup = one query row and HT tiles of 32 heads, 4 waves per head tile (wave w:
+// head tile w / 4, dim slice w % 4).  With HT = 2 both head tiles share each gathered tile;
+// with HT = 1, blockIdx.x = 2 * row + tile.
+template <int HT>
+__global__ __launch_bounds__(256 * HT, 1) void sparse_fwd(Geom g, int topk, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ latent_p,
+                                                          const uint16_t* __restrict__ latent_r,
+                                                          const int32_t* __restrict__ sel_idx,
+                                                          float* __restrict__ o, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) char kv0[kLatTile];
   __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
-  __shared__ __attribute__((aligned(16))) Xch xch;
+  __shared__ __attribute__((aligned(16))) Xch xch[HT];
   __shared__ int32_t sel_lds[kLatSelMax];
-  const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = HT == 2 ? (int)blockIdx.x : (int)(blockIdx.x >> 1);
+  const int ht = HT == 2 ? wv >> 2 : (int)(blockIdx.x & 1);
+  const int wave = wv & 3;                                // dim slice within the head tile
   const int k = row / g.R, i = row % g.R;
   if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const int64_t hrow0 = (int64_t)row * kLatH + 32 * ht;   // (k, i, first head of the tile)
   if (i >= g.r_len[k]) {
-    for (int e = threadIdx.x; e < 32 * kLatDV; e += 256) o[hrow0 * kLatDV + e] = 0.0f;
-    if (threadIdx.x < 32) lse[hrow0 + threadIdx.x] = -INFINITY;
+    const int64_t h0 = (int64_t)row * kLatH + (HT == 2 ? 0 : 32 * ht);
+    for (int e = threadIdx.x; e < 32 * HT * kLatDV; e += 256 * HT) o[h0 * kLatDV + e] = 0.0f;
+    if (threadIdx.x < 32 * HT) lse[h0 + threadIdx.x] = -INFINITY;
     return;
   }
   const int n_keys = topk + i + 1;
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
   const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
   stage_selection(sel_lds, sel_idx + (int64_t)row * topk, topk, g.P);
   const int32_t* sel = sel_lds;
-  gather_tile(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
+  gather_tile<4 * HT>(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
 
   // Q fragments of this wave's 9 k-steps of the score contraction
   bf16x8 qf[9];
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
   auto tile_step = [&](const char* cur, char* nxt, int t) {
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    if (t + 1 < n_tiles) gather_tile<4 * HT>(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
     f32x16 sp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = 0.0f;
@@ -188,10 +197,10 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd(Geom g, int topk, const uin
 #pragma unroll
     for (int s = 0; s < 9; ++s) sp = mfma32x32x16(lat_row(cur, 9 * wave + s), qf[s], sp);
     prio_valu();
-    xch_put(xch, sp);
+    xch_put(xch[HT == 2 ? ht : 0], sp, wave);
     __syncthreads();
     f32x16 sc;
-    xch_sum(xch, sc);
+    xch_sum(xch[HT == 2 ? ht : 0], sc);
     const int rel = t * kLatKeys;
     if (rel + kLatKeys > n_keys) {
 #pragma unroll
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
   stage_selection(sel_lds, sel_idx + (int64_t)row * topk, topk, g.P);
   const int32_t* sel = sel_lds;
-  gather_tile(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
+  gather_tile<4>(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
 
   bf16x8 qf[9], of[8];
   const int64_t hr = hrow0 + col;
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   auto tile_step = [&](const char* cur, char* nxt, int t) {
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_tiles) gather_tile(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    if (t + 1 < n_tiles) gather_tile<4>(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
     f32x16 sp, dpp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = dpp[e] = 0.0f;
@@ -334,8 +343,8 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
 #pragma unroll
     for (int s = 0; s < 8; ++s) dpp = mfma32x32x16(lat_row(cur, 8 * wave + s), of[s], dpp);  // value dims
     prio_valu();
-    xch_put(xs, sp);
-    xch_put(xp, dpp);
+    xch_put(xs, sp, wave);
+    xch_put(xp, dpp, wave);
     __syncthreads();
     f32x16 sc, dp;
     xch_sum(xs, sc);
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(256) void xty_reduce(const float* __restrict__ part
 hipError_t launch_sparse_fwd(const Geom& g, int topk, const void* q, const void* latent_p,
                              const void* latent_r, const int32_t* sel, float* o, float* lse,
                              hipStream_t s) {
-  hipLaunchKernelGGL(sparse_fwd, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
+  hipLaunchKernelGGL(sparse_fwd<2>, dim3((unsigned)(g.K * g.R)), dim3(512), 0, s, g, topk,
                      (const uint16_t*)q, (const uint16_t*)latent_p, (const uint16_t*)latent_r, sel,
                      o, lse);
   return hipGetLastError();
