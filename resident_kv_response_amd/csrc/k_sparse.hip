@@ -269,36 +269,41 @@ __global__ __launch_bounds__(256 * HT, 1) void sparse_fwd(Geom g, int topk, cons
 // dQ of one query row and head tile, and the response pairs' P and dS.  pds layout:
 // [K][R][64][R] bf16 (row, head, key); for row i the keys j in
 // [0, min(R, round_up(i + 1, 128))) are written, zeros for j > i.
-__global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ latent_p,
-                                                    const uint16_t* __restrict__ latent_r,
-                                                    const int32_t* __restrict__ sel_idx,
-                                                    const uint16_t* __restrict__ d_o,
-                                                    const float* __restrict__ lse,
-                                                    const float* __restrict__ Dvec,
-                                                    float* __restrict__ dq, uint16_t* __restrict__ p_r,
-                                                    uint16_t* __restrict__ ds_r, int accumulate) {
+template <int HT>
+__global__ __launch_bounds__(256 * HT, 1) void sparse_dq(Geom g, int topk, const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ latent_p,
+                                                         const uint16_t* __restrict__ latent_r,
+                                                         const int32_t* __restrict__ sel_idx,
+                                                         const uint16_t* __restrict__ d_o,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ Dvec,
+                                                         float* __restrict__ dq, uint16_t* __restrict__ p_r,
+                                                         uint16_t* __restrict__ ds_r, int accumulate) {
   __shared__ __attribute__((aligned(1024))) char kv0[kLatTile];
   __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
-  __shared__ __attribute__((aligned(16))) Xch xs;
-  __shared__ __attribute__((aligned(16))) Xch xp;
+  __shared__ __attribute__((aligned(16))) Xch xs[HT];
+  __shared__ __attribute__((aligned(16))) Xch xp[HT];
   __shared__ int32_t sel_lds[kLatSelMax];
-  const int row = blockIdx.x >> 1, ht = blockIdx.x & 1;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = HT == 2 ? (int)blockIdx.x : (int)(blockIdx.x >> 1);
+  const int ht = HT == 2 ? wv >> 2 : (int)(blockIdx.x & 1);
+  const int wave = wv & 3;                                // dim slice within the head tile
+  const int xi = HT == 2 ? ht : 0;                        // this head tile's exchange buffers
   const int k = row / g.R, i = row % g.R;
   if (k >= g.K || i < g.row_lo || i >= g.row_hi) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const int64_t hrow0 = (int64_t)row * kLatH + 32 * ht;
+  const int64_t h0 = (int64_t)row * kLatH + (HT == 2 ? 0 : 32 * ht);   // first head of the workgroup
   if (i >= g.r_len[k]) {
     if (!accumulate)
-      for (int e = threadIdx.x; e < 32 * kLatD; e += 256) dq[hrow0 * kLatD + e] = 0.0f;
+      for (int e = threadIdx.x; e < 32 * HT * kLatD; e += 256 * HT) dq[h0 * kLatD + e] = 0.0f;
     return;
   }
   const int64_t pds_row = hrow0 * g.R;                // element offset of (k, i, first head, key 0)
   const int jz_end = min(g.R, ((i + 1 + 127) / 128) * 128);
   const int nz = jz_end - i - 1;                       // causal remainder of the last 128-key group
-  for (int e = threadIdx.x; e < 32 * nz; e += 256) {
-    const int64_t at = pds_row + (int64_t)(e / nz) * g.R + i + 1 + e % nz;
+  for (int e = threadIdx.x; e < 32 * HT * nz; e += 256 * HT) {
+    const int64_t at = h0 * g.R + (int64_t)(e / nz) * g.R + i + 1 + e % nz;
     p_r[at] = 0;
     ds_r[at] = 0;
   }
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   const uint16_t* latent_rk = latent_r + (int64_t)k * g.R * kLatD;
   stage_selection(sel_lds, sel_idx + (int64_t)row * topk, topk, g.P);
   const int32_t* sel = sel_lds;
-  gather_tile<4>(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
+  gather_tile<4 * HT>(kv0, latent_p, latent_rk, sel, topk, n_keys, 0);
 
   bf16x8 qf[9], of[8];
   const int64_t hr = hrow0 + col;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
   auto tile_step = [&](const char* cur, char* nxt, int t) {
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_tiles) gather_tile<4>(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
+    if (t + 1 < n_tiles) gather_tile<4 * HT>(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
     f32x16 sp, dpp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = dpp[e] = 0.0f;
@@ -343,12 +348,12 @@ __global__ __launch_bounds__(256, 1) void sparse_dq(Geom g, int topk, const uint
 #pragma unroll
     for (int s = 0; s < 8; ++s) dpp = mfma32x32x16(lat_row(cur, 8 * wave + s), of[s], dpp);  // value dims
     prio_valu();
-    xch_put(xs, sp, wave);
-    xch_put(xp, dpp, wave);
+    xch_put(xs[xi], sp, wave);
+    xch_put(xp[xi], dpp, wave);
     __syncthreads();
     f32x16 sc, dp;
-    xch_sum(xs, sc);
-    xch_sum(xp, dp);
+    xch_sum(xs[xi], sc);
+    xch_sum(xp[xi], dp);
     const int rel = t * kLatKeys;
     float p[16], ds[16];
 #pragma unroll
@@ -559,7 +564,9 @@ hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* 
                             const void* latent_r, const int32_t* sel, const void* d_o,
                             const float* lse, const float* Dvec, float* dq, uint16_t* p_r,
                             uint16_t* ds_r, int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(sparse_dq, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
+  // one head tile per workgroup: with both, the per-wave state (Q and dO fragments, dQ^T
+  // accumulators) does not fit the 256 registers of two waves per SIMD and spills
+  hipLaunchKernelGGL(sparse_dq<1>, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
                      (const uint16_t*)q, (const uint16_t*)latent_p, (const uint16_t*)latent_r, sel,
                      (const uint16_t*)d_o, lse, Dvec, dq, p_r, ds_r, accumulate);
   return hipGetLastError();
