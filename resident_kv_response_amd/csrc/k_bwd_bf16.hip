@@ -7,8 +7,9 @@
 // what a response backward touches).  No kernel here reads or writes a prompt gradient.
 //
 // dq_partials_bf16: query-parallel, one workgroup per (k, g, part, 256-row tile) like
-// the forward; per 32-key subtile S^T = K Q^T and dP^T = V dO^T (2 x D/16 MFMAs),
-// p = 2^(S c2 - lse2), dS = p (dP - D) rounded to bf16, dQ^T += K^T dS^T (D/16 MFMAs).
+// the forward; per 32-key subtile S^T = K Q^T and dP^T = V dO^T - D (2 x D/16 MFMAs, the
+// second accumulation starting from -D), p = 2^(S c2 - lse2), dS = p (dP - D) rounded to
+// bf16, dQ^T += K^T dS^T (D/16 MFMAs).
 // Writes one dQ partial per part; the partials are summed in part order afterwards.
 //
 // dkdv_bf16: key-parallel over the response keys, one workgroup per (k, g, 128 keys),
@@ -38,17 +39,19 @@ struct DqCfg {
 };
 
 // One 32-key subtile of the dQ accumulation for this wave's 32 rows.
+// The dP^T accumulation starts from dinit (every element -D of the lane's row), so the
+// MFMAs deliver dP - D directly and dS = P (dP - D) is one multiply per element.
 template <bool MASK, int D>
 __device__ __forceinline__ void dq_subtile(const Frag<D>& fr, const char* Kt, const char* Vt, int sub,
                                            int rel, int lim,
-                                           float c2, float lse2, float dvv,
+                                           float c2, float lse2, const f32x16& dinit,
                                            const bf16x8 (&qf)[D / 16], const bf16x8 (&of)[D / 16],
                                            f32x16 (&acc)[D / 32]) {
   constexpr int KS = D / 16, DT = D / 32;
   const int hl = (threadIdx.x & 63) >> 5;
-  f32x16 s, dp;
+  f32x16 s, dp = dinit;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+  for (int i = 0; i < 16; ++i) s[i] = 0.0f;
   prio_mfma();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -66,7 +69,7 @@ __device__ __forceinline__ void dq_subtile(const Frag<D>& fr, const char* Kt, co
       const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
       if (key > lim) p = 0.0f;
     }
-    ds[i] = p * (dp[i] - dvv);
+    ds[i] = p * dp[i];
   }
   bf16x8 dsf[2];
 #pragma unroll
@@ -141,6 +144,9 @@ __global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
   const int64_t orow = m < m_hi ? ((int64_t)w.part * g.K * g.R * g.Hq + row) : -1;
   const float lse2 = valid ? lse[row] * kLog2e : INFINITY;
   const float dvv = valid ? Dvec[row] : 0.0f;
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dinit[i] = -dvv;
   bf16x8 qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -177,9 +183,9 @@ __global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
       const int rel = it * C::BN + sub * 32;
       if (rel > wmax) break;
       if (rel + 31 > wmin)
-        dq_subtile<true, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+        dq_subtile<true, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dinit, qf, of, acc);
       else
-        dq_subtile<false, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dvv, qf, of, acc);
+        dq_subtile<false, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dinit, qf, of, acc);
     }
   };
   for (int it = 0; it < n_stages; it += 2) {
