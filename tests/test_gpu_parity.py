@@ -72,6 +72,14 @@ def test_bf16_multitile_ragged(d, Hq, Hkv):
     _run_and_check(w, [w.R])
 
 
+@pytest.mark.parametrize("dtype,P,chunk", [("bf16", 1, 16), ("bf16", 33, 16), ("f32", 1, 4), ("f32", 45, 16)])
+def test_tiny_prompts_and_chunks(dtype, P, chunk):
+    # a one-position prompt, and prompts whose every chunk is shorter than a 32-key subtile
+    base = configs.TINY_F32 if dtype == "f32" else configs.SHARE_P256K
+    w = base.with_(P=P, R=70, chunk=chunk, block=32, seed=4100 + P)
+    _run_and_check(w, [70, 41], R_max=72)
+
+
 def test_bf16_varlen_microbatch():
     # K = 4 responses of different lengths in one call, including a one-row and an empty one
     w = configs.SHARE_P256K.with_(P=3000, R=400, chunk=1024, block=128, seed=4001)

@@ -214,3 +214,30 @@ def test_sparse_caller_driven_reverse_walk():
     walked = run.numpy()
     for key in ("dq", "dk", "dv"):
         assert np.array_equal(walked[key], full[key]), key
+
+
+def test_sparse_select_everything_and_empty_response():
+    """top-k = P (every prompt position selected: attention becomes dense over the prompt)
+    in a microbatch whose second response is empty (r_len = 0: all of its rows are
+    padding)."""
+    from tests import _gpu as G
+    P, Rm, topk, lens = 512, 32, 512, (32, 0)
+    ds = [_data(8600 + n, P, Rm, integer_index=False) for n in range(2)]
+    base = ds[0]
+    stack = lambda key: np.stack([d[key] for d in ds])
+    prob = G.latent_problem(P, Rm, topk, 32, K=2)
+    run = G.LatentRun(prob, base["latent_p"], base["k_idx"], stack("q"), stack("latent_r"), stack("q_idx"),
+                      stack("d_o"), lens)
+    print("[sparse] select everything + empty response", flush=True)
+    got = run.fwd().bwd().numpy()
+    sel, sig, o, lse, gr = _oracle(base, topk)
+    np.testing.assert_array_equal(got["idx"][0], np.tile(np.arange(P), (Rm, 1)))
+    np.testing.assert_array_equal(sel, np.tile(np.arange(P), (Rm, 1)))
+    assert_bf16_close("o", got["o"][0], o)
+    assert_bf16_close("dq", got["dq"][0], gr["dq"])
+    assert_bf16_close("dk_r", got["dk"][0], gr["dk_r"])
+    assert_bf16_close("dv_r", got["dv"][0], gr["dv_r"])
+    assert np.all(got["idx"][1] == -1)
+    assert np.all(got["o"][1] == 0) and np.all(np.isneginf(got["lse"][1]))
+    for key in ("dq", "dk", "dv"):
+        assert np.all(got[key][1] == 0), key
