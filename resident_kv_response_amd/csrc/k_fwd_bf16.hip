@@ -7,8 +7,9 @@
 // longstraw-2m-rl, section "Two incompatible architectures, same transaction").
 //
 // Rows: flattened m = r * grp + hh over the grp query heads that read KV head g, so one
-// K/V tile feeds all of them.  4 waves x 64 rows; each wave keeps its Q fragments and its
-// O^T accumulators (d x rows, fp32) in registers for the whole part.
+// K/V tile feeds all of them.  8 waves x 32 rows (two waves per SIMD); each wave keeps
+// its Q fragments and its O^T accumulators (d x rows, fp32) in registers for the whole
+// part.
 //
 // K/V stream: 128-key stages loaded straight from global memory into LDS (no register
 // staging), two buffers, the next stage's loads in flight while the current one is used.
@@ -16,9 +17,13 @@
 // base-2 online softmax with a lazy rescale (the reference maximum only moves when a
 // row's maximum grows by more than 2^8, so every p <= 256), P^T rounded to bf16 straight
 // from the C registers (the running sum l adds up those rounded values, so the
-// normaliser is the sum of exactly the weights the PV product uses), O^T += V^T P^T (D/16 MFMAs, V^T fragments by transposing LDS
-// reads).  The next subtile's S^T MFMAs are issued before the current softmax so the
-// matrix cores and the vector ALUs work at the same time.
+// normaliser is the sum of exactly the weights the PV product uses), O^T += V^T P^T
+// (D/16 MFMAs, V^T fragments by transposing LDS reads).
+//
+// Stages whose keys are visible to every row of the wave run a software pipeline: the
+// S^T MFMAs of subtile j+1 and the PV MFMAs of subtile j-1 are issued between short runs
+// of the softmax of subtile j, so the matrix cores and the vector ALUs work at the same
+// time.  Stages near the causal diagonal or a chunk end take the masked path.
 #include "k_attn_tile.h"
 #include "k_lds.h"
 #include "kernels.h"
