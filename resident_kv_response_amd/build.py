@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librr_attn.so")
-SOURCES = ["rr_validate.cpp", "rr_api.cpp", "k_small.hip", "k_f32.hip", "k_fwd_bf16.hip",
+SOURCES = ["rr_validate.cpp", "rr_api.cpp", "k_small.hip", "k_f32.hip", "k_fwd_bf16.hip", "k_fwd_ring_bf16.hip",
            "k_bwd_bf16.hip", "k_topk.hip", "k_sparse.hip"]
 ARCH = "gfx950"
 
@@ -37,9 +37,16 @@ def flags() -> list:
             "-Wno-unused-command-line-argument"]
 
 
+# Per-source additions.  The attention kernels never produce or consume NaN (masked scores
+# are -inf, empty rows are handled explicitly), so max/min need no NaN canonicalisation.
+SOURCE_FLAGS = {
+    "k_fwd_ring_bf16.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if not src.endswith(".hip"):
         cmd += ["-x", "hip"] if src == "rr_api.cpp" else []
     r = subprocess.run(cmd, capture_output=True, text=True)

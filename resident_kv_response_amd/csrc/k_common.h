@@ -63,6 +63,7 @@ __device__ __forceinline__ void prio_valu() {
 // so that a wave keeps issuing vector work while its matrix-core operations run.
 #define RR_SG_MFMA 0x008
 #define RR_SG_VALU 0x002
+#define RR_SG_TRANS 0x400
 #define RR_SG_DS_READ 0x100
 #define RR_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 

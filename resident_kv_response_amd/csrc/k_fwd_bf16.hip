@@ -449,7 +449,12 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
   }
 }
 
+hipError_t launch_fwd_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
+
 hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
+#ifndef RR_FWD_OLD
+  return launch_fwd_ring_bf16(g, a, s);
+#endif
   const int64_t n = tile_work_count(g, FwdCfg<128>::BM);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)xcd_grid(n)), block(64 * FwdCfg<128>::WAVES);

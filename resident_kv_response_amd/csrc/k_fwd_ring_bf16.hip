@@ -1,0 +1,415 @@
+// bf16 forward partials on MFMA (gfx950), continuous software pipeline over a ring of
+// K/V stages.
+//
+// One workgroup = one (response k, KV head g, part, 256-row tile).  A part is one prompt
+// chunk [c*chunk, (c+1)*chunk) or the response's own causal keys; each part keeps its own
+// softmax statistics (running max m, running sum l) and writes O_c = O~_c / l and
+// lse_c = m + ln l, which are then composed exactly (ai.thesatyajit.com/articles/
+// longstraw-2m-rl, section "Two incompatible architectures, same transaction").
+//
+// Rows: flattened m = r * grp + hh over the grp query heads that read KV head g, so one
+// K/V tile feeds all of them.  8 waves x 32 rows (two waves per SIMD); each wave keeps its
+// Q fragments and its O^T accumulators (d x rows, fp32) in registers for the whole part.
+//
+// K/V stream: 64-key stages in a ring of four LDS buffers, loaded straight from global
+// memory into LDS two stages ahead; one barrier per stage.  The buffers are separate
+// arrays and every read names its buffer at compile time, so the compiler can tell a read
+// of one buffer from the direct loads still landing in another.
+//
+// Pipeline over 32-key subtiles u, per wave: block B(u) issues O^T += V^T P^T of subtile
+// u-1 and S^T = K Q^T of subtile u+1 on the matrix cores (16 MFMAs with no dependence on
+// the block's vector work) while the vector ALUs run the online softmax of subtile u
+// (base 2, lazy rescale: the reference maximum only moves when a row's maximum grows by
+// more than 2^8, so every p <= 256; P^T rounded to bf16 straight from the C registers,
+// and the running sum l adds up exactly those rounded values).  A rescale of the
+// accumulators is applied at the end of the block, between PV(u-1) and PV(u).  The block
+// sequence runs across stage boundaries, so every block carries the same balanced load.
+// Subtiles whose keys are visible to every row of the workgroup run this pipeline; the
+// few near the causal diagonal or a chunk end run a masked, unpipelined path afterwards.
+#include <type_traits>
+
+#include "k_attn_tile.h"
+#include "k_lds.h"
+#include "kernels.h"
+
+namespace rr {
+
+namespace {
+
+constexpr float kRingRescaleLog2 = 8.0f;   // log2 of the largest p between rescales
+
+template <int D>
+struct RingCfg {
+  static constexpr int WAVES = 8;
+  static constexpr int BM = WAVES * 32;                 // query rows per workgroup
+  static constexpr int BN = 64;                         // keys per stage
+  static constexpr int KS = D / 16, DT = D / 32;
+  static constexpr int TILE = BN * D * 2;               // bytes of one [BN][D] bf16 tile
+  static constexpr int LOADS = 2 * (BN * D / 8) / (64 * WAVES);   // direct loads per wave per stage
+};
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding, n < 16).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+template <int D>
+__device__ __forceinline__ void ring_scores(const Frag<D>& fr, const char* Kt, int sub,
+                                            const bf16x8 (&qf)[D / 16], f32x16& s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) s = mfma32x32x16(fr.row(Kt, sub, ks), qf[ks], s);
+}
+
+// Lane offsets of the V^T fragment reads, biased by 2^16 and hidden from the compiler:
+// the V tiles lie above the 16-bit immediate offset range of a LDS read, and with the
+// bias every V buffer is reached as (one set of offset registers) + immediate instead
+// of one register set per buffer.
+template <int D>
+struct VtOffsets {
+  static constexpr uint32_t kBias = 1u << 16;
+  uint32_t o[D / 32][2];
+  __device__ __forceinline__ void init(const Frag<D>& fr) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        o[dt][hi] = fr.trans[dt][hi] + kBias;
+        asm volatile("" : "+v"(o[dt][hi]));
+      }
+  }
+  // V^T fragment (see Frag::trans_frag) of a V tile at `vt`.
+  __device__ __forceinline__ bf16x8 frag(const char* vt, int sub, int h2, int dt) const {
+    const int rb = (sub * 32 + 16 * h2) * (D * 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + (o[dt][0] - kBias) + rb));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + (o[dt][1] - kBias) + rb));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void ring_pv(const VtOffsets<D>& vo, const char* Vt, int sub, const bf16x8 (&pf)[2],
+                                        f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(vo.frag(Vt, sub, h2, dt), pf[h2], acc[dt]);
+}
+
+// Online softmax of one 32-key subtile (lane = query row, 16 of the subtile's keys per
+// lane).  Returns the wave-uniform "reference maximum moved" flag; alpha is the factor
+// the accumulators must then be scaled by (1 on rows whose maximum did not move).
+// Branch-free, so it shares a basic block with the MFMAs it is scheduled against.
+__device__ __forceinline__ bool ring_softmax(const f32x16& s, float c2, float& m_run, float& l_run,
+                                             float& alpha, bf16x8 (&pf)[2]) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+  mx = fmaxf(mx, s[15]);
+  mx = pair_max(mx);
+  const float m_new = fmaxf(m_run, mx * c2);
+  const bool grow = __any(m_new > m_run + kRingRescaleLog2);
+  const float m_use = grow ? m_new : m_run;
+  alpha = fast_exp2(m_run - m_use);
+  m_run = m_use;
+  float ls = 0.0f;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[8 * h2 + i], c2, -m_use));
+    uint4 u;
+    u.x = pack_bf16x2(p[0], p[1]);
+    u.y = pack_bf16x2(p[2], p[3]);
+    u.z = pack_bf16x2(p[4], p[5]);
+    u.w = pack_bf16x2(p[6], p[7]);
+    pf[h2] = as_bf16x8(u);
+    ls = sum_bf16x8(u, ls);
+  }
+  l_run = fmaf(l_run, alpha, ls);
+  return grow;
+}
+
+// Empty volatile statement that takes the softmax outputs as register operands: it
+// cannot move, so the instructions producing them stay in the block it ends.
+__device__ __forceinline__ void pin_operands(const bf16x8 (&pf)[2], float l) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 a = __builtin_bit_cast(u32x4, pf[0]), b = __builtin_bit_cast(u32x4, pf[1]);
+  asm volatile("" ::"v"(a), "v"(b), "v"(l));
+}
+
+template <int D>
+__device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+}
+
+// Instruction pattern of one pipelined block: D/16 score MFMAs (one read per K
+// fragment), then, with PV, D/16 PV MFMAs (two transposing reads per V^T fragment).  Each
+// fragment is read two MFMAs ahead of its use (few fragments live at once), and each
+// MFMA is followed by a share of the softmax's vector work.
+template <int D, bool HAS_PV>
+__device__ __forceinline__ void ring_sched() {
+  constexpr int NK = D / 16, NV = D / 16;
+  constexpr int VALU = HAS_PV ? (D == 128 ? 4 : 8) : (D == 128 ? 8 : 16);
+  RR_SCHED_GROUP(RR_SG_DS_READ, 2);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    RR_SCHED_GROUP(RR_SG_MFMA, 1);
+    if (i < NK - 2) RR_SCHED_GROUP(RR_SG_DS_READ, 1);
+    else if (HAS_PV) RR_SCHED_GROUP(RR_SG_DS_READ, 2);
+    RR_SCHED_GROUP(RR_SG_VALU | RR_SG_TRANS, VALU);
+  }
+  if (HAS_PV) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      RR_SCHED_GROUP(RR_SG_MFMA, 1);
+      if (i < NV - 2) RR_SCHED_GROUP(RR_SG_DS_READ, 2);
+      RR_SCHED_GROUP(RR_SG_VALU | RR_SG_TRANS, VALU);
+    }
+  }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
+    Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
+    const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
+    const uint16_t* __restrict__ v_r, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  using C = RingCfg<D>;
+  constexpr int KS = C::KS, DT = C::DT;
+  // K tiles of the four stages first, then the V tiles: the K tiles then sit within the
+  // 16-bit immediate offset of one base address, the V tiles within that of another.
+  __shared__ __attribute__((aligned(1024))) char kt0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt3[C::TILE];
+  char* const KT[4] = {kt0, kt1, kt2, kt3};
+  char* const VT[4] = {vt0, vt1, vt2, vt3};
+
+  const TileWork w = decode_tile_work(g, C::BM);
+  if (!w.ok) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int m_hi = g.row_hi * g.grp;
+  const int r_first = w.m0 / g.grp;
+  const int r_top = (min(m_hi, w.m0 + C::BM) - 1) / g.grp;
+  const int rl = g.r_len[w.k];
+
+  const bool resp = w.part >= g.n_chunks;
+  int64_t key0, key1;
+  if (!resp) {
+    key0 = (int64_t)w.part * g.chunk;
+    key1 = min(g.P, key0 + g.chunk);
+  } else {
+    key0 = 0;
+    key1 = min(rl, r_top + 1);
+  }
+  const int64_t stride = (int64_t)g.Hkv * D;
+  const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
+  const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
+  const int n_keys = (r_first >= rl || (resp && !g.resp_keys)) ? 0 : (int)(key1 - key0);
+  // Workgroup-uniform subtile counts: [0, n_full) is visible to every row of the
+  // workgroup (its first row sees the fewest response keys), [n_full, n_sub) is masked.
+  const int lim_min = resp ? min(r_first, n_keys - 1) : n_keys - 1;
+  const int n_full = n_keys > 0 ? (lim_min + 1) / 32 : 0;
+  const int n_sub = (n_keys + 31) / 32;
+  const int n_stages = (n_keys + C::BN - 1) / C::BN;
+
+  const int64_t sbytes = stride * 2;
+  const uint16_t* kc = kb + key0 * stride;
+  const uint16_t* vc = vb + key0 * stride;
+  DirectLoadRows<D, C::BN, C::WAVES> dl;
+  dl.init();
+  Frag<D> fr;
+  fr.init();
+  VtOffsets<D> vo;
+  vo.init(fr);
+
+  auto issue_stage = [&](int b, int s) {
+    const int64_t off = (int64_t)s * C::BN * sbytes;
+    const int rows = n_keys - s * C::BN;
+    dl.issue(KT[b], reinterpret_cast<const char*>(kc) + off, rows, (uint32_t)sbytes);
+    dl.issue(VT[b], reinterpret_cast<const char*>(vc) + off, rows, (uint32_t)sbytes);
+  };
+  auto issue_any = [&](int s) {
+    switch (s & 3) {
+      case 0: issue_stage(0, s); break;
+      case 1: issue_stage(1, s); break;
+      case 2: issue_stage(2, s); break;
+      default: issue_stage(3, s); break;
+    }
+  };
+  // Entering stage s: its loads are done (only stage s+1's may still be in flight), every
+  // wave is past its reads of stage s-2's buffer, and stage s+2 is loaded into it.
+  int entered = -1;
+  auto enter_stage = [&](int s) {
+    if (s + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+    __syncthreads();
+    if (s + 2 < n_stages) issue_any(s + 2);
+    entered = s;
+  };
+  if (n_stages > 0) issue_any(0);
+  if (n_stages > 1) issue_any(1);
+
+  const int m = w.m0 + wave * 32 + col;
+  const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
+  const bool valid = m < m_hi && r < rl;
+  const int lim = resp ? min(r, n_keys - 1) : n_keys - 1;
+  const int64_t orow = m < m_hi ? (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h : -1;
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = q + (((int64_t)w.k * g.R + r) * g.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hl * 8)
+                               : make_uint4(0, 0, 0, 0));
+  }
+  int wmax = lim;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, 64));
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  float m_run = kNegBig, l_run = 0.0f;
+  const float c2 = g.c2;
+
+  if (n_keys > 0) enter_stage(0);
+
+  if (n_full > 0) {
+    f32x16 s;
+    ring_scores<D>(fr, KT[0], 0, qf, s);    // S(0)
+    bf16x8 pp[2];                          // P(u-1)
+
+    // Block B(u), u = J mod 8: PV(u-1) and S(u+1) on the matrix cores, softmax of u on the
+    // vector ALUs; compile-time buffers.  The last block also computes S(n_full), which is
+    // never used (the masked path recomputes it) and reads a buffer with no loads in flight.
+    auto block = [&](auto jc, auto pvc, int u) {
+      constexpr int J = decltype(jc)::value;
+      constexpr bool HAS_PV = decltype(pvc)::value;
+      constexpr int SX = ((J + 7) >> 1) & 3, SUBX = (J + 7) & 1;   // subtile u-1
+      constexpr int SY = ((J + 1) >> 1) & 3, SUBY = (J + 1) & 1;   // subtile u+1
+      constexpr int SN = (SY + 2) & 3;                              // stage u/2 + 3's buffer
+      if (J & 1) {   // subtile u+1 starts stage (u+1)/2
+        const int st = (u + 1) >> 1;
+        if (st + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+        __syncthreads();
+        if (st + 2 < n_stages) issue_stage(SN, st + 2);
+        entered = st;
+      }
+      bf16x8 pn[2];
+      float alpha;
+      f32x16 sn;
+      ring_scores<D>(fr, KT[SY], SUBY, qf, sn);
+      if (HAS_PV) ring_pv<D>(vo, VT[SX], SUBX, pp, acc);
+      const bool grow = ring_softmax(s, c2, m_run, l_run, alpha, pn);
+      ring_sched<D, HAS_PV>();
+      // the block's softmax results must be formed here, not sunk past the rescale branch
+      pin_operands(pn, l_run);
+      if (grow) ring_scale<D>(acc, alpha);
+      pp[0] = pn[0];
+      pp[1] = pn[1];
+      s = sn;
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    block(std::integral_constant<int, 0>{}, F{}, 0);
+    int u = 1;
+    // straight-line groups of eight blocks (u = 8i+1 .. 8i+8), so that every block's
+    // buffers are compile-time and one block's softmax feeds the next block directly
+    for (; u + 8 <= n_full; u += 8) {
+      block(std::integral_constant<int, 1>{}, T{}, u);
+      block(std::integral_constant<int, 2>{}, T{}, u + 1);
+      block(std::integral_constant<int, 3>{}, T{}, u + 2);
+      block(std::integral_constant<int, 4>{}, T{}, u + 3);
+      block(std::integral_constant<int, 5>{}, T{}, u + 4);
+      block(std::integral_constant<int, 6>{}, T{}, u + 5);
+      block(std::integral_constant<int, 7>{}, T{}, u + 6);
+      block(std::integral_constant<int, 0>{}, T{}, u + 7);
+    }
+    if (u < n_full) block(std::integral_constant<int, 1>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 2>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 3>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 4>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 5>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 6>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 7>{}, T{}, u++);
+    // PV of the last pipelined subtile
+    const int ul = n_full - 1;
+    switch ((ul >> 1) & 3) {
+      case 0: ring_pv<D>(vo, VT[0], ul & 1, pp, acc); break;
+      case 1: ring_pv<D>(vo, VT[1], ul & 1, pp, acc); break;
+      case 2: ring_pv<D>(vo, VT[2], ul & 1, pp, acc); break;
+      default: ring_pv<D>(vo, VT[3], ul & 1, pp, acc); break;
+    }
+  }
+
+  // Masked subtiles near the causal diagonal or a chunk end (keys past a row's limit
+  // are invisible to it).
+  for (int u = n_full; u < n_sub; ++u) {
+    const int st = u >> 1;
+    while (entered < st) enter_stage(entered + 1);
+    const int rel = u * 32;
+    if (rel > wmax) continue;
+    const int b = st & 3;
+    const char* const kt = b == 0 ? kt0 : b == 1 ? kt1 : b == 2 ? kt2 : kt3;
+    const char* const vt = b == 0 ? vt0 : b == 1 ? vt1 : b == 2 ? vt2 : vt3;
+    f32x16 s;
+    ring_scores<D>(fr, kt, u & 1, qf, s);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
+      if (key > lim) s[i] = -INFINITY;
+    }
+    bf16x8 pf[2];
+    float alpha;
+    if (ring_softmax(s, c2, m_run, l_run, alpha, pf)) ring_scale<D>(acc, alpha);
+    ring_pv<D>(vo, vt, u & 1, pf, acc);
+  }
+
+  const float l = pair_sum(l_run);
+  if (orow < 0) return;
+  const bool live = valid && l > 0.0f;
+  const float inv = live ? 1.0f / l : 0.0f;
+  float* dst = part_o + orow * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = dt * 32 + i4 * 8 + hl * 4;
+      *reinterpret_cast<float4*>(dst + d0) =
+          make_float4(acc[dt][4 * i4 + 0] * inv, acc[dt][4 * i4 + 1] * inv,
+                      acc[dt][4 * i4 + 2] * inv, acc[dt][4 * i4 + 3] * inv);
+    }
+  if (hl == 0) part_lse[orow] = live ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_fwd_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
+  const int64_t n = tile_work_count(g, RingCfg<128>::BM);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)xcd_grid(n)), block(64 * RingCfg<128>::WAVES);
+  const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
+  const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r;
+  if (g.dqk == 64)
+    hipLaunchKernelGGL(fwd_ring_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
+  else
+    hipLaunchKernelGGL(fwd_ring_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace rr

@@ -92,6 +92,40 @@ struct DirectLoad {
   }
 };
 
+// Lighter form of DirectLoad::issue: tile rows [0, N_ROWS) <- rows of a stream whose row 0
+// starts at the wave-uniform address `base`; rows at or past `rows_valid` (>= 1) re-read
+// row rows_valid - 1 (their values are masked by the caller).  Only the base is 64-bit;
+// lane offsets are 32-bit, so N_ROWS * stride_bytes must stay below 2^31.
+template <int D, int N_ROWS, int WAVES>
+struct DirectLoadRows {
+  using DL = DirectLoad<D, N_ROWS, WAVES>;
+  static constexpr int G = DL::G, RPI = DL::RPI, PER_WAVE = DL::PER_WAVE;
+  uint32_t gran[4];     // swizzled granule byte offset, by instruction index mod 4
+  int row0;             // first tile row of this wave
+  int r_lane;           // row of this lane inside an instruction
+
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    row0 = wave * PER_WAVE * RPI;
+    r_lane = lane / G;
+#pragma unroll
+    for (int par = 0; par < 4; ++par) {
+      const int r = row0 + RPI * par + r_lane;
+      gran[par] = (uint32_t)(((lane % G) ^ Swz<D>::f(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(char* tile, const char* base, int rows_valid,
+                                        uint32_t stride_bytes) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int p0 = (row0 / RPI + i) * 64;            // first granule of this instruction
+      const int row = min(row0 + RPI * i + r_lane, rows_valid - 1);
+      const uint32_t off = (uint32_t)row * stride_bytes + gran[i & 3];
+      __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(tile + p0 * 16), 16, 0, 0);
+    }
+  }
+};
+
 // Fragment reads from a swizzled [rows][D] tile.  Every read address is a per-lane
 // offset computed once (the swizzle depends only on the row mod 16, and the subtile and
 // half-subtile row offsets used below are multiples of 16 rows) plus a compile-time
