@@ -448,7 +448,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
     }
 }
 
+hipError_t launch_dq_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
+
 hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
+#ifndef RR_DQ_OLD
+  return launch_dq_ring_bf16(g, a, s);
+#endif
   const int64_t n = tile_work_count(g, DqCfg<128>::BM);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)xcd_grid(n)), block(64 * DqCfg<128>::WAVES);

@@ -8,28 +8,33 @@
 // longstraw-2m-rl, section "Two incompatible architectures, same transaction").
 //
 // Rows: flattened m = r * grp + hh over the grp query heads that read KV head g, so one
-// K/V tile feeds all of them.  8 waves x 32 rows (two waves per SIMD); each wave keeps its
-// Q fragments and its O^T accumulators (d x rows, fp32) in registers for the whole part.
+// K/V tile feeds all of them.  A wave owns NT 32-row tiles: 8 waves x 32 rows (two waves
+// per SIMD, NT = 1) or 4 waves x 64 rows (one wave per SIMD, NT = 2, where every K or V
+// fragment read from LDS feeds two MFMAs).  Each wave keeps its Q fragments and its O^T
+// accumulators (d x rows, fp32) in registers for the whole part.
 //
 // K/V stream: 64-key stages in a ring of four LDS buffers, loaded straight from global
-// memory into LDS two stages ahead; one barrier per stage.  The buffers are separate
-// arrays and every read names its buffer at compile time, so the compiler can tell a read
-// of one buffer from the direct loads still landing in another.
+// memory into LDS two stages ahead; one barrier per stage.  The K and V tiles of the
+// four stages are separate arrays and every read names its buffer at compile time, so the
+// compiler can tell a read of one buffer from the direct loads still landing in another.
 //
 // Pipeline over 32-key subtiles u, per wave: block B(u) issues O^T += V^T P^T of subtile
-// u-1 and S^T = K Q^T of subtile u+1 on the matrix cores (16 MFMAs with no dependence on
-// the block's vector work) while the vector ALUs run the online softmax of subtile u
-// (base 2, lazy rescale: the reference maximum only moves when a row's maximum grows by
-// more than 2^8, so every p <= 256; P^T rounded to bf16 straight from the C registers,
-// and the running sum l adds up exactly those rounded values).  A rescale of the
-// accumulators is applied at the end of the block, between PV(u-1) and PV(u).  The block
-// sequence runs across stage boundaries, so every block carries the same balanced load.
-// Subtiles whose keys are visible to every row of the workgroup run this pipeline; the
-// few near the causal diagonal or a chunk end run a masked, unpipelined path afterwards.
+// u-1 and S^T = K Q^T of subtile u+1 on the matrix cores (MFMAs with no dependence on the
+// block's vector work) while the vector ALUs run the online softmax of subtile u (base 2,
+// lazy rescale: the reference maximum only moves when a row's maximum grows by more than
+// 2^8, so every p <= 256; P^T rounded to bf16 straight from the C registers, and the
+// running sum l adds up exactly those rounded values).  The block is laid out by hand in
+// slots (one fragment read two slots ahead, its MFMAs, a fixed share of the softmax),
+// separated by scheduling barriers.  A rescale of the accumulators is applied at the end
+// of the block, between PV(u-1) and PV(u).  The block sequence runs across stage
+// boundaries, so every block carries the same balanced load.  Subtiles whose keys are
+// visible to every row of the workgroup run this pipeline; the few near the causal
+// diagonal or a chunk end run a masked, unpipelined path afterwards.
 #include <type_traits>
 
 #include "k_attn_tile.h"
 #include "k_lds.h"
+#include "k_ring.h"
 #include "kernels.h"
 
 namespace rr {
@@ -38,73 +43,48 @@ namespace {
 
 constexpr float kRingRescaleLog2 = 8.0f;   // log2 of the largest p between rescales
 
-template <int D>
+template <int D, int NT>
 struct RingCfg {
-  static constexpr int WAVES = 8;
-  static constexpr int BM = WAVES * 32;                 // query rows per workgroup
+  static constexpr int WAVES = 8 / NT;
+  static constexpr int BM = WAVES * 32 * NT;            // query rows per workgroup
   static constexpr int BN = 64;                         // keys per stage
   static constexpr int KS = D / 16, DT = D / 32;
   static constexpr int TILE = BN * D * 2;               // bytes of one [BN][D] bf16 tile
   static constexpr int LOADS = 2 * (BN * D / 8) / (64 * WAVES);   // direct loads per wave per stage
 };
 
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding, n < 16).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void ring_scores(const Frag<D>& fr, const char* Kt, int sub,
-                                            const bf16x8 (&qf)[D / 16], f32x16& s) {
+                                            const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) s = mfma32x32x16(fr.row(Kt, sub, ks), qf[ks], s);
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 kf = fr.row(Kt, sub, ks);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf, qf[t][ks], s[t]);
+  }
 }
 
-// Lane offsets of the V^T fragment reads, biased by 2^16 and hidden from the compiler:
-// the V tiles lie above the 16-bit immediate offset range of a LDS read, and with the
-// bias every V buffer is reached as (one set of offset registers) + immediate instead
-// of one register set per buffer.
-template <int D>
-struct VtOffsets {
-  static constexpr uint32_t kBias = 1u << 16;
-  uint32_t o[D / 32][2];
-  __device__ __forceinline__ void init(const Frag<D>& fr) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        o[dt][hi] = fr.trans[dt][hi] + kBias;
-        asm volatile("" : "+v"(o[dt][hi]));
-      }
-  }
-  // V^T fragment (see Frag::trans_frag) of a V tile at `vt`.
-  __device__ __forceinline__ bf16x8 frag(const char* vt, int sub, int h2, int dt) const {
-    const int rb = (sub * 32 + 16 * h2) * (D * 2);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + (o[dt][0] - kBias) + rb));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + (o[dt][1] - kBias) + rb));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void ring_pv(const VtOffsets<D>& vo, const char* Vt, int sub, const bf16x8 (&pf)[2],
-                                        f32x16 (&acc)[D / 32]) {
+template <int D, int NT>
+__device__ __forceinline__ void ring_pv(const FarFrags<D>& vo, const char* Vt, int sub,
+                                        const bf16x8 (&pf)[NT][2], f32x16 (&acc)[NT][D / 32]) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(vo.frag(Vt, sub, h2, dt), pf[h2], acc[dt]);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 vf = vo.trans_frag(Vt, sub, h2, dt);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf, pf[t][h2], acc[t][dt]);
+    }
 }
 
-// Online softmax of one 32-key subtile (lane = query row, 16 of the subtile's keys per
-// lane).  Returns the wave-uniform "reference maximum moved" flag; alpha is the factor
-// the accumulators must then be scaled by (1 on rows whose maximum did not move).
-// Branch-free, so it shares a basic block with the MFMAs it is scheduled against.
+// Online softmax of one 32-key subtile of one tile (lane = query row, 16 of the subtile's
+// keys per lane), unpipelined form for the masked path.  Returns the wave-uniform
+// "reference maximum moved" flag; alpha is the factor the accumulators must then be
+// scaled by (1 on rows whose maximum did not move).
 __device__ __forceinline__ bool ring_softmax(const f32x16& s, float c2, float& m_run, float& l_run,
                                              float& alpha, bf16x8 (&pf)[2]) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
@@ -135,14 +115,6 @@ __device__ __forceinline__ bool ring_softmax(const f32x16& s, float c2, float& m
   return grow;
 }
 
-// Empty volatile statement that takes the softmax outputs as register operands: it
-// cannot move, so the instructions producing them stay in the block it ends.
-__device__ __forceinline__ void pin_operands(const bf16x8 (&pf)[2], float l) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 a = __builtin_bit_cast(u32x4, pf[0]), b = __builtin_bit_cast(u32x4, pf[1]);
-  asm volatile("" ::"v"(a), "v"(b), "v"(l));
-}
-
 template <int D>
 __device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
 #pragma unroll
@@ -151,40 +123,112 @@ __device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
     for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
 }
 
-// Instruction pattern of one pipelined block: D/16 score MFMAs (one read per K
-// fragment), then, with PV, D/16 PV MFMAs (two transposing reads per V^T fragment).  Each
-// fragment is read two MFMAs ahead of its use (few fragments live at once), and each
-// MFMA is followed by a share of the softmax's vector work.
-template <int D, bool HAS_PV>
-__device__ __forceinline__ void ring_sched() {
-  constexpr int NK = D / 16, NV = D / 16;
-  constexpr int VALU = HAS_PV ? (D == 128 ? 4 : 8) : (D == 128 ? 8 : 16);
-  RR_SCHED_GROUP(RR_SG_DS_READ, 2);
-#pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    RR_SCHED_GROUP(RR_SG_MFMA, 1);
-    if (i < NK - 2) RR_SCHED_GROUP(RR_SG_DS_READ, 1);
-    else if (HAS_PV) RR_SCHED_GROUP(RR_SG_DS_READ, 2);
-    RR_SCHED_GROUP(RR_SG_VALU | RR_SG_TRANS, VALU);
-  }
-  if (HAS_PV) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      RR_SCHED_GROUP(RR_SG_MFMA, 1);
-      if (i < NV - 2) RR_SCHED_GROUP(RR_SG_DS_READ, 2);
-      RR_SCHED_GROUP(RR_SG_VALU | RR_SG_TRANS, VALU);
+// One pipelined block, laid out by hand as NSLOT slots separated by scheduling
+// barriers.  Slot i issues the LDS reads of slot i+2's fragment (so every read has two
+// slots' time to land), then the NT MFMAs of its own fragment, then a fixed share of the
+// softmax of subtile u for every tile: the row maximum over the first slots, then the
+// reference-maximum update, then the exponentials in pairs (each pair packed to bf16 and
+// added to the running sum at once), spread over the remaining slots.  With PV, even
+// slots hold the K fragments of subtile u+1's scores and odd slots the V^T fragments of
+// subtile u-1's PV.  Sets, per tile, the wave-uniform flag "the reference maximum moved"
+// (the caller then scales that tile's accumulators by alpha).
+template <int D, int NT, bool HAS_PV>
+__device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrags<D>& vo, const char* Kt,
+                                                int subk, const char* Vt, int subv,
+                                                const bf16x8 (&qf)[NT][D / 16], const f32x16 (&s)[NT],
+                                                const bf16x8 (&pp)[NT][2], f32x16 (&acc)[NT][D / 32],
+                                                float c2, float (&m_run)[NT], float (&l_run)[NT],
+                                                float (&alpha)[NT], bool (&grow)[NT], f32x16 (&sn)[NT],
+                                                bf16x8 (&pn)[NT][2]) {
+  constexpr int KS = D / 16;
+  constexpr int NSLOT = (HAS_PV ? 2 : 1) * KS;
+  constexpr int MAXS = NSLOT >= 8 ? 2 : 1;          // slots of the max tree
+  constexpr int FIN = MAXS;                          // slot of the reference-maximum update
+  constexpr int E = NSLOT - FIN - 1;                 // slots of the exponentials
+  auto load = [&](int i) -> bf16x8 {
+    if (HAS_PV && (i & 1)) {
+      const int j = i >> 1;
+      return vo.trans_frag(Vt, subv, j & 1, j >> 1);
     }
+    return fr.row(Kt, subk, HAS_PV ? (i >> 1) : i);
+  };
+  bf16x8 frag[NSLOT];
+  frag[0] = load(0);
+  frag[1] = load(1);
+  float mx[NT], m_use[NT], ls[NT];
+  uint32_t w[NT][8];
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < NSLOT; ++i) {
+    if (i + 2 < NSLOT) frag[i + 2] = load(i + 2);
+    if (HAS_PV && (i & 1)) {
+      const int j = i >> 1;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][j >> 1] = mfma32x32x16(frag[i], pp[t][j & 1], acc[t][j >> 1]);
+    } else {
+      const int ks = HAS_PV ? (i >> 1) : i;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (ks == 0) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sn[t][e] = 0.0f;
+        }
+        sn[t] = mfma32x32x16(frag[i], qf[t][ks], sn[t]);
+      }
+    }
+    // this slot's share of the softmax, for every tile
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x16& st = s[t];
+      if (i == 0) {
+        mx[t] = fmaxf(fmaxf(st[0], st[1]), st[2]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[3]), st[4]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[5]), st[6]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[7]), st[8]);
+      }
+      if (i == MAXS - 1) {
+        mx[t] = fmaxf(fmaxf(mx[t], st[9]), st[10]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[11]), st[12]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[13]), st[14]);
+        mx[t] = fmaxf(mx[t], st[15]);
+      }
+      if (i == FIN) {
+        mx[t] = pair_max(mx[t]);
+        const float m_new = fmaxf(m_run[t], mx[t] * c2);
+        grow[t] = __any(m_new > m_run[t] + kRingRescaleLog2);
+        m_use[t] = grow[t] ? m_new : m_run[t];
+        alpha[t] = fast_exp2(m_run[t] - m_use[t]);
+        m_run[t] = m_use[t];
+        ls[t] = 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (i == FIN + 1 + (k * E) / 8) {
+          const float p0 = fast_exp2(fmaf(st[2 * k], c2, -m_use[t]));
+          const float p1 = fast_exp2(fmaf(st[2 * k + 1], c2, -m_use[t]));
+          w[t][k] = pack_bf16x2(p0, p1);
+          ls[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[t][k]), one, ls[t], false);
+        }
+      }
+      if (i == NSLOT - 1) l_run[t] = fmaf(l_run[t], alpha[t], ls[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    pn[t][0] = as_bf16x8(make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]));
+    pn[t][1] = as_bf16x8(make_uint4(w[t][4], w[t][5], w[t][6], w[t][7]));
   }
 }
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
+template <int D, int NT>
+__global__ __launch_bounds__(512 / NT, 1) void fwd_ring_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
     const uint16_t* __restrict__ v_r, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  using C = RingCfg<D>;
+  using C = RingCfg<D, NT>;
   constexpr int KS = C::KS, DT = C::DT;
   // K tiles of the four stages first, then the V tiles: the K tiles then sit within the
   // 16-bit immediate offset of one base address, the V tiles within that of another.
@@ -235,8 +279,8 @@ __global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
   dl.init();
   Frag<D> fr;
   fr.init();
-  VtOffsets<D> vo;
-  vo.init(fr);
+  FarFrags<D> vo;
+  vo.template init<false, true>(fr);
 
   auto issue_stage = [&](int b, int s) {
     const int64_t off = (int64_t)s * C::BN * sbytes;
@@ -264,37 +308,47 @@ __global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
   if (n_stages > 0) issue_any(0);
   if (n_stages > 1) issue_any(1);
 
-  const int m = w.m0 + wave * 32 + col;
-  const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
-  const bool valid = m < m_hi && r < rl;
-  const int lim = resp ? min(r, n_keys - 1) : n_keys - 1;
-  const int64_t orow = m < m_hi ? (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h : -1;
-  bf16x8 qf[KS];
-  {
+  int lim[NT];
+  bool valid[NT];
+  int64_t orow[NT];
+  bf16x8 qf[NT][KS];
+  int wmax = -1;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = w.m0 + (wave * NT + t) * 32 + col;
+    const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
+    valid[t] = m < m_hi && r < rl;
+    lim[t] = resp ? min(r, n_keys - 1) : n_keys - 1;
+    orow[t] = m < m_hi ? (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h : -1;
     const uint16_t* qrow = q + (((int64_t)w.k * g.R + r) * g.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hl * 8)
-                               : make_uint4(0, 0, 0, 0));
+      qf[t][ks] = as_bf16x8(valid[t] ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hl * 8)
+                                     : make_uint4(0, 0, 0, 0));
+    wmax = max(wmax, lim[t]);
   }
-  int wmax = lim;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, 64));
 
-  f32x16 acc[DT];
+  f32x16 acc[NT][DT];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = kNegBig;
+    l_run[t] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
-  float m_run = kNegBig, l_run = 0.0f;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][dt][i] = 0.0f;
+  }
   const float c2 = g.c2;
 
   if (n_keys > 0) enter_stage(0);
 
   if (n_full > 0) {
-    f32x16 s;
-    ring_scores<D>(fr, KT[0], 0, qf, s);    // S(0)
-    bf16x8 pp[2];                          // P(u-1)
+    f32x16 s[NT];
+    ring_scores<D, NT>(fr, KT[0], 0, qf, s);    // S(0)
+    bf16x8 pp[NT][2];                           // P(u-1)
 
     // Block B(u), u = J mod 8: PV(u-1) and S(u+1) on the matrix cores, softmax of u on the
     // vector ALUs; compile-time buffers.  The last block also computes S(n_full), which is
@@ -312,19 +366,24 @@ __global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
         if (st + 2 < n_stages) issue_stage(SN, st + 2);
         entered = st;
       }
-      bf16x8 pn[2];
-      float alpha;
-      f32x16 sn;
-      ring_scores<D>(fr, KT[SY], SUBY, qf, sn);
-      if (HAS_PV) ring_pv<D>(vo, VT[SX], SUBX, pp, acc);
-      const bool grow = ring_softmax(s, c2, m_run, l_run, alpha, pn);
-      ring_sched<D, HAS_PV>();
-      // the block's softmax results must be formed here, not sunk past the rescale branch
-      pin_operands(pn, l_run);
-      if (grow) ring_scale<D>(acc, alpha);
-      pp[0] = pn[0];
-      pp[1] = pn[1];
-      s = sn;
+      bf16x8 pn[NT][2];
+      float alpha[NT];
+      bool grow[NT];
+      f32x16 sn[NT];
+      ring_block_body<D, NT, HAS_PV>(fr, vo, KT[SY], SUBY, VT[SX], SUBX, qf, s, pp, acc, c2, m_run, l_run,
+                                     alpha, grow, sn, pn);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // the block's softmax results must be formed here, not sunk past the rescale branch
+        pin_operands(pn[t], l_run[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (grow[t]) ring_scale<D>(acc[t], alpha[t]);
+        pp[t][0] = pn[t][0];
+        pp[t][1] = pn[t][1];
+        s[t] = sn[t];
+      }
     };
     using T = std::true_type;
     using F = std::false_type;
@@ -352,10 +411,10 @@ __global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
     // PV of the last pipelined subtile
     const int ul = n_full - 1;
     switch ((ul >> 1) & 3) {
-      case 0: ring_pv<D>(vo, VT[0], ul & 1, pp, acc); break;
-      case 1: ring_pv<D>(vo, VT[1], ul & 1, pp, acc); break;
-      case 2: ring_pv<D>(vo, VT[2], ul & 1, pp, acc); break;
-      default: ring_pv<D>(vo, VT[3], ul & 1, pp, acc); break;
+      case 0: ring_pv<D, NT>(vo, VT[0], ul & 1, pp, acc); break;
+      case 1: ring_pv<D, NT>(vo, VT[1], ul & 1, pp, acc); break;
+      case 2: ring_pv<D, NT>(vo, VT[2], ul & 1, pp, acc); break;
+      default: ring_pv<D, NT>(vo, VT[3], ul & 1, pp, acc); break;
     }
   }
 
@@ -369,46 +428,62 @@ __global__ __launch_bounds__(512, 1) void fwd_ring_bf16(
     const int b = st & 3;
     const char* const kt = b == 0 ? kt0 : b == 1 ? kt1 : b == 2 ? kt2 : kt3;
     const char* const vt = b == 0 ? vt0 : b == 1 ? vt1 : b == 2 ? vt2 : vt3;
-    f32x16 s;
-    ring_scores<D>(fr, kt, u & 1, qf, s);
+    f32x16 s[NT];
+    ring_scores<D, NT>(fr, kt, u & 1, qf, s);
+    bf16x8 pf[NT][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
-      if (key > lim) s[i] = -INFINITY;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
+        if (key > lim[t]) s[t][i] = -INFINITY;
+      }
+      float alpha;
+      if (ring_softmax(s[t], c2, m_run[t], l_run[t], alpha, pf[t])) ring_scale<D>(acc[t], alpha);
     }
-    bf16x8 pf[2];
-    float alpha;
-    if (ring_softmax(s, c2, m_run, l_run, alpha, pf)) ring_scale<D>(acc, alpha);
-    ring_pv<D>(vo, vt, u & 1, pf, acc);
+    ring_pv<D, NT>(vo, vt, u & 1, pf, acc);
   }
 
-  const float l = pair_sum(l_run);
-  if (orow < 0) return;
-  const bool live = valid && l > 0.0f;
-  const float inv = live ? 1.0f / l : 0.0f;
-  float* dst = part_o + orow * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int t = 0; t < NT; ++t) {
+    const float l = pair_sum(l_run[t]);
+    if (orow[t] < 0) continue;
+    const bool live = valid[t] && l > 0.0f;
+    const float inv = live ? 1.0f / l : 0.0f;
+    float* dst = part_o + orow[t] * D;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = dt * 32 + i4 * 8 + hl * 4;
-      *reinterpret_cast<float4*>(dst + d0) =
-          make_float4(acc[dt][4 * i4 + 0] * inv, acc[dt][4 * i4 + 1] * inv,
-                      acc[dt][4 * i4 + 2] * inv, acc[dt][4 * i4 + 3] * inv);
-    }
-  if (hl == 0) part_lse[orow] = live ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = dt * 32 + i4 * 8 + hl * 4;
+        *reinterpret_cast<float4*>(dst + d0) =
+            make_float4(acc[t][dt][4 * i4 + 0] * inv, acc[t][dt][4 * i4 + 1] * inv,
+                        acc[t][dt][4 * i4 + 2] * inv, acc[t][dt][4 * i4 + 3] * inv);
+      }
+    if (hl == 0) part_lse[orow[t]] = live ? (m_run[t] + log2f(l)) * kLn2 : -INFINITY;
+  }
 }
 
+#ifndef RR_FWD_NT
+#define RR_FWD_NT 1
+#endif
+
 hipError_t launch_fwd_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
-  const int64_t n = tile_work_count(g, RingCfg<128>::BM);
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)xcd_grid(n)), block(64 * RingCfg<128>::WAVES);
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r;
-  if (g.dqk == 64)
-    hipLaunchKernelGGL(fwd_ring_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
-  else
-    hipLaunchKernelGGL(fwd_ring_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
+  if (g.dqk == 64) {
+    using C = RingCfg<64, 1>;
+    const int64_t n = tile_work_count(g, C::BM);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_ring_bf16<64, 1>), dim3((unsigned)xcd_grid(n)), dim3(64 * C::WAVES), 0, s, g, q,
+                       kp, vp, kr, vr, a.part_o, a.part_lse);
+  } else {
+    using C = RingCfg<128, RR_FWD_NT>;
+    const int64_t n = tile_work_count(g, C::BM);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_ring_bf16<128, RR_FWD_NT>), dim3((unsigned)xcd_grid(n)), dim3(64 * C::WAVES), 0, s,
+                       g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
+  }
   return hipGetLastError();
 }
 
