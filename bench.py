@@ -76,8 +76,8 @@ def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
 
 
 KERNEL_SOURCES = {
-    "fwd_partials": ["k_fwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "dq_partials": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "fwd_partials": ["k_fwd_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "dq_partials": ["k_dq_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
     "dkdv": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
 }
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librr_attn.so")
-SOURCES = ["rr_validate.cpp", "rr_api.cpp", "k_small.hip", "k_f32.hip", "k_fwd_bf16.hip", "k_fwd_ring_bf16.hip", "k_dq_ring_bf16.hip",
+SOURCES = ["rr_validate.cpp", "rr_api.cpp", "k_small.hip", "k_f32.hip", "k_fwd_bf16.hip", "k_dq_bf16.hip",
            "k_bwd_bf16.hip", "k_topk.hip", "k_sparse.hip"]
 ARCH = "gfx950"
 
@@ -40,7 +40,7 @@ def flags() -> list:
 # Per-source additions.  The attention kernels never produce or consume NaN (masked scores
 # are -inf, empty rows are handled explicitly), so max/min need no NaN canonicalisation.
 SOURCE_FLAGS = {
-    "k_fwd_ring_bf16.hip": ["-fno-honor-nans"],
+    "k_fwd_bf16.hip": ["-fno-honor-nans"],
 }
 
 

@@ -1,16 +1,11 @@
-// bf16 response-only backward on MFMA (gfx950).
+// bf16 response dK/dV on MFMA (gfx950): the reverse block walk over the response's own
+// keys.
 //
 // Source of the contract: ai.thesatyajit.com/articles/longstraw-2m-rl, sections "The
 // move: change the graph boundary" (the resident prompt state is a stop-gradient: only
 // the direct response gradient is formed) and "Two incompatible architectures, same
 // transaction" (response blocks replayed in reverse; K/V gradient storage only for
 // what a response backward touches).  No kernel here reads or writes a prompt gradient.
-//
-// dq_partials_bf16: query-parallel, one workgroup per (k, g, part, 256-row tile) like
-// the forward; per 32-key subtile S^T = K Q^T and dP^T = V dO^T - D (2 x D/16 MFMAs, the
-// second accumulation starting from -D), p = 2^(S c2 - lse2), dS = p (dP - D) rounded to
-// bf16, dQ^T += K^T dS^T (D/16 MFMAs).
-// Writes one dQ partial per part; the partials are summed in part order afterwards.
 //
 // dkdv_bf16: key-parallel over the response keys, one workgroup per (k, g, 128 keys),
 // each wave owning 32 keys (K, V fragments in registers, dK^T and dV^T accumulators in
@@ -23,189 +18,6 @@
 #include "kernels.h"
 
 namespace rr {
-
-#ifndef RR_DQ_WAVES
-#define RR_DQ_WAVES 8
-#endif
-
-template <int D>
-struct DqCfg {
-  static constexpr int WAVES = RR_DQ_WAVES;
-  static constexpr int BM = WAVES * 32;          // query rows per workgroup (32 per wave)
-  static constexpr int BN = 128;                 // keys per LDS stage
-  static constexpr int NSUB = BN / 32;
-  static constexpr int KS = D / 16, DT = D / 32;
-  static constexpr int TILE = BN * D * 2;
-};
-
-// One 32-key subtile of the dQ accumulation for this wave's 32 rows.
-// The dP^T accumulation starts from dinit (every element -D of the lane's row), so the
-// MFMAs deliver dP - D directly and dS = P (dP - D) is one multiply per element.
-template <bool MASK, int D>
-__device__ __forceinline__ void dq_subtile(const Frag<D>& fr, const char* Kt, const char* Vt, int sub,
-                                           int rel, int lim,
-                                           float c2, float lse2, const f32x16& dinit,
-                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&of)[D / 16],
-                                           f32x16 (&acc)[D / 32]) {
-  constexpr int KS = D / 16, DT = D / 32;
-  const int hl = (threadIdx.x & 63) >> 5;
-  f32x16 s, dp = dinit;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-  prio_mfma();
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 ak = fr.row(Kt, sub, ks);
-    const bf16x8 av = fr.row(Vt, sub, ks);
-    s = mfma32x32x16(ak, qf[ks], s);
-    dp = mfma32x32x16(av, of[ks], dp);
-  }
-  prio_valu();
-  float ds[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float p = fast_exp2(fmaf(s[i], c2, -lse2));
-    if (MASK) {
-      const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
-      if (key > lim) p = 0.0f;
-    }
-    ds[i] = p * dp[i];
-  }
-  bf16x8 dsf[2];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    uint4 u;
-    u.x = pack_bf16x2(ds[8 * h2 + 0], ds[8 * h2 + 1]);
-    u.y = pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]);
-    u.z = pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]);
-    u.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
-    dsf[h2] = as_bf16x8(u);
-  }
-  prio_mfma();
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-      acc[dt] = mfma32x32x16(fr.trans_frag(Kt, sub, h2, dt), dsf[h2], acc[dt]);
-  prio_valu();
-}
-
-template <int D>
-__global__ __launch_bounds__(64 * RR_DQ_WAVES, 1) void dq_partials_bf16(
-    Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
-    const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
-    const uint16_t* __restrict__ v_r, const uint16_t* __restrict__ d_o,
-    const float* __restrict__ lse, const float* __restrict__ Dvec, float* __restrict__ dq_part) {
-  using C = DqCfg<D>;
-  constexpr int KS = C::KS, DT = C::DT;
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * C::TILE];   // K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * C::TILE];
-
-  const TileWork w = decode_tile_work(g, C::BM);
-  if (!w.ok) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hl = lane >> 5, col = lane & 31;
-  const int m_hi = g.row_hi * g.grp;
-  const int r_first = w.m0 / g.grp;
-  const int r_top = (min(m_hi, w.m0 + C::BM) - 1) / g.grp;
-  const int rl = g.r_len[w.k];
-
-  const bool resp = w.part >= g.n_chunks;
-  int64_t key0, key1;
-  if (!resp) {
-    key0 = (int64_t)w.part * g.chunk;
-    key1 = min(g.P, key0 + g.chunk);
-  } else {
-    key0 = 0;
-    key1 = min(rl, r_top + 1);
-  }
-  const int64_t stride = (int64_t)g.Hkv * D;
-  const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
-  const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
-  const int n_keys = (r_first >= rl || (resp && !g.resp_keys)) ? 0 : (int)(key1 - key0);
-  const int n_stages = (n_keys + C::BN - 1) / C::BN;
-  const int64_t sb = stride * 2;
-  const uint16_t* kc = kb + key0 * stride;
-  const uint16_t* vc = vb + key0 * stride;
-  DirectLoad<D, C::BN, C::WAVES> dl;
-  dl.init(sb);
-  if (n_stages > 0) {
-    dl.issue(buf0, kc, 0, n_keys, sb);
-    dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
-  }
-  Frag<D> fr;
-  fr.init();
-
-  const int m = w.m0 + wave * 32 + col;
-  const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
-  const bool valid = m < m_hi && r < rl;
-  const int lim = resp ? min(r, n_keys - 1) : n_keys - 1;
-  const int64_t row = ((int64_t)w.k * g.R + r) * g.Hq + h;
-  const int64_t orow = m < m_hi ? ((int64_t)w.part * g.K * g.R * g.Hq + row) : -1;
-  const float lse2 = valid ? lse[row] * kLog2e : INFINITY;
-  const float dvv = valid ? Dvec[row] : 0.0f;
-  f32x16 dinit;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dinit[i] = -dvv;
-  bf16x8 qf[KS], of[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(q + row * D + ks * 16 + hl * 8)
-                             : make_uint4(0, 0, 0, 0));
-    of[ks] = as_bf16x8(valid ? *reinterpret_cast<const uint4*>(d_o + row * D + ks * 16 + hl * 8)
-                             : make_uint4(0, 0, 0, 0));
-  }
-  int wmin = lim, wmax = lim;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    wmin = min(wmin, __shfl_xor(wmin, off, 64));
-    wmax = max(wmax, __shfl_xor(wmax, off, 64));
-  }
-
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
-
-  auto stage = [&](const char* cur, char* nxt, int it) {
-    wait_vmcnt0();
-    __syncthreads();
-    if (it + 1 < n_stages) {
-      const int64_t nk0 = (int64_t)(it + 1) * C::BN;
-      dl.issue(nxt, kc, nk0, n_keys, sb);
-      dl.issue(nxt + C::TILE, vc, nk0, n_keys, sb);
-    }
-    const char* Kt = cur;
-    const char* Vt = cur + C::TILE;
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int rel = it * C::BN + sub * 32;
-      if (rel > wmax) break;
-      if (rel + 31 > wmin)
-        dq_subtile<true, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dinit, qf, of, acc);
-      else
-        dq_subtile<false, D>(fr, Kt, Vt, sub, rel, lim, g.c2, lse2, dinit, qf, of, acc);
-    }
-  };
-  for (int it = 0; it < n_stages; it += 2) {
-    stage(buf0, buf1, it);
-    if (it + 1 < n_stages) stage(buf1, buf0, it + 1);
-  }
-
-  if (orow < 0) return;
-  const float sc = valid ? g.tau : 0.0f;
-  float* dst = dq_part + orow * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = dt * 32 + i4 * 8 + hl * 4;
-      *reinterpret_cast<float4*>(dst + d0) =
-          make_float4(acc[dt][4 * i4 + 0] * sc, acc[dt][4 * i4 + 1] * sc, acc[dt][4 * i4 + 2] * sc,
-                      acc[dt][4 * i4 + 3] * sc);
-    }
-}
 
 // ---- response dK / dV --------------------------------------------------------------------
 
@@ -446,26 +258,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
       *reinterpret_cast<float4*>(dkp + d0) = a;
       *reinterpret_cast<float4*>(dvp + d0) = b;
     }
-}
-
-hipError_t launch_dq_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
-
-hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
-#ifndef RR_DQ_OLD
-  return launch_dq_ring_bf16(g, a, s);
-#endif
-  const int64_t n = tile_work_count(g, DqCfg<128>::BM);
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)xcd_grid(n)), block(64 * DqCfg<128>::WAVES);
-  const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
-  const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r, *dO = (const uint16_t*)a.d_o;
-  if (g.dqk == 64)
-    hipLaunchKernelGGL(dq_partials_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec,
-                       a.dq_part);
-  else
-    hipLaunchKernelGGL(dq_partials_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec,
-                       a.dq_part);
-  return hipGetLastError();
 }
 
 hipError_t launch_dkdv_bf16(const Geom& g, const AttnPtrs& a, int key_hi, hipStream_t s) {

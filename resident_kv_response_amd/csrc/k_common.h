@@ -57,16 +57,6 @@ __device__ __forceinline__ void prio_valu() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier(mask, count, sync_id): a
-// sequence of such calls at the end of a basic block asks the scheduler to order the
-// block's instructions in that pattern (e.g. one MFMA, then a few vector ops, repeated),
-// so that a wave keeps issuing vector work while its matrix-core operations run.
-#define RR_SG_MFMA 0x008
-#define RR_SG_VALU 0x002
-#define RR_SG_TRANS 0x400
-#define RR_SG_DS_READ 0x100
-#define RR_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-
 // 16-byte vector <-> 8 bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -75,9 +65,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Value held by lane (lane ^ 32) of the wave.
-__device__ __forceinline__ float partner32(float x) { return __shfl_xor(x, 32, 64); }
 
 // Workgroup -> work-item map that keeps consecutive work items on one XCD.  Workgroups
 // are dispatched round-robin over the 8 XCDs (blockIdx % 8), each XCD with its own L2;

@@ -16,9 +16,10 @@
 //
 // K/V stream: 64-key stages in a ring of four LDS buffers (K tiles and V tiles as
 // separate arrays), loaded straight from global memory two stages ahead; one barrier per
-// stage.  Pipeline: block B(u) first issues dQ^T += K^T dS^T of subtile u-1 on the
-// matrix cores while the vector ALUs turn S(u), dP(u) into dS(u), then the S and dP MFMAs
-// of subtile u+1 (which reuse the registers of S(u), dP(u)).  The block is laid out by
+// stage.  Pipeline: block B(u) issues dQ^T += K^T dS^T of subtile u-1, then the S and dP
+// MFMAs of subtile u+1 (which reuse the registers of S(u), dP(u)), while the vector ALUs
+// turn S(u), dP(u) into dS(u): exponentials during the dQ MFMAs, products and packing
+// during the S MFMAs.  The block is laid out by
 // hand in slots (the LDS reads of a fragment two slots ahead of its MFMA), separated by
 // scheduling barriers, and the block sequence runs across stage boundaries.  Subtiles
 // visible to every row of the workgroup run this pipeline; those near the causal
@@ -70,18 +71,12 @@ __device__ __forceinline__ void dqr_dq(const Frag<D>& fr, const char* Kt, int su
     for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(fr.trans_frag(Kt, sub, h2, dt), dsf[h2], acc[dt]);
 }
 
-// dS = p (dP - D), p = 2^(S c2 - lse2), for elements 2k and 2k+1, packed to bf16.
-__device__ __forceinline__ uint32_t dqr_pair(const f32x16& s, const f32x16& dp, int k, float c2, float lse2) {
-  const float p0 = fast_exp2(fmaf(s[2 * k], c2, -lse2));
-  const float p1 = fast_exp2(fmaf(s[2 * k + 1], c2, -lse2));
-  return pack_bf16x2(p0 * dp[2 * k], p1 * dp[2 * k + 1]);
-}
-
 // One pipelined block, laid out by hand in slots separated by scheduling barriers.
-// With PREV, slots 0..D/16-1 hold the dQ MFMAs of subtile u-1 (K^T fragments) and carry
-// the vector work that turns S(u), dP(u) into dS(u), one element pair per slot; the
-// following 2*D/16 slots alternate the S and dP MFMAs of subtile u+1.  Every slot first
-// issues the LDS reads of the fragment two slots ahead.
+// With PREV the slots are: D/16 dQ MFMAs of subtile u-1 (K^T fragments), carrying the
+// exponentials p = 2^(S c2 - lse2) of subtile u (each p replaces its S value); D/16 S
+// MFMAs of subtile u+1, carrying dS = p (dP - D) and the bf16 packing (dP(u) is still
+// live there); D/16 dP MFMAs of subtile u+1.  Every slot first issues the LDS reads of
+// the fragment two slots ahead.
 template <int D, bool PREV>
 __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags<D>& far, const char* Kx,
                                                int subx, const char* Ky, const char* Vy, int suby,
@@ -95,13 +90,14 @@ __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags
   auto load = [&](int i) -> bf16x8 {
     if (i < NX) return fr.trans_frag(Kx, subx, i & 1, i >> 1);
     const int j = i - NX;
-    return (j & 1) ? far.row(Vy, suby, j >> 1) : fr.row(Ky, suby, j >> 1);
+    return j < KS ? fr.row(Ky, suby, j) : far.row(Vy, suby, j - KS);
   };
+  float p[16];
   uint32_t w[8];
   if (!PREV) {
-    // first block: no dQ MFMAs to overlap, so the vector work runs up front
+    // first block: no dQ MFMAs to overlap, so the exponentials run up front
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = dqr_pair(s, dp, k, c2, lse2);
+    for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(s[e], c2, -lse2));
     __builtin_amdgcn_sched_barrier(0);
   }
   bf16x8 frag[NSLOT];
@@ -112,22 +108,29 @@ __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags
     if (i + 2 < NSLOT) frag[i + 2] = load(i + 2);
     if (i < NX) {
       acc[i >> 1] = mfma32x32x16(frag[i], dsp[i & 1], acc[i >> 1]);
-      // vector work of subtile u: element pairs spread over the dQ slots
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e * NX) / 16 == i) {
+          p[e] = fast_exp2(fmaf(s[e], c2, -lse2));
+          asm volatile("" ::"v"(p[e]));   // keeps the exponential in this slot
+        }
+    } else if (i < NX + KS) {
+      const int ks = i - NX;
+      if (ks == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+      }
+      s = mfma32x32x16(frag[i], qf[ks], s);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if ((k * NX) / 8 == i) {
-          w[k] = dqr_pair(s, dp, k, c2, lse2);
+        if ((k * KS) / 8 == ks) {
+          w[k] = pack_bf16x2(p[2 * k] * dp[2 * k], p[2 * k + 1] * dp[2 * k + 1]);
           asm volatile("" ::"v"(w[k]));   // keeps the pair in this slot
         }
     } else {
-      const int j = i - NX, ks = j >> 1;
-      if (j == 0) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
-        dp = dinit;
-      }
-      if (j & 1) dp = mfma32x32x16(frag[i], of[ks], dp);
-      else s = mfma32x32x16(frag[i], qf[ks], s);
+      const int ks = i - NX - KS;
+      if (ks == 0) dp = dinit;
+      dp = mfma32x32x16(frag[i], of[ks], dp);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -138,7 +141,7 @@ __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void dq_ring_bf16(
+__global__ __launch_bounds__(512, 1) void dq_partials_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
     const uint16_t* __restrict__ v_r, const uint16_t* __restrict__ d_o,
@@ -362,16 +365,16 @@ __global__ __launch_bounds__(512, 1) void dq_ring_bf16(
     }
 }
 
-hipError_t launch_dq_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
+hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
   const int64_t n = tile_work_count(g, DqRingCfg<128>::BM);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)xcd_grid(n)), block(64 * DqRingCfg<128>::WAVES);
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r, *dO = (const uint16_t*)a.d_o;
   if (g.dqk == 64)
-    hipLaunchKernelGGL(dq_ring_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec, a.dq_part);
+    hipLaunchKernelGGL(dq_partials_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec, a.dq_part);
   else
-    hipLaunchKernelGGL(dq_ring_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec, a.dq_part);
+    hipLaunchKernelGGL(dq_partials_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, dO, a.lse, a.Dvec, a.dq_part);
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// bf16 forward partials on MFMA (gfx950).
+// bf16 forward partials on MFMA (gfx950), continuous software pipeline over a ring of
+// K/V stages.
 //
 // One workgroup = one (response k, KV head g, part, 256-row tile).  A part is one prompt
 // chunk [c*chunk, (c+1)*chunk) or the response's own causal keys; each part keeps its own
@@ -7,172 +8,106 @@
 // longstraw-2m-rl, section "Two incompatible architectures, same transaction").
 //
 // Rows: flattened m = r * grp + hh over the grp query heads that read KV head g, so one
-// K/V tile feeds all of them.  8 waves x 32 rows (two waves per SIMD); each wave keeps
-// its Q fragments and its O^T accumulators (d x rows, fp32) in registers for the whole
-// part.
+// K/V tile feeds all of them.  A wave owns NT 32-row tiles: 8 waves x 32 rows (two waves
+// per SIMD, NT = 1) or 4 waves x 64 rows (one wave per SIMD, NT = 2, where every K or V
+// fragment read from LDS feeds two MFMAs).  Each wave keeps its Q fragments and its O^T
+// accumulators (d x rows, fp32) in registers for the whole part.
 //
-// K/V stream: 128-key stages loaded straight from global memory into LDS (no register
-// staging), two buffers, the next stage's loads in flight while the current one is used.
-// Per 32-key subtile and 32-row N-tile: S^T = K Q^T (D/16 MFMAs, K row fragments),
-// base-2 online softmax with a lazy rescale (the reference maximum only moves when a
-// row's maximum grows by more than 2^8, so every p <= 256), P^T rounded to bf16 straight
-// from the C registers (the running sum l adds up those rounded values, so the
-// normaliser is the sum of exactly the weights the PV product uses), O^T += V^T P^T
-// (D/16 MFMAs, V^T fragments by transposing LDS reads).
+// K/V stream: 64-key stages in a ring of four LDS buffers, loaded straight from global
+// memory into LDS two stages ahead; one barrier per stage.  The K and V tiles of the
+// four stages are separate arrays and every read names its buffer at compile time, so the
+// compiler can tell a read of one buffer from the direct loads still landing in another.
 //
-// Stages whose keys are visible to every row of the wave run a software pipeline: the
-// S^T MFMAs of subtile j+1 and the PV MFMAs of subtile j-1 are issued between short runs
-// of the softmax of subtile j, so the matrix cores and the vector ALUs work at the same
-// time.  Stages near the causal diagonal or a chunk end take the masked path.
+// Pipeline over 32-key subtiles u, per wave: block B(u) issues O^T += V^T P^T of subtile
+// u-1 and S^T = K Q^T of subtile u+1 on the matrix cores (MFMAs with no dependence on the
+// block's vector work) while the vector ALUs run the online softmax of subtile u (base 2,
+// lazy rescale: the reference maximum only moves when a row's maximum grows by more than
+// 2^8, so every p <= 256; P^T rounded to bf16 straight from the C registers, and the
+// running sum l adds up exactly those rounded values).  The block is laid out by hand in
+// slots (one fragment read two slots ahead, its MFMAs, a fixed share of the softmax),
+// separated by scheduling barriers.  A rescale of the accumulators is applied at the end
+// of the block, between PV(u-1) and PV(u).  The block sequence runs across stage
+// boundaries, so every block carries the same balanced load.  Subtiles whose keys are
+// visible to every row of the workgroup run this pipeline; the few near the causal
+// diagonal or a chunk end run a masked, unpipelined path afterwards.
+#include <type_traits>
+
 #include "k_attn_tile.h"
 #include "k_lds.h"
+#include "k_ring.h"
 #include "kernels.h"
 
 namespace rr {
 
-constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest p between rescales
+namespace {
 
-#ifndef RR_FWD_WAVES
-#define RR_FWD_WAVES 8
-#endif
-#ifndef RR_FWD_NT
-#define RR_FWD_NT 1
-#endif
+constexpr float kRingRescaleLog2 = 8.0f;   // log2 of the largest p between rescales
 
-template <int D>
-struct FwdCfg {
-  static constexpr int WAVES = RR_FWD_WAVES;
-  static constexpr int NT = RR_FWD_NT;           // 32-row N-tiles per wave
-  static constexpr int ROWS_W = 32 * NT;
-  static constexpr int BM = WAVES * ROWS_W;      // query rows per workgroup
-  static constexpr int BN = 128;                 // keys per LDS stage
-  static constexpr int NSUB = BN / 32;
+template <int D, int NT>
+struct RingCfg {
+  static constexpr int WAVES = 8 / NT;
+  static constexpr int BM = WAVES * 32 * NT;            // query rows per workgroup
+  static constexpr int BN = 64;                         // keys per stage
   static constexpr int KS = D / 16, DT = D / 32;
-  static constexpr int TILE = BN * D * 2;        // bytes of one [BN][D] bf16 tile
+  static constexpr int TILE = BN * D * 2;               // bytes of one [BN][D] bf16 tile
+  static constexpr int LOADS = 2 * (BN * D / 8) / (64 * WAVES);   // direct loads per wave per stage
 };
 
 template <int D, int NT>
-__device__ __forceinline__ void scores_T(const Frag<D>& fr, const char* Kt, int sub,
-                                         const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
-  constexpr int KS = D / 16;
-  bf16x8 kf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kf[ks] = fr.row(Kt, sub, ks);
+__device__ __forceinline__ void ring_scores(const Frag<D>& fr, const char* Kt, int sub,
+                                            const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
-  prio_mfma();
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 kf = fr.row(Kt, sub, ks);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf[ks], qf[t][ks], s[t]);
-  prio_valu();
-}
-
-template <bool MASK, int D, int NT>
-__device__ __forceinline__ void online_softmax(f32x16 (&s)[NT], const int (&lim)[NT], int rel,
-                                               float c2, float (&m_run)[NT], float (&l_run)[NT],
-                                               f32x16 (&acc)[NT][D / 32], bf16x8 (&pf)[NT][2]) {
-  constexpr int DT = D / 32;
-  const int hl = (threadIdx.x & 63) >> 5;
-  float m_new[NT];
-  bool grow = false;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (MASK) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
-        if (key > lim[t]) s[t][i] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[t][i]), s[t][i + 1]);
-    mx = fmaxf(mx, s[t][15]);
-    mx = pair_max(mx);
-    m_new[t] = fmaxf(m_run[t], mx * c2);
-    grow |= m_new[t] > m_run[t] + kRescaleThreshold;
-  }
-  if (__any(grow)) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float alpha = fast_exp2(m_run[t] - m_new[t]);
-      l_run[t] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][dt][i] *= alpha;
-      m_run[t] = m_new[t];
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[t][i], c2, -m_run[t]));
-    float ls = 0.0f;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      uint4 u;
-      u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
-      u.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
-      u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
-      u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
-      pf[t][h2] = as_bf16x8(u);
-      ls = sum_bf16x8(u, ls);
-    }
-    l_run[t] += ls;
+    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf, qf[t][ks], s[t]);
   }
 }
 
 template <int D, int NT>
-__device__ __forceinline__ void pv_accumulate(const Frag<D>& fr, const char* Vt, int sub,
-                                              const bf16x8 (&pf)[NT][2], f32x16 (&acc)[NT][D / 32]) {
-  constexpr int DT = D / 32;
-  bf16x8 vf[DT][2];
+__device__ __forceinline__ void ring_pv(const FarFrags<D>& vo, const char* Vt, int sub,
+                                        const bf16x8 (&pf)[NT][2], f32x16 (&acc)[NT][D / 32]) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = fr.trans_frag(Vt, sub, h2, dt);
-  prio_mfma();
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 vf = vo.trans_frag(Vt, sub, h2, dt);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf[dt][h2], pf[t][h2], acc[t][dt]);
-  prio_valu();
+      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf, pf[t][h2], acc[t][dt]);
+    }
 }
 
-// Softmax of one unmasked 32-key subtile (one 32-row N-tile): P^T as bf16 MFMA operands
-// in pf, and alpha, the factor the accumulators must be scaled by when the reference
-// maximum moved (returned wave-uniform flag; alpha = 1 otherwise).  Branch-free, so it
-// can share a basic block with the MFMAs it is scheduled against.
-__device__ __forceinline__ bool softmax_plain(const f32x16& s, float c2, float& m_run, float& l_run,
-                                              float& alpha, bf16x8 (&pf)[2]) {
+// Online softmax of one 32-key subtile of one tile (lane = query row, 16 of the subtile's
+// keys per lane), unpipelined form for the masked path.  Returns the wave-uniform
+// "reference maximum moved" flag; alpha is the factor the accumulators must then be
+// scaled by (1 on rows whose maximum did not move).
+__device__ __forceinline__ bool ring_softmax(const f32x16& s, float c2, float& m_run, float& l_run,
+                                             float& alpha, bf16x8 (&pf)[2]) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
   for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
   mx = fmaxf(mx, s[15]);
   mx = pair_max(mx);
   const float m_new = fmaxf(m_run, mx * c2);
-  const bool grow = __any(m_new > m_run + kRescaleThreshold);
+  const bool grow = __any(m_new > m_run + kRingRescaleLog2);
   const float m_use = grow ? m_new : m_run;
   alpha = fast_exp2(m_run - m_use);
   m_run = m_use;
-  float p[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], c2, -m_use));
   float ls = 0.0f;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[8 * h2 + i], c2, -m_use));
     uint4 u;
-    u.x = pack_bf16x2(p[8 * h2 + 0], p[8 * h2 + 1]);
-    u.y = pack_bf16x2(p[8 * h2 + 2], p[8 * h2 + 3]);
-    u.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
-    u.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
+    u.x = pack_bf16x2(p[0], p[1]);
+    u.y = pack_bf16x2(p[2], p[3]);
+    u.z = pack_bf16x2(p[4], p[5]);
+    u.w = pack_bf16x2(p[6], p[7]);
     pf[h2] = as_bf16x8(u);
     ls = sum_bf16x8(u, ls);
   }
@@ -181,114 +116,132 @@ __device__ __forceinline__ bool softmax_plain(const f32x16& s, float c2, float& 
 }
 
 template <int D>
-__device__ __forceinline__ void scale_acc(f32x16 (&acc)[D / 32], float alpha) {
+__device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
 }
 
-// S^T of subtile `sub` for the wave's NT N-tiles: each K row fragment is read once and
-// feeds NT MFMAs.
-template <int D, int NT>
-__device__ __forceinline__ void mma_scores(const Frag<D>& fr, const char* Kt, int sub,
-                                           const bf16x8 (&qf)[NT][D / 16], f32x16 (&s)[NT]) {
-  bf16x8 kf[D / 16];
+// One pipelined block, laid out by hand as NSLOT slots separated by scheduling
+// barriers.  Slot i issues the LDS reads of slot i+2's fragment (so every read has two
+// slots' time to land), then the NT MFMAs of its own fragment, then a fixed share of the
+// softmax of subtile u for every tile: the row maximum over the first slots, then the
+// reference-maximum update, then the exponentials in pairs (each pair packed to bf16 and
+// added to the running sum at once), spread over the remaining slots.  With PV, even
+// slots hold the K fragments of subtile u+1's scores and odd slots the V^T fragments of
+// subtile u-1's PV.  Sets, per tile, the wave-uniform flag "the reference maximum moved"
+// (the caller then scales that tile's accumulators by alpha).
+template <int D, int NT, bool HAS_PV>
+__device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrags<D>& vo, const char* Kt,
+                                                int subk, const char* Vt, int subv,
+                                                const bf16x8 (&qf)[NT][D / 16], const f32x16 (&s)[NT],
+                                                const bf16x8 (&pp)[NT][2], f32x16 (&acc)[NT][D / 32],
+                                                float c2, float (&m_run)[NT], float (&l_run)[NT],
+                                                float (&alpha)[NT], bool (&grow)[NT], f32x16 (&sn)[NT],
+                                                bf16x8 (&pn)[NT][2]) {
+  constexpr int KS = D / 16;
+  constexpr int NSLOT = (HAS_PV ? 2 : 1) * KS;
+  constexpr int MAXS = NSLOT >= 8 ? 2 : 1;          // slots of the max tree
+  constexpr int FIN = MAXS;                          // slot of the reference-maximum update
+  constexpr int E = NSLOT - FIN - 1;                 // slots of the exponentials
+  auto load = [&](int i) -> bf16x8 {
+    if (HAS_PV && (i & 1)) {
+      const int j = i >> 1;
+      return vo.trans_frag(Vt, subv, j & 1, j >> 1);
+    }
+    return fr.row(Kt, subk, HAS_PV ? (i >> 1) : i);
+  };
+  bf16x8 frag[NSLOT];
+  frag[0] = load(0);
+  frag[1] = load(1);
+  float mx[NT], m_use[NT], ls[NT];
+  uint32_t w[NT][8];
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = fr.row(Kt, sub, ks);
+  for (int i = 0; i < NSLOT; ++i) {
+    if (i + 2 < NSLOT) frag[i + 2] = load(i + 2);
+    if (HAS_PV && (i & 1)) {
+      const int j = i >> 1;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t) acc[t][j >> 1] = mfma32x32x16(frag[i], pp[t][j & 1], acc[t][j >> 1]);
+    } else {
+      const int ks = HAS_PV ? (i >> 1) : i;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+      for (int t = 0; t < NT; ++t) {
+        if (ks == 0) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
+          for (int e = 0; e < 16; ++e) sn[t][e] = 0.0f;
+        }
+        sn[t] = mfma32x32x16(frag[i], qf[t][ks], sn[t]);
+      }
+    }
+    // this slot's share of the softmax, for every tile
 #pragma unroll
-    for (int t = 0; t < NT; ++t) s[t] = mfma32x32x16(kf[ks], qf[t][ks], s[t]);
-}
-
-// O^T += V^T P^T of subtile `sub` for the wave's NT N-tiles (each V^T fragment feeds NT
-// MFMAs).
-template <int D, int NT>
-__device__ __forceinline__ void mma_pv(const Frag<D>& fr, const char* Vt, int sub, const bf16x8 (&pf)[NT][2],
-                                       f32x16 (&acc)[NT][D / 32]) {
-  bf16x8 vf[D / 32][2];
+    for (int t = 0; t < NT; ++t) {
+      const f32x16& st = s[t];
+      if (i == 0) {
+        mx[t] = fmaxf(fmaxf(st[0], st[1]), st[2]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[3]), st[4]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[5]), st[6]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[7]), st[8]);
+      }
+      if (i == MAXS - 1) {
+        mx[t] = fmaxf(fmaxf(mx[t], st[9]), st[10]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[11]), st[12]);
+        mx[t] = fmaxf(fmaxf(mx[t], st[13]), st[14]);
+        mx[t] = fmaxf(mx[t], st[15]);
+      }
+      if (i == FIN) {
+        mx[t] = pair_max(mx[t]);
+        const float m_new = fmaxf(m_run[t], mx[t] * c2);
+        grow[t] = __any(m_new > m_run[t] + kRingRescaleLog2);
+        m_use[t] = grow[t] ? m_new : m_run[t];
+        alpha[t] = fast_exp2(m_run[t] - m_use[t]);
+        m_run[t] = m_use[t];
+        ls[t] = 0.0f;
+      }
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+      for (int k = 0; k < 8; ++k) {
+        if (i == FIN + 1 + (k * E) / 8) {
+          const float p0 = fast_exp2(fmaf(st[2 * k], c2, -m_use[t]));
+          const float p1 = fast_exp2(fmaf(st[2 * k + 1], c2, -m_use[t]));
+          w[t][k] = pack_bf16x2(p0, p1);
+          ls[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[t][k]), one, ls[t], false);
+        }
+      }
+      if (i == NSLOT - 1) l_run[t] = fmaf(l_run[t], alpha[t], ls[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) vf[dt][h2] = fr.trans_frag(Vt, sub, h2, dt);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][dt] = mfma32x32x16(vf[dt][h2], pf[t][h2], acc[t][dt]);
-}
-
-// Softmax of the NT tiles of one subtile; true when any reference maximum moved (the
-// accumulators of tile t must then be scaled by alpha[t], which is 1 for tiles that did
-// not move).
-template <int NT>
-__device__ __forceinline__ bool softmax_tiles(const f32x16 (&s)[NT], float c2, float (&m_run)[NT],
-                                              float (&l_run)[NT], float (&alpha)[NT], bf16x8 (&pf)[NT][2]) {
-  bool grow = false;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) grow |= softmax_plain(s[t], c2, m_run[t], l_run[t], alpha[t], pf[t]);
-  return grow;
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void scale_tiles(f32x16 (&acc)[NT][D / 32], const float (&alpha)[NT]) {
-#pragma unroll
-  for (int t = 0; t < NT; ++t) scale_acc<D>(acc[t], alpha[t]);
-}
-
-// Schedules of the pipelined stage's basic blocks: (D/16) K-fragment reads and D/16 * NT
-// MFMAs per S^T, (D/8) V^T reads and D/16 * NT MFMAs per PV.  Operand reads run a few
-// MFMAs ahead of their use (not all up front, which would hold every fragment in
-// registers at once), and each MFMA is followed by a share of the softmax's vector work.
-template <int D, int NT>
-__device__ __forceinline__ void sched_s_softmax() {      // S(j+1) with softmax(j)
-  constexpr int NM = D / 16 * NT;
-  RR_SCHED_GROUP(RR_SG_DS_READ, 4);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    RR_SCHED_GROUP(RR_SG_MFMA, 1);
-    if (i % NT == NT - 1 && i / NT < D / 16 - 4) RR_SCHED_GROUP(RR_SG_DS_READ, 1);
-    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 9 : 7);
+  for (int t = 0; t < NT; ++t) {
+    pn[t][0] = as_bf16x8(make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]));
+    pn[t][1] = as_bf16x8(make_uint4(w[t][4], w[t][5], w[t][6], w[t][7]));
   }
 }
-template <int D, int NT>
-__device__ __forceinline__ void sched_s_pv_softmax() {   // S(j+1) and PV(j-1) with softmax(j)
-  constexpr int NM = D / 8 * NT, READS = D / 16 - 4 + D / 8, PER = NT == 1 ? 2 : 1;
-  RR_SCHED_GROUP(RR_SG_DS_READ, 4);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    RR_SCHED_GROUP(RR_SG_MFMA, 1);
-    if (i < READS / PER) RR_SCHED_GROUP(RR_SG_DS_READ, PER);
-    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 5 : 4);
-  }
-}
-template <int D, int NT>
-__device__ __forceinline__ void sched_pv_softmax() {     // PV(j-1) with softmax(j)
-  constexpr int NM = D / 16 * NT, READS = D / 8 - 6, PER = NT == 1 ? 2 : 1;
-  RR_SCHED_GROUP(RR_SG_DS_READ, 6);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    RR_SCHED_GROUP(RR_SG_MFMA, 1);
-    if (i < READS / PER) RR_SCHED_GROUP(RR_SG_DS_READ, PER);
-    RR_SCHED_GROUP(RR_SG_VALU, NT == 1 ? 9 : 8);
-  }
-}
 
-template <int D>
-__global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
+}  // namespace
+
+template <int D, int NT>
+__global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
     Geom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ k_r,
     const uint16_t* __restrict__ v_r, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  using C = FwdCfg<D>;
-  constexpr int NT = C::NT, KS = C::KS, DT = C::DT;
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * C::TILE];   // K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * C::TILE];
+  using C = RingCfg<D, NT>;
+  constexpr int KS = C::KS, DT = C::DT;
+  // K tiles of the four stages first, then the V tiles: the K tiles then sit within the
+  // 16-bit immediate offset of one base address, the V tiles within that of another.
+  __shared__ __attribute__((aligned(1024))) char kt0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kt3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt3[C::TILE];
+  char* const KT[4] = {kt0, kt1, kt2, kt3};
+  char* const VT[4] = {vt0, vt1, vt2, vt3};
 
   const TileWork w = decode_tile_work(g, C::BM);
   if (!w.ok) return;
@@ -312,27 +265,57 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
   const uint16_t* kb = resp ? k_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : k_p + (int64_t)w.g * D;
   const uint16_t* vb = resp ? v_r + ((int64_t)w.k * g.R * g.Hkv + w.g) * D : v_p + (int64_t)w.g * D;
   const int n_keys = (r_first >= rl || (resp && !g.resp_keys)) ? 0 : (int)(key1 - key0);
+  // Workgroup-uniform subtile counts: [0, n_full) is visible to every row of the
+  // workgroup (its first row sees the fewest response keys), [n_full, n_sub) is masked.
+  const int lim_min = resp ? min(r_first, n_keys - 1) : n_keys - 1;
+  const int n_full = n_keys > 0 ? (lim_min + 1) / 32 : 0;
+  const int n_sub = (n_keys + 31) / 32;
   const int n_stages = (n_keys + C::BN - 1) / C::BN;
 
-  const int64_t sb = stride * 2;                  // bytes between consecutive keys
-  const uint16_t* kc = kb + key0 * stride;          // part-relative streams
+  const int64_t sbytes = stride * 2;
+  const uint16_t* kc = kb + key0 * stride;
   const uint16_t* vc = vb + key0 * stride;
-  DirectLoad<D, C::BN, C::WAVES> dl;
-  dl.init(sb);
+  DirectLoadRows<D, C::BN, C::WAVES> dl;
+  dl.init();
   Frag<D> fr;
   fr.init();
-  if (n_stages > 0) {
-    dl.issue(buf0, kc, 0, n_keys, sb);
-    dl.issue(buf0 + C::TILE, vc, 0, n_keys, sb);
-  }
+  FarFrags<D> vo;
+  vo.template init<false, true>(fr);
+
+  auto issue_stage = [&](int b, int s) {
+    const int64_t off = (int64_t)s * C::BN * sbytes;
+    const int rows = n_keys - s * C::BN;
+    dl.issue(KT[b], reinterpret_cast<const char*>(kc) + off, rows, (uint32_t)sbytes);
+    dl.issue(VT[b], reinterpret_cast<const char*>(vc) + off, rows, (uint32_t)sbytes);
+  };
+  auto issue_any = [&](int s) {
+    switch (s & 3) {
+      case 0: issue_stage(0, s); break;
+      case 1: issue_stage(1, s); break;
+      case 2: issue_stage(2, s); break;
+      default: issue_stage(3, s); break;
+    }
+  };
+  // Entering stage s: its loads are done (only stage s+1's may still be in flight), every
+  // wave is past its reads of stage s-2's buffer, and stage s+2 is loaded into it.
+  int entered = -1;
+  auto enter_stage = [&](int s) {
+    if (s + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+    __syncthreads();
+    if (s + 2 < n_stages) issue_any(s + 2);
+    entered = s;
+  };
+  if (n_stages > 0) issue_any(0);
+  if (n_stages > 1) issue_any(1);
 
   int lim[NT];
   bool valid[NT];
   int64_t orow[NT];
   bf16x8 qf[NT][KS];
+  int wmax = -1;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int m = w.m0 + wave * C::ROWS_W + t * 32 + col;
+    const int m = w.m0 + (wave * NT + t) * 32 + col;
     const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
     valid[t] = m < m_hi && r < rl;
     lim[t] = resp ? min(r, n_keys - 1) : n_keys - 1;
@@ -342,13 +325,10 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
     for (int ks = 0; ks < KS; ++ks)
       qf[t][ks] = as_bf16x8(valid[t] ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hl * 8)
                                      : make_uint4(0, 0, 0, 0));
+    wmax = max(wmax, lim[t]);
   }
-  int wmin = min(lim[0], lim[NT - 1]), wmax = max(lim[0], lim[NT - 1]);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    wmin = min(wmin, __shfl_xor(wmin, off, 64));
-    wmax = max(wmax, __shfl_xor(wmax, off, 64));
-  }
+  for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, 64));
 
   f32x16 acc[NT][DT];
   float m_run[NT], l_run[NT];
@@ -361,72 +341,107 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][dt][i] = 0.0f;
   }
+  const float c2 = g.c2;
 
-  // one stage: wait for its loads, prefetch the next stage into the other buffer, then
-  // four 32-key subtiles with the next subtile's scores issued ahead of the softmax
-  auto stage = [&](const char* cur, char* nxt, int it) {
-    wait_vmcnt0();
-    __syncthreads();
-    if (it + 1 < n_stages) {
-      const int64_t nk0 = (int64_t)(it + 1) * C::BN;
-      dl.issue(nxt, kc, nk0, n_keys, sb);
-      dl.issue(nxt + C::TILE, vc, nk0, n_keys, sb);
-    }
-    const char* Kt = cur;
-    const char* Vt = cur + C::TILE;
-    const int rel0 = it * C::BN;
-    if (rel0 > wmax) return;
-    if (C::NSUB == 4 && rel0 + C::BN - 1 <= wmin) {
-      // every key of the stage is visible to every row of the wave: software-pipelined
-      // subtiles, S(j+1) and PV(j-1) on the matrix cores while the softmax of j runs
-      f32x16 sa[NT], sb[NT];
-      bf16x8 pa[NT][2], pb[NT][2];
+  if (n_keys > 0) enter_stage(0);
+
+  if (n_full > 0) {
+    f32x16 s[NT];
+    ring_scores<D, NT>(fr, KT[0], 0, qf, s);    // S(0)
+    bf16x8 pp[NT][2];                           // P(u-1)
+
+    // Block B(u), u = J mod 8: PV(u-1) and S(u+1) on the matrix cores, softmax of u on the
+    // vector ALUs; compile-time buffers.  The last block also computes S(n_full), which is
+    // never used (the masked path recomputes it) and reads a buffer with no loads in flight.
+    auto block = [&](auto jc, auto pvc, int u) {
+      constexpr int J = decltype(jc)::value;
+      constexpr bool HAS_PV = decltype(pvc)::value;
+      constexpr int SX = ((J + 7) >> 1) & 3, SUBX = (J + 7) & 1;   // subtile u-1
+      constexpr int SY = ((J + 1) >> 1) & 3, SUBY = (J + 1) & 1;   // subtile u+1
+      constexpr int SN = (SY + 2) & 3;                              // stage u/2 + 3's buffer
+      if (J & 1) {   // subtile u+1 starts stage (u+1)/2
+        const int st = (u + 1) >> 1;
+        if (st + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+        __syncthreads();
+        if (st + 2 < n_stages) issue_stage(SN, st + 2);
+        entered = st;
+      }
+      bf16x8 pn[NT][2];
       float alpha[NT];
-      mma_scores<D, NT>(fr, Kt, 0, qf, sa);
-      mma_scores<D, NT>(fr, Kt, 1, qf, sb);
-      bool grow = softmax_tiles<NT>(sa, g.c2, m_run, l_run, alpha, pa);
-      sched_s_softmax<D, NT>();
-      if (grow) scale_tiles<D, NT>(acc, alpha);
-      mma_scores<D, NT>(fr, Kt, 2, qf, sa);
-      mma_pv<D, NT>(fr, Vt, 0, pa, acc);
-      grow = softmax_tiles<NT>(sb, g.c2, m_run, l_run, alpha, pb);
-      sched_s_pv_softmax<D, NT>();
-      if (grow) scale_tiles<D, NT>(acc, alpha);
-      mma_scores<D, NT>(fr, Kt, 3, qf, sb);
-      mma_pv<D, NT>(fr, Vt, 1, pb, acc);
-      grow = softmax_tiles<NT>(sa, g.c2, m_run, l_run, alpha, pa);
-      sched_s_pv_softmax<D, NT>();
-      if (grow) scale_tiles<D, NT>(acc, alpha);
-      mma_pv<D, NT>(fr, Vt, 2, pa, acc);
-      grow = softmax_tiles<NT>(sb, g.c2, m_run, l_run, alpha, pb);
-      sched_pv_softmax<D, NT>();
-      if (grow) scale_tiles<D, NT>(acc, alpha);
-      mma_pv<D, NT>(fr, Vt, 3, pb, acc);
-      return;
-    }
-    f32x16 s_cur[NT];
-    scores_T<D, NT>(fr, Kt, 0, qf, s_cur);
+      bool grow[NT];
+      f32x16 sn[NT];
+      ring_block_body<D, NT, HAS_PV>(fr, vo, KT[SY], SUBY, VT[SX], SUBX, qf, s, pp, acc, c2, m_run, l_run,
+                                     alpha, grow, sn, pn);
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int rel = rel0 + sub * 32;
-      const bool has_next = sub + 1 < C::NSUB && rel + 32 <= wmax;
-      f32x16 s_next[NT];
-      if (has_next) scores_T<D, NT>(fr, Kt, sub + 1, qf, s_next);
-      bf16x8 pf[NT][2];
-      if (rel + 31 > wmin)
-        online_softmax<true, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
-      else
-        online_softmax<false, D, NT>(s_cur, lim, rel, g.c2, m_run, l_run, acc, pf);
-      pv_accumulate<D, NT>(fr, Vt, sub, pf, acc);
-      if (!has_next) break;
+      for (int t = 0; t < NT; ++t) {
+        // the block's softmax results must be formed here, not sunk past the rescale branch
+        pin_operands(pn[t], l_run[t]);
+      }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s_cur[t] = s_next[t];
+      for (int t = 0; t < NT; ++t) {
+        if (grow[t]) ring_scale<D>(acc[t], alpha[t]);
+        pp[t][0] = pn[t][0];
+        pp[t][1] = pn[t][1];
+        s[t] = sn[t];
+      }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    block(std::integral_constant<int, 0>{}, F{}, 0);
+    int u = 1;
+    // straight-line groups of eight blocks (u = 8i+1 .. 8i+8), so that every block's
+    // buffers are compile-time and one block's softmax feeds the next block directly
+    for (; u + 8 <= n_full; u += 8) {
+      block(std::integral_constant<int, 1>{}, T{}, u);
+      block(std::integral_constant<int, 2>{}, T{}, u + 1);
+      block(std::integral_constant<int, 3>{}, T{}, u + 2);
+      block(std::integral_constant<int, 4>{}, T{}, u + 3);
+      block(std::integral_constant<int, 5>{}, T{}, u + 4);
+      block(std::integral_constant<int, 6>{}, T{}, u + 5);
+      block(std::integral_constant<int, 7>{}, T{}, u + 6);
+      block(std::integral_constant<int, 0>{}, T{}, u + 7);
     }
-  };
+    if (u < n_full) block(std::integral_constant<int, 1>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 2>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 3>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 4>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 5>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 6>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 7>{}, T{}, u++);
+    // PV of the last pipelined subtile
+    const int ul = n_full - 1;
+    switch ((ul >> 1) & 3) {
+      case 0: ring_pv<D, NT>(vo, VT[0], ul & 1, pp, acc); break;
+      case 1: ring_pv<D, NT>(vo, VT[1], ul & 1, pp, acc); break;
+      case 2: ring_pv<D, NT>(vo, VT[2], ul & 1, pp, acc); break;
+      default: ring_pv<D, NT>(vo, VT[3], ul & 1, pp, acc); break;
+    }
+  }
 
-  for (int it = 0; it < n_stages; it += 2) {
-    stage(buf0, buf1, it);
-    if (it + 1 < n_stages) stage(buf1, buf0, it + 1);
+  // Masked subtiles near the causal diagonal or a chunk end (keys past a row's limit
+  // are invisible to it).
+  for (int u = n_full; u < n_sub; ++u) {
+    const int st = u >> 1;
+    while (entered < st) enter_stage(entered + 1);
+    const int rel = u * 32;
+    if (rel > wmax) continue;
+    const int b = st & 3;
+    const char* const kt = b == 0 ? kt0 : b == 1 ? kt1 : b == 2 ? kt2 : kt3;
+    const char* const vt = b == 0 ? vt0 : b == 1 ? vt1 : b == 2 ? vt2 : vt3;
+    f32x16 s[NT];
+    ring_scores<D, NT>(fr, kt, u & 1, qf, s);
+    bf16x8 pf[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = rel + (i >> 2) * 8 + hl * 4 + (i & 3);
+        if (key > lim[t]) s[t][i] = -INFINITY;
+      }
+      float alpha;
+      if (ring_softmax(s[t], c2, m_run[t], l_run[t], alpha, pf[t])) ring_scale<D>(acc[t], alpha);
+    }
+    ring_pv<D, NT>(vo, vt, u & 1, pf, acc);
   }
 
 #pragma unroll
@@ -449,21 +464,25 @@ __global__ __launch_bounds__(64 * RR_FWD_WAVES, 1) void fwd_partials_bf16(
   }
 }
 
-hipError_t launch_fwd_ring_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
-
+// Launched with one 32-row tile per wave.  Two tiles per wave (64 rows, one wave per
+// SIMD) halve LDS reads per MFMA, but their accumulators, Q fragments and score tiles need
+// more registers than this compiler allocates without spilling.
 hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
-#ifndef RR_FWD_OLD
-  return launch_fwd_ring_bf16(g, a, s);
-#endif
-  const int64_t n = tile_work_count(g, FwdCfg<128>::BM);
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)xcd_grid(n)), block(64 * FwdCfg<128>::WAVES);
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r;
-  if (g.dqk == 64)
-    hipLaunchKernelGGL(fwd_partials_bf16<64>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
-  else
-    hipLaunchKernelGGL(fwd_partials_bf16<128>, grid, block, 0, s, g, q, kp, vp, kr, vr, a.part_o, a.part_lse);
+  if (g.dqk == 64) {
+    using C = RingCfg<64, 1>;
+    const int64_t n = tile_work_count(g, C::BM);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_partials_bf16<64, 1>), dim3((unsigned)xcd_grid(n)), dim3(64 * C::WAVES), 0, s, g, q,
+                       kp, vp, kr, vr, a.part_o, a.part_lse);
+  } else {
+    using C = RingCfg<128, 1>;
+    const int64_t n = tile_work_count(g, C::BM);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_partials_bf16<128, 1>), dim3((unsigned)xcd_grid(n)), dim3(64 * C::WAVES), 0, s, g, q,
+                       kp, vp, kr, vr, a.part_o, a.part_lse);
+  }
   return hipGetLastError();
 }
 
