@@ -285,8 +285,8 @@ __global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
   auto issue_stage = [&](int b, int s) {
     const int64_t off = (int64_t)s * C::BN * sbytes;
     const int rows = n_keys - s * C::BN;
-    dl.issue(KT[b], reinterpret_cast<const char*>(kc) + off, rows, (uint32_t)sbytes);
-    dl.issue(VT[b], reinterpret_cast<const char*>(vc) + off, rows, (uint32_t)sbytes);
+    dl.issue(lds_addr(KT[b]), reinterpret_cast<const char*>(kc) + off, rows, (uint32_t)sbytes);
+    dl.issue(lds_addr(VT[b]), reinterpret_cast<const char*>(vc) + off, rows, (uint32_t)sbytes);
   };
   auto issue_any = [&](int s) {
     switch (s & 3) {

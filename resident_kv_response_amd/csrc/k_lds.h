@@ -92,10 +92,19 @@ struct DirectLoad {
   }
 };
 
-// Lighter form of DirectLoad::issue: tile rows [0, N_ROWS) <- rows of a stream whose row 0
-// starts at the wave-uniform address `base`; rows at or past `rows_valid` (>= 1) re-read
-// row rows_valid - 1 (their values are masked by the caller).  Only the base is 64-bit;
-// lane offsets are 32-bit, so N_ROWS * stride_bytes must stay below 2^31.
+// Direct loads of a [N_ROWS][D] tile for the ring kernels: tile rows [0, N_ROWS) <- rows of
+// a stream whose row 0 starts at the wave-uniform address `base`; rows at or past
+// `rows_valid` (>= 1) re-read row rows_valid - 1 (their values are masked by the caller).
+// Only the base is 64-bit; lane offsets are 32-bit, so N_ROWS * stride_bytes must stay
+// below 2^31.  The destination is a LDS byte address (see lds_addr).
+//
+// The loads are issued from inline assembly (M0 = the wave's LDS destination, then
+// global_load_lds_dwordx4 with a scalar base and a 32-bit lane offset).  The compiler
+// then does not track them, and callers order them explicitly: s_waitcnt vmcnt before
+// the barrier that publishes a stage, and no load into a buffer that a wave may still
+// read.  (When the compiler does track them it treats every outstanding LDS read as
+// unordered and waits for all of them before each use, which defeats reading fragments
+// ahead.)
 template <int D, int N_ROWS, int WAVES>
 struct DirectLoadRows {
   using DL = DirectLoad<D, N_ROWS, WAVES>;
@@ -103,28 +112,42 @@ struct DirectLoadRows {
   uint32_t gran[4];     // swizzled granule byte offset, by instruction index mod 4
   int row0;             // first tile row of this wave
   int r_lane;           // row of this lane inside an instruction
+  uint32_t lds0;        // byte offset of this wave's first granule in the tile (uniform)
 
   __device__ __forceinline__ void init() {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     row0 = wave * PER_WAVE * RPI;
     r_lane = lane / G;
+    lds0 = (uint32_t)(row0 / RPI) * 64u * 16u;
 #pragma unroll
     for (int par = 0; par < 4; ++par) {
       const int r = row0 + RPI * par + r_lane;
       gran[par] = (uint32_t)(((lane % G) ^ Swz<D>::f(r)) << 4);
     }
   }
-  __device__ __forceinline__ void issue(char* tile, const char* base, int rows_valid,
+  __device__ __forceinline__ void issue(uint32_t tile_lds, const char* base, int rows_valid,
                                         uint32_t stride_bytes) const {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int p0 = (row0 / RPI + i) * 64;            // first granule of this instruction
       const int row = min(row0 + RPI * i + r_lane, rows_valid - 1);
       const uint32_t off = (uint32_t)row * stride_bytes + gran[i & 3];
-      __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(tile + p0 * 16), 16, 0, 0);
+      const uint32_t lds = tile_lds + lds0 + (uint32_t)i * 64u * 16u;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(lds), "v"(off), "s"(base)
+          : "memory", "m0");
     }
   }
 };
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 // Fragment reads from a swizzled [rows][D] tile.  Every read address is a per-lane
 // offset computed once (the swizzle depends only on the row mod 16, and the subtile and
