@@ -33,6 +33,10 @@
 
 namespace rr {
 
+#ifndef RR_AHEAD
+#define RR_AHEAD 2   // slots between a fragment's LDS read and its MFMA
+#endif
+
 namespace {
 
 template <int D>
@@ -101,11 +105,11 @@ __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags
     __builtin_amdgcn_sched_barrier(0);
   }
   bf16x8 frag[NSLOT];
-  frag[0] = load(0);
-  frag[1] = load(1);
+#pragma unroll
+  for (int i = 0; i < RR_AHEAD && i < NSLOT; ++i) frag[i] = load(i);
 #pragma unroll
   for (int i = 0; i < NSLOT; ++i) {
-    if (i + 2 < NSLOT) frag[i + 2] = load(i + 2);
+    if (i + RR_AHEAD < NSLOT) frag[i + RR_AHEAD] = load(i + RR_AHEAD);
     if (i < NX) {
       acc[i >> 1] = mfma32x32x16(frag[i], dsp[i & 1], acc[i >> 1]);
 #pragma unroll
@@ -350,6 +354,10 @@ __global__ __launch_bounds__(512, 1) void dq_partials_bf16(
     dsf[1] = as_bf16x8(make_uint4(wv[4], wv[5], wv[6], wv[7]));
     dqr_dq<D>(fr, kt, u & 1, dsf, acc);
   }
+  // The direct loads are not tracked by the compiler: none may still be writing LDS when
+  // the workgroup ends (every issued stage has been entered and waited for by now; this
+  // makes it unconditional).
+  wait_vmcnt0();
 
   if (orow < 0) return;
   const float sc = valid ? g.tau : 0.0f;

@@ -39,9 +39,16 @@
 
 namespace rr {
 
+#ifndef RR_AHEAD
+#define RR_AHEAD 2   // slots between a fragment's LDS read and its MFMA
+#endif
+
 namespace {
 
-constexpr float kRingRescaleLog2 = 8.0f;   // log2 of the largest p between rescales
+constexpr float kRingRescaleLog2 = 8.0f;   // masked path: log2 of the largest p between rescales
+// Pipelined path: largest partial row sum (16 bf16 p values of one lane) accepted against
+// the current reference maximum; it bounds every p the PV product consumes.
+constexpr float kRingSumLimit = 4096.0f;
 
 template <int D, int NT>
 struct RingCfg {
@@ -124,27 +131,23 @@ __device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
 }
 
 // One pipelined block, laid out by hand as NSLOT slots separated by scheduling
-// barriers.  Slot i issues the LDS reads of slot i+2's fragment (so every read has two
-// slots' time to land), then the NT MFMAs of its own fragment, then a fixed share of the
-// softmax of subtile u for every tile: the row maximum over the first slots, then the
-// reference-maximum update, then the exponentials in pairs (each pair packed to bf16 and
-// added to the running sum at once), spread over the remaining slots.  With PV, even
+// barriers.  Slot i issues the LDS reads of slot i+RR_AHEAD's fragment, then the NT MFMAs
+// of its own fragment, then a fixed share of the softmax of subtile u for every tile: the
+// exponentials p = 2^(S c2 - m) against the current reference maximum m, in pairs, each
+// pair packed to bf16 and added to the lane's partial row sum ls at once.  With PV, even
 // slots hold the K fragments of subtile u+1's scores and odd slots the V^T fragments of
-// subtile u-1's PV.  Sets, per tile, the wave-uniform flag "the reference maximum moved"
-// (the caller then scales that tile's accumulators by alpha).
+// subtile u-1's PV.  The caller accepts the subtile when every lane's ls is at most
+// kRingSumLimit (then every p is at most that, since all p >= 0); otherwise it redoes the
+// subtile against the true running maximum (ring_redo).
 template <int D, int NT, bool HAS_PV>
 __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrags<D>& vo, const char* Kt,
                                                 int subk, const char* Vt, int subv,
                                                 const bf16x8 (&qf)[NT][D / 16], const f32x16 (&s)[NT],
                                                 const bf16x8 (&pp)[NT][2], f32x16 (&acc)[NT][D / 32],
-                                                float c2, float (&m_run)[NT], float (&l_run)[NT],
-                                                float (&alpha)[NT], bool (&grow)[NT], f32x16 (&sn)[NT],
-                                                bf16x8 (&pn)[NT][2]) {
+                                                float c2, const float (&m_run)[NT], float (&ls)[NT],
+                                                f32x16 (&sn)[NT], bf16x8 (&pn)[NT][2]) {
   constexpr int KS = D / 16;
   constexpr int NSLOT = (HAS_PV ? 2 : 1) * KS;
-  constexpr int MAXS = NSLOT >= 8 ? 2 : 1;          // slots of the max tree
-  constexpr int FIN = MAXS;                          // slot of the reference-maximum update
-  constexpr int E = NSLOT - FIN - 1;                 // slots of the exponentials
   auto load = [&](int i) -> bf16x8 {
     if (HAS_PV && (i & 1)) {
       const int j = i >> 1;
@@ -153,14 +156,15 @@ __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrag
     return fr.row(Kt, subk, HAS_PV ? (i >> 1) : i);
   };
   bf16x8 frag[NSLOT];
-  frag[0] = load(0);
-  frag[1] = load(1);
-  float mx[NT], m_use[NT], ls[NT];
+#pragma unroll
+  for (int i = 0; i < RR_AHEAD && i < NSLOT; ++i) frag[i] = load(i);
   uint32_t w[NT][8];
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
+  for (int t = 0; t < NT; ++t) ls[t] = 0.0f;
+#pragma unroll
   for (int i = 0; i < NSLOT; ++i) {
-    if (i + 2 < NSLOT) frag[i + 2] = load(i + 2);
+    if (i + RR_AHEAD < NSLOT) frag[i + RR_AHEAD] = load(i + RR_AHEAD);
     if (HAS_PV && (i & 1)) {
       const int j = i >> 1;
 #pragma unroll
@@ -179,38 +183,15 @@ __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrag
     // this slot's share of the softmax, for every tile
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const f32x16& st = s[t];
-      if (i == 0) {
-        mx[t] = fmaxf(fmaxf(st[0], st[1]), st[2]);
-        mx[t] = fmaxf(fmaxf(mx[t], st[3]), st[4]);
-        mx[t] = fmaxf(fmaxf(mx[t], st[5]), st[6]);
-        mx[t] = fmaxf(fmaxf(mx[t], st[7]), st[8]);
-      }
-      if (i == MAXS - 1) {
-        mx[t] = fmaxf(fmaxf(mx[t], st[9]), st[10]);
-        mx[t] = fmaxf(fmaxf(mx[t], st[11]), st[12]);
-        mx[t] = fmaxf(fmaxf(mx[t], st[13]), st[14]);
-        mx[t] = fmaxf(mx[t], st[15]);
-      }
-      if (i == FIN) {
-        mx[t] = pair_max(mx[t]);
-        const float m_new = fmaxf(m_run[t], mx[t] * c2);
-        grow[t] = __any(m_new > m_run[t] + kRingRescaleLog2);
-        m_use[t] = grow[t] ? m_new : m_run[t];
-        alpha[t] = fast_exp2(m_run[t] - m_use[t]);
-        m_run[t] = m_use[t];
-        ls[t] = 0.0f;
-      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (i == FIN + 1 + (k * E) / 8) {
-          const float p0 = fast_exp2(fmaf(st[2 * k], c2, -m_use[t]));
-          const float p1 = fast_exp2(fmaf(st[2 * k + 1], c2, -m_use[t]));
+        if (i == (k * NSLOT) / 8) {
+          const float p0 = fast_exp2(fmaf(s[t][2 * k], c2, -m_run[t]));
+          const float p1 = fast_exp2(fmaf(s[t][2 * k + 1], c2, -m_run[t]));
           w[t][k] = pack_bf16x2(p0, p1);
           ls[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[t][k]), one, ls[t], false);
         }
       }
-      if (i == NSLOT - 1) l_run[t] = fmaf(l_run[t], alpha[t], ls[t]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -219,6 +200,37 @@ __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrag
     pn[t][0] = as_bf16x8(make_uint4(w[t][0], w[t][1], w[t][2], w[t][3]));
     pn[t][1] = as_bf16x8(make_uint4(w[t][4], w[t][5], w[t][6], w[t][7]));
   }
+}
+
+// Slow path of a pipelined subtile whose partial row sum exceeded the limit (and the
+// first subtile of a part): move the reference to the true running maximum, and
+// recompute P and the subtile's sum against it.  Returns alpha, the factor the running
+// sum and the accumulators (which already hold PV of subtile u-1) must be scaled by.
+__device__ __forceinline__ float ring_redo(const f32x16& s, float c2, float& m_run, float& ls,
+                                           bf16x8 (&pn)[2]) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+  mx = fmaxf(mx, s[15]);
+  mx = pair_max(mx);
+  const float m_new = fmaxf(m_run, mx * c2);
+  const float alpha = fast_exp2(m_run - m_new);
+  ls = 0.0f;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[8 * h2 + i], c2, -m_new));
+    uint4 u;
+    u.x = pack_bf16x2(p[0], p[1]);
+    u.y = pack_bf16x2(p[2], p[3]);
+    u.z = pack_bf16x2(p[4], p[5]);
+    u.w = pack_bf16x2(p[6], p[7]);
+    pn[h2] = as_bf16x8(u);
+    ls = sum_bf16x8(u, ls);
+  }
+  m_run = m_new;
+  return alpha;
 }
 
 }  // namespace
@@ -367,19 +379,22 @@ __global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
         entered = st;
       }
       bf16x8 pn[NT][2];
-      float alpha[NT];
-      bool grow[NT];
+      float ls[NT];
       f32x16 sn[NT];
-      ring_block_body<D, NT, HAS_PV>(fr, vo, KT[SY], SUBY, VT[SX], SUBX, qf, s, pp, acc, c2, m_run, l_run,
-                                     alpha, grow, sn, pn);
+      ring_block_body<D, NT, HAS_PV>(fr, vo, KT[SY], SUBY, VT[SX], SUBX, qf, s, pp, acc, c2, m_run, ls, sn,
+                                     pn);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        // the block's softmax results must be formed here, not sunk past the rescale branch
-        pin_operands(pn[t], l_run[t]);
+        // the block's softmax results must be formed here, not sunk past the check below
+        pin_operands(pn[t], ls[t]);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (grow[t]) ring_scale<D>(acc[t], alpha[t]);
+        const bool redo = __any(!(ls[t] <= kRingSumLimit));
+        float alpha = 1.0f;
+        if (redo) alpha = ring_redo(s[t], c2, m_run[t], ls[t], pn[t]);
+        if (redo) ring_scale<D>(acc[t], alpha);
+        l_run[t] = fmaf(l_run[t], alpha, ls[t]);
         pp[t][0] = pn[t][0];
         pp[t][1] = pn[t][1];
         s[t] = sn[t];
@@ -443,6 +458,10 @@ __global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
     }
     ring_pv<D, NT>(vo, vt, u & 1, pf, acc);
   }
+  // The direct loads are not tracked by the compiler: none may still be writing LDS when
+  // the workgroup ends (every issued stage has been entered and waited for by now; this
+  // makes it unconditional).
+  wait_vmcnt0();
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
