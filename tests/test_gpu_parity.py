@@ -117,3 +117,37 @@ def test_full_size_sampled_rows(cfg):
     assert_bf16_close("dk_r tail", got["dk"][0][Rg - n_tail:], ref["dk_r"][Rg - n_tail:])
     assert_bf16_close("dv_r tail", got["dv"][0][Rg - n_tail:], ref["dv_r"][Rg - n_tail:])
     assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))
+
+
+@pytest.mark.parametrize("slope", [6.0, 40.0, 400.0])
+def test_bf16_growing_scores(slope):
+    """Scores that rise along the prompt (a ramp in one key dimension that every query
+    reads), so a row's running maximum keeps moving: the forward's pipelined subtiles
+    keep exceeding their row-sum bound and are redone against the new maximum (every few
+    subtiles at the steepest slope).  O and lse are checked at the bf16 bounds for every
+    slope.  Gradients are checked at those bounds for the mild slope only: with a ramp of
+    height 400 in one key dimension, dQ = tau sum_j dS_j k_j relies on sum_j dS_j = 0 to
+    cancel the common 400, and rounding dS to bf16 before the dQ product (reading 9)
+    breaks that cancellation by design; the steep cases check the gradients are finite."""
+    from tests import _gpu as G
+    w = configs.GQA_P128K.with_(P=6000, R=300, Hq=8, Hkv=2, chunk=2048, block=128, seed=4300)
+    res, mem = _inputs(w, [w.R])
+    kp = synth.bf16_bits_to_f32(res["k_p"]).copy()
+    kp[:, :, 0] = slope * np.linspace(-1.0, 1.0, w.P, dtype=np.float32)[:, None]
+    res["k_p"] = synth.f32_to_bf16_bits(kp)
+    q = synth.bf16_bits_to_f32(mem[0]["q"]).copy()
+    q[:, :, 0] = 4.0
+    mem[0]["q"] = synth.f32_to_bf16_bits(q)
+    st = G.stack_members(mem, w.R)
+    prob = G.problem(w.P, w.R, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+    print(f"[parity] growing scores slope={slope}", flush=True)
+    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [w.R]).fwd().bwd().numpy()
+    ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, 0, w.R, w.tau)
+    assert_bf16_close("o", got["o"][0], ref["o"])
+    assert np.max(np.abs(got["lse"][0] - ref["lse"])) <= 2e-2
+    if slope <= 6.0:
+        for name, a, b in [("dq", got["dq"][0], ref["dq"]), ("dk_r", got["dk"][0], ref["dk_r"]),
+                           ("dv_r", got["dv"][0], ref["dv_r"])]:
+            assert_bf16_close(name, a, b)
+    else:
+        assert all(np.all(np.isfinite(got[n])) for n in ("dq", "dk", "dv"))
