@@ -1,11 +1,13 @@
 """Benchmark: response-replay attention fwd + response-only bwd at a 2,097,152-position
 resident prompt (one GPU).
 
-One step = one group of G = 8 members replayed serially (replay microbatch K = 1): for
-each member, rr_attn_fwd (chunk partials + exact merge), rr_attn_bwd (D, dQ partials +
-ordered reduction, reverse block walk for response dK/dV) and rr_grad_accum of dQ, dK, dV
-into position-aligned fp32 accumulators (zeroed at the start of the group).  All inputs
-are synthetic (seeded N(0,1), rounded to bf16) and resident in HBM before timing starts.
+One step = one group of G = 8 members replayed serially, K members per call (replay
+microbatch K, default 1; --microbatch K stacks K consecutive members, zero-padded to the
+longest of them, into one call).  Each call runs rr_attn_fwd (chunk partials + exact
+merge) and rr_attn_bwd (D, dQ partials + ordered reduction, reverse block walk for
+response dK/dV); each member's dQ, dK, dV then go through rr_grad_accum into
+position-aligned fp32 accumulators (zeroed at the start of the group).  All inputs are
+synthetic (seeded N(0,1), rounded to bf16) and resident in HBM before timing starts.
 
 With --workload bf16_latent_P1048576_R4096_top2048 a step is one response of the
 latent-page top-k variant: fp32 index scores, exact top-2048 selection, sparse attention
@@ -41,6 +43,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="bf16_full_P2097152_G8")
     ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample rows (0 = skip)")
+    ap.add_argument("--microbatch", type=int, default=1,
+                    help="replay microbatch K: the group's members run as calls of K responses each")
     return ap.parse_args()
 
 
@@ -130,50 +134,71 @@ def run_dense(a, w) -> int:
     gen_s = time.time() - t0
 
     kv = R.resident(k_p, v_p, version=1)
+    Kmb = max(1, min(int(a.microbatch), len(lens)))
+    # microbatches: consecutive members, K per call; inputs stacked [K][R_max][...] and
+    # zero-padded (rows past a member's length are padding rows of the call)
+    mbs = []
+    for b0 in range(0, len(lens), Kmb):
+        gs = list(range(b0, min(b0 + Kmb, len(lens))))
+        rmax_b = int(max(lens[g] for g in gs))
+        st = {}
+        for key in ("q", "k_r", "v_r", "d_o"):
+            t = torch.zeros((len(gs), rmax_b) + tuple(members[0][key].shape[2:]), device=dev,
+                            dtype=torch.bfloat16)
+            for i, g in enumerate(gs):
+                t[i, :int(lens[g])] = members[g][key][0]
+            st[key] = t
+        prob = R.Problem(P=w.P, R_max=rmax_b, Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v,
+                         chunk=w.chunk, block=w.block, tau=w.tau, K=len(gs))
+        mbs.append((gs, [int(lens[g]) for g in gs], st, prob))
+    members = None   # the stacked copies are the resident inputs now
     pmax = R.Problem(P=w.P, R_max=Rmax, Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v, chunk=w.chunk,
-                     block=w.block, tau=w.tau)
+                     block=w.block, tau=w.tau, K=Kmb)
     ws_f = R.workspace(pmax, R.RR_OP_FWD, dev)
     ws_b = R.workspace(pmax, R.RR_OP_BWD, dev)
     f32 = dict(device=dev, dtype=torch.float32)
-    o = torch.empty(Rmax, w.Hq, w.d_v, **f32)
-    lse = torch.empty(Rmax, w.Hq, **f32)
-    dq = torch.empty(Rmax, w.Hq, w.d_qk, **f32)
-    dk = torch.empty(Rmax, w.Hkv, w.d_qk, **f32)
-    dv = torch.empty(Rmax, w.Hkv, w.d_v, **f32)
+    # flat output buffers; a call of K responses of stride R_max uses their leading part
+    row_elems = {"o": w.Hq * w.d_v, "lse": w.Hq, "dq": w.Hq * w.d_qk, "dk": w.Hkv * w.d_qk, "dv": w.Hkv * w.d_v}
+    flat = {n: torch.empty(Kmb * Rmax * e, **f32) for n, e in row_elems.items()}
+    shape = {"o": (w.Hq, w.d_v), "lse": (w.Hq,), "dq": (w.Hq, w.d_qk), "dk": (w.Hkv, w.d_qk),
+             "dv": (w.Hkv, w.d_v)}
+
+    def outs(K, rm):
+        return [flat[n][:K * rm * row_elems[n]].view((K, rm) + shape[n]) for n in ("o", "lse", "dq", "dk", "dv")]
     acc = [torch.zeros(Rmax, w.Hq, w.d_qk, **f32), torch.zeros(Rmax, w.Hkv, w.d_qk, **f32),
            torch.zeros(Rmax, w.Hkv, w.d_v, **f32)]
-    probs = [R.Problem(P=w.P, R_max=int(rg), Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v,
-                       chunk=w.chunk, block=w.block, tau=w.tau) for rg in lens]
 
-    def member_pass(g, win=None):
-        rg = int(lens[g])
-        m = members[g]
-        og, lg, dqg, dkg, dvg = o[:rg], lse[:rg], dq[:rg], dk[:rg], dv[:rg]
-        R.rr_attn_fwd(probs[g], kv, m["q"], m["k_r"], m["v_r"], [rg], o=og, lse=lg, ws=ws_f)
-        R.rr_attn_bwd(probs[g], kv, m["q"], m["k_r"], m["v_r"], [rg], og, lg, m["d_o"], dqg, dkg, dvg,
+    def mb_pass(b, win=None):
+        gs, rls, st, prob = mbs[b]
+        og, lg, dqg, dkg, dvg = outs(len(gs), prob.R_max)
+        R.rr_attn_fwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, o=og, lse=lg, ws=ws_f)
+        R.rr_attn_bwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, og, lg, st["d_o"], dqg, dkg, dvg,
                       ws=ws_b)
         if win is not None:
-            R.rr_grad_accum(win, g, 1, [dqg, dkg, dvg])
+            for i, g in enumerate(gs):
+                rg = rls[i]
+                R.rr_grad_accum(win, g, 1, [dqg[i, :rg], dkg[i, :rg], dvg[i, :rg]])
 
     def step():
         for t in acc:
             t.zero_()
         win = R.Accum(acc, G=len(lens), version=1)
-        for g in range(len(lens)):
-            member_pass(g, win)
+        for b in range(len(mbs)):
+            mb_pass(b, win)
         R.rr_accum_check_complete(win)
 
     # parity gate on member 0 (sampled rows, one KV group) before any timing
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
-    member_pass(0)
+    mb_pass(0)
     torch.cuda.synchronize()
     mem_g1 = torch.cuda.max_memory_allocated()
     rows = synth.sample_rows(w.seed, int(lens[0]), a.cpu_rows, w.block) if a.cpu_rows > 0 else None
     got = None
     if rows is not None:
         grp = w.Hq // w.Hkv
-        got = {"o": o[rows, :grp].double().cpu().numpy(), "dq": dq[rows, :grp].double().cpu().numpy()}
+        o0, _, dq0, _, _ = outs(len(mbs[0][0]), mbs[0][3].R_max)
+        got = {"o": o0[0, rows, :grp].double().cpu().numpy(), "dq": dq0[0, rows, :grp].double().cpu().numpy()}
 
     for _ in range(a.warmup):
         step()
@@ -266,11 +291,11 @@ def run_dense(a, w) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "P": w.P, "G": len(lens), "R_g": [int(x) for x in lens],
                    "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk, "chunk": w.chunk, "block": w.block,
-                   "replay_microbatch": 1, "flops_per_step": flops_step},
+                   "replay_microbatch": Kmb, "flops_per_step": flops_step},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
-        "peak_mem_bytes": {"after_1_member": int(mem_g1), "timed_G_groups": int(mem_g8)},
+        "peak_mem_bytes": {"after_1_microbatch": int(mem_g1), "timed_G_groups": int(mem_g8)},
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)

@@ -142,7 +142,9 @@ int32_t rr_num_parts(const rr_problem* p);
  *   o, lse    outputs (see layouts); both NULL = partials only (export required)
  *   part_o    NULL, or export buffer [n_parts][K][R][Hq][d_v] fp32 (n_parts =
  *   part_lse  rr_num_parts); with part_lse [n_parts][K][R][Hq] fp32.  Exported
- *             partials make the per-chunk statistics available to an external merge.
+ *             partials make the per-chunk statistics available to an external merge;
+ *             entries of padding rows (i >= r_len[k]) are unspecified and may be left
+ *             unwritten.
  *   topk_idx  topk > 0: output [K][R][topk] int32, the selected prompt positions of
  *             each row in ascending order (-1 in padding rows); else NULL
  *

@@ -36,27 +36,43 @@ struct TileWork {
   bool ok;
 };
 
+// Row tiles of response k inside the launch's row range: only rows below r_len[k] get a
+// workgroup, so responses shorter than the stride R_max cost nothing for their padding.
+__host__ __device__ __forceinline__ int64_t member_tiles(const Geom& g, int k, int BM) {
+  const int hi = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
+  const int64_t m = hi > g.row_lo ? (int64_t)(hi - g.row_lo) * g.grp : 0;
+  return (m + BM - 1) / BM;
+}
+
+__host__ __device__ __forceinline__ int64_t tiles_per_part(const Geom& g, int BM) {
+  int64_t t = 0;
+  for (int k = 0; k < g.K; ++k) t += member_tiles(g, k, BM);
+  return t;
+}
+
+// Work order: (KV head, part) outermost, then every response's row tiles.  Consecutive
+// work items (which xcd_work_index keeps on one XCD) read the same prompt chunk, and each
+// XCD receives an equal share of real tiles whatever the spread of response lengths.
 __device__ __forceinline__ TileWork decode_tile_work(const Geom& g, int BM) {
   TileWork w;
-  const int64_t m_lo = (int64_t)g.row_lo * g.grp, m_hi = (int64_t)g.row_hi * g.grp;
-  const int64_t n_mt = (m_hi - m_lo + BM - 1) / BM;
-  const int64_t n_work = (int64_t)g.K * g.Hkv * g.n_parts * n_mt;
+  const int64_t T = tiles_per_part(g, BM);
+  const int64_t n_work = (int64_t)g.Hkv * g.n_parts * T;
   int64_t idx = xcd_work_index(n_work);
   w.ok = idx >= 0;
   if (!w.ok) return w;
-  const int64_t mt = idx % n_mt;
-  idx /= n_mt;
+  int64_t j = idx % T;
+  idx /= T;
   w.part = (int)(idx % g.n_parts);
-  idx /= g.n_parts;
-  w.g = (int)(idx % g.Hkv);
-  w.k = (int)(idx / g.Hkv);
-  w.m0 = (int)(m_lo + mt * BM);
+  w.g = (int)(idx / g.n_parts);
+  int k = 0;
+  for (int64_t t = member_tiles(g, 0, BM); j >= t; t = member_tiles(g, ++k, BM)) j -= t;
+  w.k = k;
+  w.m0 = (int)((int64_t)g.row_lo * g.grp + j * BM);
   return w;
 }
 
 inline int64_t tile_work_count(const Geom& g, int BM) {
-  const int64_t m = (int64_t)(g.row_hi - g.row_lo) * g.grp;
-  return (int64_t)g.K * g.Hkv * g.n_parts * ((m + BM - 1) / BM);
+  return (int64_t)g.Hkv * g.n_parts * tiles_per_part(g, BM);
 }
 
 }  // namespace rr

@@ -6,6 +6,7 @@
 // Rows are "flattened": for KV head g, index m = r * grp + hh enumerates response row r
 // and query head h = g * grp + hh, so the grp query heads that read the same K/V run
 // side by side.
+#include "k_attn_tile.h"
 #include "k_common.h"
 #include "kernels.h"
 
@@ -36,30 +37,6 @@ __device__ __forceinline__ PartRange part_range(const Geom& g, int part, int k, 
   return pr;
 }
 
-// Work decomposition shared by the forward and dQ kernels.
-struct RowWork {
-  int k, g, part, m0;
-  bool ok;
-};
-
-__device__ __forceinline__ RowWork decode_rows(const Geom& g, int rows_per_wg) {
-  RowWork w;
-  const int64_t m_lo = (int64_t)g.row_lo * g.grp, m_hi = (int64_t)g.row_hi * g.grp;
-  const int64_t n_mt = (m_hi - m_lo + rows_per_wg - 1) / rows_per_wg;
-  const int64_t n_work = (int64_t)g.K * g.Hkv * g.n_parts * n_mt;
-  int64_t idx = xcd_work_index(n_work);
-  w.ok = idx >= 0;
-  if (!w.ok) return w;
-  const int64_t mt = idx % n_mt;
-  idx /= n_mt;
-  w.part = (int)(idx % g.n_parts);
-  idx /= g.n_parts;
-  w.g = (int)(idx % g.Hkv);
-  w.k = (int)(idx / g.Hkv);
-  w.m0 = (int)(m_lo + mt * rows_per_wg);
-  return w;
-}
-
 }  // namespace
 
 template <int D>
@@ -72,7 +49,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_partials_f32(Geom g, const float
                                                              float* __restrict__ part_lse) {
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
-  const RowWork w = decode_rows(g, kF32Rows);
+  const TileWork w = decode_tile_work(g, kF32Rows);
   if (!w.ok) return;
   const int m_hi = g.row_hi * g.grp;
   const int m = w.m0 + threadIdx.x;
@@ -144,7 +121,7 @@ __global__ __launch_bounds__(kF32Rows) void dq_partials_f32(Geom g, const float*
                                                             float* __restrict__ dq_part) {
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
-  const RowWork w = decode_rows(g, kF32Rows);
+  const TileWork w = decode_tile_work(g, kF32Rows);
   if (!w.ok) return;
   const int m_hi = g.row_hi * g.grp;
   const int m = w.m0 + threadIdx.x;
@@ -266,10 +243,9 @@ __global__ __launch_bounds__(32 * (D / 32)) void dkdv_f32(Geom g, int key_hi,
 
 namespace {
 
-int64_t row_work(const Geom& g, int rows_per_wg) {
-  const int64_t m = (int64_t)(g.row_hi - g.row_lo) * g.grp;
-  return (int64_t)g.K * g.Hkv * g.n_parts * ((m + rows_per_wg - 1) / rows_per_wg);
-}
+// The forward and dQ kernels share the bf16 kernels' work order (decode_tile_work), with
+// one workgroup per kF32Rows flattened rows.
+int64_t row_work(const Geom& g, int rows_per_wg) { return tile_work_count(g, rows_per_wg); }
 
 }  // namespace
 
