@@ -9,6 +9,11 @@ response dK/dV); each member's dQ, dK, dV then go through rr_grad_accum into
 position-aligned fp32 accumulators (zeroed at the start of the group).  All inputs are
 synthetic (seeded N(0,1), rounded to bf16) and resident in HBM before timing starts.
 
+With --full-sequence every call also forms the prompt K/V gradients (rr_attn_prompt_grads,
+summed over the group): the term the response-only contract drops, for differential
+comparison.  `value` then counts its flops too, and the line reports the gradient norms
+and the cosine between the response-only and the full gradient at the attention boundary.
+
 With --workload bf16_latent_P1048576_R4096_top2048 a step is one response of the
 latent-page top-k variant: fp32 index scores, exact top-2048 selection, sparse attention
 forward and response-only backward (64 heads sharing 576-wide latent rows).
@@ -45,6 +50,9 @@ def _args():
     ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample rows (0 = skip)")
     ap.add_argument("--microbatch", type=int, default=1,
                     help="replay microbatch K: the group's members run as calls of K responses each")
+    ap.add_argument("--full-sequence", action="store_true",
+                    help="full-sequence differential mode: every call also forms the prompt K/V "
+                         "gradients (rr_attn_prompt_grads), summed over the group")
     return ap.parse_args()
 
 
@@ -52,12 +60,14 @@ def kernel_flops(w, R: int) -> dict:
     """Algorithmic flops of each launch kind for one member of length R (d_qk = d_v = d).
     dq_partials: S, dP and dQ over every visible pair; fwd_partials: S and PV over every
     visible pair; dkdv: dK and dV over the response pairs (the S / dP it recomputes are
-    not counted)."""
+    not counted); prompt_dkdv (full-sequence mode only): S, dP, dK and dV over every
+    (row, prompt key) pair, since without stored scores the prompt gradient needs all four."""
     d, Hq = w.d_qk, w.Hq
     n_p, n_r = R * w.P, R * (R + 1) // 2
     return {"fwd_partials": 4.0 * d * Hq * (n_p + n_r),
             "dq_partials": 6.0 * d * Hq * (n_p + n_r),
-            "dkdv": 4.0 * d * Hq * n_r}
+            "dkdv": 4.0 * d * Hq * n_r,
+            "prompt_dkdv": 8.0 * d * Hq * n_p}
 
 
 def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
@@ -83,6 +93,7 @@ KERNEL_SOURCES = {
     "fwd_partials": ["k_fwd_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
     "dq_partials": ["k_dq_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
     "dkdv": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "prompt_dkdv": ["k_prompt_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
 }
 
 
@@ -167,6 +178,11 @@ def run_dense(a, w) -> int:
         return [flat[n][:K * rm * row_elems[n]].view((K, rm) + shape[n]) for n in ("o", "lse", "dq", "dk", "dv")]
     acc = [torch.zeros(Rmax, w.Hq, w.d_qk, **f32), torch.zeros(Rmax, w.Hkv, w.d_qk, **f32),
            torch.zeros(Rmax, w.Hkv, w.d_v, **f32)]
+    full = bool(a.full_sequence)
+    if full:   # the group's prompt K/V gradients, summed over its members
+        dk_p = torch.empty(w.P, w.Hkv, w.d_qk, **f32)
+        dv_p = torch.empty(w.P, w.Hkv, w.d_v, **f32)
+        ws_pg = R.workspace(pmax, R.RR_OP_PROMPT_GRADS, dev)
 
     def mb_pass(b, win=None):
         gs, rls, st, prob = mbs[b]
@@ -174,6 +190,9 @@ def run_dense(a, w) -> int:
         R.rr_attn_fwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, o=og, lse=lg, ws=ws_f)
         R.rr_attn_bwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, og, lg, st["d_o"], dqg, dkg, dvg,
                       ws=ws_b)
+        if full:
+            R.rr_attn_prompt_grads(prob, kv, st["q"], rls, og, lg, st["d_o"], dk_p, dv_p,
+                                   accumulate=1 if b > 0 else 0, ws=ws_pg)
         if win is not None:
             for i, g in enumerate(gs):
                 rg = rls[i]
@@ -217,9 +236,13 @@ def run_dense(a, w) -> int:
 
     flops_step = 0.0
     per_kernel_flops = {"fwd_partials": 0.0, "dq_partials": 0.0, "dkdv": 0.0}
+    if full:
+        per_kernel_flops["prompt_dkdv"] = 0.0
     for rg in lens:
         kf = kernel_flops(w, int(rg))
         flops_step += configs.flops_dense(w.Hq, w.d_qk, w.d_v, int(rg), w.P)["total"]
+        if full:
+            flops_step += kf["prompt_dkdv"]
         for k in per_kernel_flops:
             per_kernel_flops[k] += kf[k]
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -284,17 +307,31 @@ def run_dense(a, w) -> int:
         parity["pass"] = bool(parity["o_rel_l2"] <= 5e-3 and parity["dq_rel_l2"] <= 5e-3
                               and parity["o_max_abs"] <= 2e-2 and parity["dq_max_abs"] <= 2e-2)
 
+    fs = None
+    if full:   # norms of the group's response-side and prompt-side gradients after the last step
+        nrm = lambda x: float(torch.linalg.vector_norm(x, dtype=torch.float64))
+        n_resp = float(np.sqrt(sum(nrm(t) ** 2 for t in acc)))
+        n_prompt = float(np.sqrt(nrm(dk_p) ** 2 + nrm(dv_p) ** 2))
+        fs = {"prompt_flops_per_step": float(sum(kernel_flops(w, int(rg))["prompt_dkdv"] for rg in lens)),
+              "norm_response_grads": n_resp, "norm_dk_p": nrm(dk_p), "norm_dv_p": nrm(dv_p),
+              "cosine_response_only_vs_full": n_resp / float(np.hypot(n_resp, n_prompt)),
+              "note": "gradient vector (dQ, dK_r, dV_r, dK_p, dV_p) of the group at the attention "
+                      "boundary; the response-only vector has dK_p = dV_p = 0"}
+
     out = {
-        "metric": "response-replay attention fwd+bwd TFLOP/s + % bf16 MFMA peak at P=2M",
+        "metric": "response-replay attention fwd+bwd TFLOP/s + % bf16 MFMA peak at P=2M"
+                  + (", full-sequence differential mode" if full else ""),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "P": w.P, "G": len(lens), "R_g": [int(x) for x in lens],
                    "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk, "chunk": w.chunk, "block": w.block,
-                   "replay_microbatch": Kmb, "flops_per_step": flops_step},
+                   "replay_microbatch": Kmb, "flops_per_step": flops_step,
+                   "mode": "full_sequence" if full else "response_only"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
+        "full_sequence": fs,
         "peak_mem_bytes": {"after_1_microbatch": int(mem_g1), "timed_G_groups": int(mem_g8)},
         "input_gen_s": round(gen_s, 1),
     }

@@ -79,6 +79,7 @@ extern "C" {
 
 #define RR_OP_FWD 0           /* workspace query for rr_attn_fwd                      */
 #define RR_OP_BWD 1           /* workspace query for rr_attn_bwd                      */
+#define RR_OP_PROMPT_GRADS 2  /* workspace query for rr_attn_prompt_grads             */
 
 #define RR_MAX_K     64       /* responses per replay microbatch                      */
 
@@ -215,6 +216,39 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv,
                 const int32_t* topk_idx, const float* o, const float* lse, const void* d_o,
                 float* dq, float* dk_r, float* dv_r, int32_t accumulate, int32_t block_idx,
                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rr_attn_prompt_grads - full-sequence differential mode: the prompt-side gradient term
+ * that the response-only contract drops, for comparing the two paths.
+ *
+ * Source: ai.thesatyajit.com/articles/longstraw-2m-rl, section "The move: change the
+ * graph boundary" (a full-sequence gradient is the direct response term plus a term
+ * through the prompt state; the contract keeps the first); networkfinds.com/long-context-
+ * rl-is-a-state-lifetime-problem, section "Preserve gradient semantics, not just forward
+ * outputs" (validate against a conventional run).  rr_attn_bwd never forms this term;
+ * a caller asks for it explicitly, with its own output buffers.
+ *
+ * For every prompt position j, KV head g, and every row i < r_len[k] of every response
+ * k of the call, over the query heads h of g's group (no mask: rows see all of the
+ * prompt):
+ *   p = exp(tau q_ih.k_jg - lse_ih),  D_ih = dO_ih . O_ih,  ds = p (dO_ih.v_jg - D_ih),
+ *   dk_p[j][g] = tau sum ds q_ih,     dv_p[j][g] = sum p dO_ih.
+ * bf16 problems round p and ds to bf16 before the two products (fp32 accumulation);
+ * fp32 problems compute in fp32 throughout.
+ *
+ *   q, d_o      [K][R][Hq][d] (problem dtype), the rows of rr_attn_bwd
+ *   o, lse      the forward's fp32 outputs (global statistics; a caller holding one shard
+ *               of the prompt passes the merged ones and gets its shard's gradients)
+ *   dk_p, dv_p  outputs [P][Hkv][d] fp32, device; every position is written (=) or
+ *               added to (+=, accumulate = 1), e.g. across the members of a group
+ *   ws          workspace of rr_workspace_bytes(p, RR_OP_PROMPT_GRADS) bytes: the rows of
+ *               each KV head repacked contiguously, with their lse and D
+ * Dense pages only (latent = 0; RR_E_UNSUPPORTED otherwise); d_qk = d_v in {64, 128}.
+ */
+int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
+                         const int32_t* r_len, const float* o, const float* lse, const void* d_o,
+                         float* dk_p, float* dv_p, int32_t accumulate, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Update-boundary accumulator for G serially replayed members.
    Source: networkfinds.com/long-context-rl-is-a-state-lifetime-problem, sections

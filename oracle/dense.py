@@ -147,6 +147,33 @@ def attend_bwd(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Optional[Sequence[i
     return out
 
 
+def prompt_grads_given_stats(q, k_p, v_p, d_o, o, lse, tau: float, keys: Sequence[int]):
+    """dk_p, dv_p [n][Hkv][d] of the given prompt positions (the term the response-only
+    contract drops; full-sequence differential mode), from the rows' global output O and
+    natural-log lse instead of recomputing them over the whole prompt.  q, d_o, o, lse are
+    those of every row that sees the prompt (any number of responses stacked along the
+    row axis: every row sees every prompt position).  Per row i, head h, key j:
+      p_ij = exp(tau q.k_j - lse_i),  D_i = d_o_i . O_i,  ds_ij = p_ij (d_o_i . v_j - D_i),
+      dk_p[j] = tau sum_{i,h} ds_ij q_ih,  dv_p[j] = sum_{i,h} p_ij d_o_ih
+    over the query heads h of key j's KV head.  With exact O and lse this is the dk_p,
+    dv_p of attend_bwd(full_sequence=True); with a device's O and lse it is exact
+    conditional on them."""
+    R, Hq, d_qk = q.shape
+    P, Hkv, d_v = v_p.shape
+    keys = np.asarray(keys, dtype=np.int64)
+    dk = np.zeros((keys.size, Hkv, d_qk))
+    dv = np.zeros((keys.size, Hkv, d_v))
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        qh, doh = q[:, h, :], d_o[:, h, :]
+        D = np.sum(doh * o[:, h, :], axis=1)
+        p = np.exp(tau * (qh @ k_p[keys, g, :].T) - lse[:, h][:, None])   # [R][n]
+        ds = p * (doh @ v_p[keys, g, :].T - D[:, None])
+        dk[:, g, :] += tau * (ds.T @ qh)
+        dv[:, g, :] += p.T @ doh
+    return dk, dv
+
+
 def chunk_bounds(P: int, chunk: int) -> List[tuple]:
     """Contiguous prompt chunks [c*chunk, min((c+1)*chunk, P)); the last may be partial."""
     return [(a, min(a + chunk, P)) for a in range(0, P, chunk)]

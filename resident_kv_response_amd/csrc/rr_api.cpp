@@ -264,6 +264,31 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   return RR_OK;
 }
 
+int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q, const int32_t* r_len,
+                         const float* o, const float* lse, const void* d_o, float* dk_p, float* dv_p,
+                         int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = validate_prompt_grads(p, kv, q, r_len, o, lse, d_o, dk_p, dv_p, accumulate, ws, ws_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Geom g = make_geom(p, r_len);
+  const PgGeom pg = make_pg_geom(p, r_len);
+  const size_t rows = (size_t)p->Hkv * pg.n_rows;
+  const size_t esz = p->dtype == RR_BF16 ? 2 : 4;
+  const size_t rows_bytes = align_up(rows * p->d_qk * esz, 256);
+  void* qs = ws;
+  void* os = carve(ws, rows_bytes);
+  float* sts = carve(ws, 2 * rows_bytes);
+  hipError_t e;
+  if ((e = timed("pg_pack", s, [&] { return launch_pg_pack(g, pg, p->dtype, q, o, lse, d_o, qs, os, sts, s); })))
+    return hip_fail(e, "pg_pack");
+  if ((e = timed("prompt_dkdv", s, [&] {
+         return launch_prompt_dkdv(g, pg, p->dtype, kv->k_p, kv->v_p, qs, os, sts, dk_p, dv_p, accumulate, s);
+       })))
+    return hip_fail(e, "prompt_dkdv");
+  return RR_OK;
+}
+
 int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version, const float* const* grads,
                   const int64_t* n_elems, float scale, void* stream) {
   clear_error();

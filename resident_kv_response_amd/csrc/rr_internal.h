@@ -51,6 +51,20 @@ int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
                    const float* const* grads, const int64_t* n_elems);
 Geom make_geom(const rr_problem* p, const int32_t* r_len);
 
+// Prompt-gradient stream (full-sequence differential mode): the rows of each KV head,
+// response after response, each response's r_len[k] * grp flattened rows padded to a
+// multiple of 64.  off[k] is response k's first stream row; off[K] = n_rows.
+struct PgGeom {
+  int32_t n_rows;
+  int32_t off[RR_MAX_K + 1];
+};
+PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len);
+size_t ws_prompt_bytes(const rr_problem* p);
+int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
+                          const int32_t* r_len, const float* o, const float* lse, const void* d_o,
+                          const float* dk_p, const float* dv_p, int32_t accumulate, const void* ws,
+                          size_t ws_bytes);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Row chunks of the latent response-pair GEMM (dK_r, dV_r): the response rows are split

@@ -111,6 +111,19 @@ size_t ws_bwd_bytes(const rr_problem* p) {
          align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256);
 }
 
+// Stream rows per KV head bound for the workspace: every response at R_max rows.
+static int64_t pg_rows_max(const rr_problem* p) {
+  const int64_t per = ((int64_t)p->R_max * (p->Hq / p->Hkv) + 63) / 64 * 64;
+  return per * p->K;
+}
+
+size_t ws_prompt_bytes(const rr_problem* p) {
+  // packed Q and dO rows [Hkv][n_rows][d], then per 64-row stage lse2 and -D
+  const size_t rows = (size_t)p->Hkv * pg_rows_max(p);
+  const size_t esz = p->dtype == RR_BF16 ? 2 : 4;
+  return 2 * align_up(rows * p->d_qk * esz, 256) + align_up(rows * 2 * sizeof(float), 256);
+}
+
 static int check_r_len(const rr_problem* p, const int32_t* r_len) {
   if (!r_len) return set_error(RR_E_NULL, "r_len is NULL");
   for (int k = 0; k < p->K; ++k)
@@ -191,6 +204,44 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
   return RR_OK;
 }
 
+int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
+                          const int32_t* r_len, const float* o, const float* lse, const void* d_o,
+                          const float* dk_p, const float* dv_p, int32_t accumulate, const void* ws,
+                          size_t ws_bytes) {
+  int rc = validate_problem(p);
+  if (rc) return rc;
+  if (p->latent) return set_error(RR_E_UNSUPPORTED, "prompt gradients are built for dense K/V pages");
+  if ((rc = check_resident(p, kv))) return rc;
+  if (!q || !o || !lse || !d_o || !dk_p || !dv_p)
+    return set_error(RR_E_NULL, "q / o / lse / d_o / dk_p / dv_p is NULL");
+  if ((rc = check_r_len(p, r_len))) return rc;
+  if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
+  if ((rc = check_aligned("q / k_p / v_p / o / d_o / dk_p / dv_p / ws",
+                          {q, kv->k_p, kv->v_p, o, d_o, dk_p, dv_p, ws})))
+    return rc;
+  if ((int64_t)p->Hkv * pg_rows_max(p) * p->d_qk > ((int64_t)1 << 31))
+    return set_error(RR_E_SHAPE, "stream of K*R_max*Hq*d_qk elements exceeds 2^31");
+  const size_t need = ws_prompt_bytes(p);
+  if (!ws || ws_bytes < need)
+    return set_error(RR_E_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                     ws ? "" : ", NULL");
+  return RR_OK;
+}
+
+PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len) {
+  PgGeom pg;
+  memset(&pg, 0, sizeof(pg));
+  const int64_t grp = p->Hq / p->Hkv;
+  int64_t at = 0;
+  for (int k = 0; k < p->K; ++k) {
+    pg.off[k] = (int32_t)at;
+    at += ((int64_t)r_len[k] * grp + 63) / 64 * 64;
+  }
+  for (int k = p->K; k <= RR_MAX_K; ++k) pg.off[k] = (int32_t)at;
+  pg.n_rows = (int32_t)at;
+  return pg;
+}
+
 int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
                    const float* part_lse, const float* o, const float* lse) {
   if (n_parts < 1) return set_error(RR_E_SHAPE, "n_parts must be >= 1 (got %d)", n_parts);
@@ -259,6 +310,13 @@ size_t rr_workspace_bytes(const rr_problem* p, int op) {
   if (rr::validate_problem(p)) return 0;
   if (op == RR_OP_FWD) return rr::ws_fwd_bytes(p, false);
   if (op == RR_OP_BWD) return rr::ws_bwd_bytes(p);
+  if (op == RR_OP_PROMPT_GRADS) {
+    if (p->latent) {
+      rr::set_error(RR_E_UNSUPPORTED, "prompt gradients are built for dense K/V pages");
+      return 0;
+    }
+    return rr::ws_prompt_bytes(p);
+  }
   rr::set_error(RR_E_SHAPE, "unknown op %d", op);
   return 0;
 }

@@ -21,12 +21,12 @@ RR_OK = 0
 RR_E_NULL, RR_E_SHAPE, RR_E_UNSUPPORTED, RR_E_WORKSPACE = -1, -2, -3, -4
 RR_E_RANGE, RR_E_DUPLICATE, RR_E_STALE, RR_E_MISSING, RR_E_HIP = -5, -6, -7, -8, -9
 RR_F32, RR_BF16 = 0, 1
-RR_OP_FWD, RR_OP_BWD = 0, 1
+RR_OP_FWD, RR_OP_BWD, RR_OP_PROMPT_GRADS = 0, 1, 2
 RR_MAX_K, RR_MAX_ACC = 64, 8
 RR_FLAG_SHARD_NO_RESPONSE = 1
 
 EXPORTS = ["rr_workspace_bytes", "rr_num_parts", "rr_attn_fwd", "rr_lse_merge", "rr_attn_bwd",
-           "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
+           "rr_attn_prompt_grads", "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
            "rr_profile_end"]
 
 
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.rr_attn_bwd.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp, vp, vp,
                                   ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         L.rr_attn_bwd.restype = ctypes.c_int
+        L.rr_attn_prompt_grads.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp,
+                                           ctypes.POINTER(i32), vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.rr_attn_prompt_grads.restype = ctypes.c_int
         L.rr_grad_accum.argtypes = [ctypes.POINTER(CAccum), i32, ctypes.c_uint64,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.c_float, vp]
         L.rr_grad_accum.restype = ctypes.c_int
@@ -201,6 +204,17 @@ def rr_attn_bwd(p: Problem, kv: CResident, q, k_r, v_r, r_len, o, lse, d_o, dq, 
                              _r_len(r_len), _ptr(topk_idx), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq),
                              _ptr(dk_r), _ptr(dv_r), int(accumulate), int(block_idx), _ptr(ws),
                              nbytes, _stream(stream)))
+
+
+def rr_attn_prompt_grads(p: Problem, kv: CResident, q, r_len, o, lse, d_o, dk_p, dv_p,
+                         accumulate: int = 0, ws=None, stream=None) -> None:
+    """Full-sequence differential mode: dk_p, dv_p [P][Hkv][d] fp32, the prompt-side term
+    that rr_attn_bwd drops."""
+    cp = p.c()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _r_len(r_len),
+                                      _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dk_p), _ptr(dv_p),
+                                      int(accumulate), _ptr(ws), nbytes, _stream(stream)))
 
 
 class Accum:

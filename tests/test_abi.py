@@ -101,6 +101,40 @@ def test_bwd_rejects_bad_arguments():
     assert call(ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_BWD) - 1) == R.RR_E_WORKSPACE
 
 
+def test_prompt_grads_rejects_bad_arguments():
+    L = R.lib()
+    p = _prob()
+    kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
+
+    def call(prob=p, r_len=(256,), accumulate=0, ws=FAKE, ws_bytes=1 << 40, dk_p=FAKE, kv_=kv):
+        cp = prob.c()
+        arr = (ctypes.c_int32 * len(r_len))(*r_len)
+        return L.rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv_), FAKE, arr, FAKE, FAKE, FAKE,
+                                      dk_p, FAKE, accumulate, ws, ws_bytes, None)
+
+    assert call(r_len=(257,)) == R.RR_E_SHAPE
+    assert call(accumulate=2) == R.RR_E_SHAPE
+    assert call(dk_p=None) == R.RR_E_NULL
+    assert call(dk_p=FAKE + 4) == R.RR_E_SHAPE                      # misaligned
+    assert call(ws=None) == R.RR_E_WORKSPACE
+    assert call(ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_PROMPT_GRADS) - 1) == R.RR_E_WORKSPACE
+    assert call(kv_=R.CResident(k_p=FAKE, v_p=None, k_idx=None, P=p.P, version=0)) == R.RR_E_NULL
+    lat = R.Problem(P=4096, R_max=64, Hq=64, Hkv=1, d_qk=576, d_v=512, chunk=4096, block=64, tau=0.04,
+                    dtype=R.RR_BF16, topk=256, idx_dim=128, latent=1)
+    assert call(prob=lat, r_len=(64,)) == R.RR_E_UNSUPPORTED
+
+
+def test_prompt_grads_workspace_formula():
+    # rows of each KV head, every response at R_max rows, padded to 64 per response
+    p = _prob(P=2097152, R_max=7666, Hq=24, Hkv=4, d_qk=128, d_v=128, chunk=131072, dtype=R.RR_BF16, K=3)
+    up = lambda x: -(-x // 256) * 256
+    rows = 4 * 3 * (-(-7666 * 6 // 64) * 64)
+    assert R.rr_workspace_bytes(p, R.RR_OP_PROMPT_GRADS) == 2 * up(rows * 128 * 2) + up(rows * 8)
+    p32 = _prob()
+    rows = 1 * 1 * 256 * 4
+    assert R.rr_workspace_bytes(p32, R.RR_OP_PROMPT_GRADS) == 2 * up(rows * 64 * 4) + up(rows * 8)
+
+
 def test_merge_rejects_bad_arguments():
     L = R.lib()
     assert L.rr_lse_merge(0, 10, 64, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE

@@ -89,6 +89,31 @@ def test_full_sequence_mode_differs_only_by_prompt_grads():
     assert np.abs(full["dk_p"]).max() > 1e-3          # the dropped term is not trivially zero
 
 
+def test_prompt_grads_given_stats_equal_full_sequence_mode():
+    # two responses sharing the prompt: the conditional form over the stacked rows of both,
+    # fed the exact O and lse, equals the sum of the two full-sequence prompt gradients
+    x = rand_problem(31, 23, 9, 4, 2, 6)
+    y = rand_problem(32, 23, 5, 4, 2, 6)
+    y["k_p"], y["v_p"] = x["k_p"], x["v_p"]
+    tau = 0.45
+    rows_q, rows_do, rows_o, rows_lse = [], [], [], []
+    ref_k = np.zeros_like(x["k_p"])
+    ref_v = np.zeros_like(x["v_p"])
+    for z in (x, y):
+        o, lse = dense.attend(z["q"], z["k_p"], z["v_p"], z["k_r"], z["v_r"], tau)
+        g = dense.attend_bwd(z["q"], z["k_p"], z["v_p"], z["k_r"], z["v_r"], z["d_o"], tau,
+                             full_sequence=True)
+        ref_k += g["dk_p"]
+        ref_v += g["dv_p"]
+        rows_q.append(z["q"]); rows_do.append(z["d_o"]); rows_o.append(o); rows_lse.append(lse)
+    keys = np.array([0, 7, 22])
+    dk, dv = dense.prompt_grads_given_stats(np.concatenate(rows_q), x["k_p"], x["v_p"],
+                                            np.concatenate(rows_do), np.concatenate(rows_o),
+                                            np.concatenate(rows_lse), tau, keys)
+    np.testing.assert_allclose(dk, ref_k[keys], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv, ref_v[keys], atol=1e-12, rtol=0)
+
+
 def _loss(x, tau):
     o, _ = dense.attend(x["q"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], tau)
     return float(np.sum(o * x["d_o"]))
