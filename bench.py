@@ -14,6 +14,10 @@ summed over the group): the term the response-only contract drops, for different
 comparison.  `value` then counts its flops too, and the line reports the gradient norms
 and the cosine between the response-only and the full gradient at the attention boundary.
 
+With --workload bf16_lastkv_P2097152_C8192 a step is one layer's current chunk of a LastKV
+recurrence (8192 positions after 2,097,152 of history): the previous chunk's blend,
+forward, response-only backward, the blended chunk's gradient and the blend's backward.
+
 With --workload bf16_latent_P1048576_R4096_top2048 a step is one response of the
 latent-page top-k variant: fp32 index scores, exact top-2048 selection, sparse attention
 forward and response-only backward (64 heads sharing 576-wide latent rows).
@@ -115,6 +119,8 @@ def main() -> int:
     w = configs.BY_NAME[a.workload]
     if w.latent:
         return run_latent(a, w)
+    if "lastkv" in w.name:
+        return run_lastkv(a, w)
     return run_dense(a, w)
 
 
@@ -390,6 +396,140 @@ def roofline_entry(name, model, launches_per_step, avg_ms, traffic):
             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
             "avg_launch_ms": round(avg_ms, 4), "algorithmic_bytes_per_launch": model["bytes"] * per,
             "flops_per_launch": model["flops"] * per}
+
+
+def run_lastkv(a, w) -> int:
+    """One layer's current chunk of a LastKV recurrence (C = w.R positions after w.P of
+    history): blend of the previous chunk (K, V), forward, response-only backward of the
+    chunk, the blended chunk's gradient (rr_attn_prompt_grads over its key range) and the
+    blend's backward (both K/V sources and the gate)."""
+    import torch
+
+    from resident_kv_response_amd import configs, rr_attn as R, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    C, P = w.R, w.P
+    t0 = time.time()
+    x = synth.lastkv_chunk(w)
+
+    def up(v):
+        return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    hist_k, hist_v = up(x["k_last"]), up(x["v_last"])           # the previous chunk's slot: [P-C, P)
+    kL_prev, vL_prev = hist_k[P - C:].clone(), hist_v[P - C:].clone()
+    kl_prev, vl_prev = up(x["k_prev_layer"]), up(x["v_prev_layer"])
+    q, k_cur, v_cur, d_o = (up(x[n])[None] for n in ("q", "k_cur", "v_cur", "d_o"))
+    alpha = torch.tensor(x["alpha"], device=dev)
+    gen_s = time.time() - t0
+    kv = R.resident(hist_k, hist_v, version=1)
+    prob = R.Problem(P=P, R_max=C, Hq=w.Hq, Hkv=w.Hkv, d_qk=w.d_qk, d_v=w.d_v, chunk=w.chunk, block=w.block,
+                     tau=w.tau, K=1)
+    ws_f = R.workspace(prob, R.RR_OP_FWD, dev)
+    ws_b = R.workspace(prob, R.RR_OP_BWD, dev)
+    ws_pg = R.workspace(prob, R.RR_OP_PROMPT_GRADS, dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    o = torch.empty(1, C, w.Hq, w.d_v, **f32)
+    lse = torch.empty(1, C, w.Hq, **f32)
+    dq = torch.empty(1, C, w.Hq, w.d_qk, **f32)
+    dk = torch.empty(1, C, w.Hkv, w.d_qk, **f32)
+    dv = torch.empty(1, C, w.Hkv, w.d_v, **f32)
+    dkb = torch.empty(C, w.Hkv, w.d_qk, **f32)
+    dvb = torch.empty(C, w.Hkv, w.d_v, **f32)
+    g_src = {n: torch.empty(C, w.Hkv, w.d_qk, **f32) for n in ("kl", "kL", "vl", "vL")}
+    d_alpha = torch.empty(w.Hkv, **f32)
+
+    def step():
+        R.rr_lastkv_blend(alpha, kl_prev, kL_prev, hist_k[P - C:])
+        R.rr_lastkv_blend(alpha, vl_prev, vL_prev, hist_v[P - C:])
+        R.rr_attn_fwd(prob, kv, q, k_cur, v_cur, [C], o=o, lse=lse, ws=ws_f)
+        R.rr_attn_bwd(prob, kv, q, k_cur, v_cur, [C], o, lse, d_o, dq, dk, dv, ws=ws_b)
+        R.rr_attn_prompt_grads(prob, kv, q, [C], o, lse, d_o, dkb, dvb, key_range=(P - C, P), ws=ws_pg)
+        R.rr_lastkv_blend_bwd(alpha, kl_prev, kL_prev, dkb, g_src["kl"], g_src["kL"], d_alpha)
+        R.rr_lastkv_blend_bwd(alpha, vl_prev, vL_prev, dvb, g_src["vl"], g_src["vL"], d_alpha, accumulate=1)
+
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w.seed, C, a.cpu_rows, w.block) if a.cpu_rows > 0 else None
+    grp = w.Hq // w.Hkv
+    got = None
+    if rows is not None:
+        got = {"o": o[0, rows, :grp].double().cpu().numpy(), "dq": dq[0, rows, :grp].double().cpu().numpy()}
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    R.rr_profile_begin()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    prof = R.rr_profile_end()
+    ms_per_step = (t2 - t1) * 1e3 / a.steps
+
+    kf = kernel_flops(w, C)
+    per_kernel_flops = {"fwd_partials": kf["fwd_partials"], "dq_partials": kf["dq_partials"], "dkdv": kf["dkdv"],
+                        "prompt_dkdv": 8.0 * w.d_qk * w.Hq * C * C}
+    flops_step = configs.flops_dense(w.Hq, w.d_qk, w.d_v, C, P)["total"] + per_kernel_flops["prompt_dkdv"]
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    dom_name, (dom_launches, dom_ms) = max(prof.items(), key=lambda kv_: kv_[1][1])
+    roof = None
+    if dom_name in per_kernel_flops:
+        avg_ms = dom_ms / dom_launches
+        flops_per_launch = per_kernel_flops[dom_name] / (dom_launches / a.steps)
+        achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profiles(dom_name, w.name, source_sha(KERNEL_SOURCES[dom_name])),
+                "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": flops_per_launch}
+    kernels = {k: {"launches_per_step": v[0] / a.steps, "ms_per_step": round(v[1] / a.steps, 3)}
+               for k, v in sorted(prof.items(), key=lambda kv_: -kv_[1][1])}
+    for k, fl in per_kernel_flops.items():
+        if k in kernels:
+            kernels[k]["tflops"] = round(fl / (kernels[k]["ms_per_step"] * 1e-3) / 1e12, 2)
+
+    cpu = parity = None
+    if rows is not None:
+        from oracle import dense, lastkv
+        f = lambda v: synth.as_f64(v, w.dtype)
+        tc = time.perf_counter()
+        # history of KV head 0: last-layer K/V of the older chunks, then the blended chunk
+        al = np.asarray(x["alpha"][:1], dtype=np.float64)
+        hk = np.concatenate([f(x["k_last"][:P - C, :1]),
+                             lastkv.blend(f(x["k_prev_layer"][:, :1]), f(x["k_last"][P - C:, :1]), al)], 0)
+        hv = np.concatenate([f(x["v_last"][:P - C, :1]),
+                             lastkv.blend(f(x["v_prev_layer"][:, :1]), f(x["v_last"][P - C:, :1]), al)], 0)
+        qs, kr, vr, do = f(x["q"][:, :grp]), f(x["k_cur"][:, :1]), f(x["v_cur"][:, :1]), f(x["d_o"][:, :grp])
+        ro, _ = dense.attend(qs, hk, hv, kr, vr, w.tau, rows=rows)
+        rgr = dense.attend_bwd(qs, hk, hv, kr, vr, do, w.tau, rows=rows)
+        cpu_s = time.perf_counter() - tc
+        cpu_flops = sum(grp * 10.0 * w.d_qk * (P + int(r) + 1) for r in rows)
+        cores = len(os.sched_getaffinity(0))
+        cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(rows)} rows of the chunk {list(map(int, rows))}, KV head 0 and its {grp} query "
+                         f"heads, blend + fwd + dQ over {P} history keys and the causal chunk keys; {cpu_s:.1f} s"}
+        rel = lambda u, y: float(np.linalg.norm(u - y) / np.linalg.norm(y))
+        parity = {"rows": len(rows), "o_rel_l2": rel(got["o"], ro), "dq_rel_l2": rel(got["dq"], rgr["dq"]),
+                  "o_max_abs": float(np.abs(got["o"] - ro).max()),
+                  "dq_max_abs": float(np.abs(got["dq"] - rgr["dq"]).max())}
+        parity["pass"] = bool(parity["o_rel_l2"] <= 5e-3 and parity["dq_rel_l2"] <= 5e-3
+                              and parity["o_max_abs"] <= 2e-2 and parity["dq_max_abs"] <= 2e-2)
+
+    out = {
+        "metric": "LastKV chunk attention fwd+bwd TFLOP/s + % bf16 MFMA peak (blend, history of 2M positions)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "history_P": P, "chunk_C": C, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d_qk,
+                   "chunk": w.chunk, "flops_per_step": flops_step},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity, "kernels": kernels,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if (parity is None or parity["pass"]) else 1
 
 
 def run_latent(a, w) -> int:

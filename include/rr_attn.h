@@ -93,7 +93,8 @@ extern "C" {
 
 /* Problem description shared by rr_attn_fwd / rr_attn_bwd / rr_workspace_bytes. */
 typedef struct rr_problem {
-  int64_t P;        /* resident prompt positions, >= 1                                  */
+  int64_t P;        /* resident prompt positions, >= 0 (0: no resident keys, the rows
+                       attend to their own causal keys only; k_p / v_p may be NULL)     */
   int64_t chunk;    /* prompt chunk length: the prompt is split into ceil(P/chunk)
                        contiguous chunks, each with its own softmax statistics; >= 1     */
   int32_t R_max;    /* row stride of the per-response tensors, >= 1                     */
@@ -239,16 +240,54 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv,
  *   q, d_o      [K][R][Hq][d] (problem dtype), the rows of rr_attn_bwd
  *   o, lse      the forward's fp32 outputs (global statistics; a caller holding one shard
  *               of the prompt passes the merged ones and gets its shard's gradients)
- *   dk_p, dv_p  outputs [P][Hkv][d] fp32, device; every position is written (=) or
- *               added to (+=, accumulate = 1), e.g. across the members of a group
+ *   key_lo, key_hi  the resident positions [key_lo, key_hi) whose gradients are formed,
+ *               0 <= key_lo <= key_hi <= P (the whole prompt: 0, P)
+ *   dk_p, dv_p  outputs [key_hi - key_lo][Hkv][d] fp32, device, row j - key_lo for
+ *               position j; every row is written (=) or added to (+=, accumulate = 1),
+ *               e.g. across the members of a group
  *   ws          workspace of rr_workspace_bytes(p, RR_OP_PROMPT_GRADS) bytes: the rows of
  *               each KV head repacked contiguously, with their lse and D
  * Dense pages only (latent = 0; RR_E_UNSUPPORTED otherwise); d_qk = d_v in {64, 128}.
  */
 int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
                          const int32_t* r_len, const float* o, const float* lse, const void* d_o,
-                         float* dk_p, float* dv_p, int32_t accumulate, void* ws, size_t ws_bytes,
-                         void* stream);
+                         int64_t key_lo, int64_t key_hi, float* dk_p, float* dv_p,
+                         int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rr_lastkv_blend - LastKV previous-chunk blending, the pre-step of a chunk's attention.
+ *
+ * Source: zefan-cai.github.io/en/blog/lastkv-rl ("In RL, Does the Trainer Evaluate the
+ * Policy That Generated the Rollout?"), section "LastKV: making recurrence boundaries part
+ * of the policy": chunk c of layer l attends to the last-layer K/V of completed chunks
+ * plus its own per-layer K/V (causal); with previous-chunk blending the chunk c-1 enters
+ * as x~ = (1 - alpha_{l,g}) x^l_{c-1} + alpha_{l,g} x^L_{c-1}, one gate per layer and KV
+ * head.  A caller lays out the resident history of chunk c as [x^L of chunks < c-1; x~ of
+ * chunk c-1] (P = c * C positions), passes the chunk's rows as the response (K/V causal),
+ * and runs rr_attn_fwd / rr_attn_bwd; rr_attn_prompt_grads over the key range of x~ gives
+ * d x~, which rr_lastkv_blend_bwd takes back to the two K/V sources and the gate.
+ *
+ *   out[r][g][e] = (1 - alpha[g]) x_layer[r][g][e] + alpha[g] x_last[r][g][e]
+ * in fp32, stored in `dtype` (bf16: round to nearest even).  Apply once to K, once to V.
+ *   rows                    positions of the chunk, >= 0
+ *   Hkv, d                  KV heads, head dim (a multiple of 8)
+ *   alpha                   device [Hkv] fp32 gates of this layer
+ *   x_layer, x_last, x_out  device [rows][Hkv][d] dtype, 16-byte aligned; x_out may alias
+ *                           neither input
+ */
+int rr_lastkv_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                    const void* x_layer, const void* x_last, void* x_out, void* stream);
+
+/*
+ * rr_lastkv_blend_bwd - gradients of rr_lastkv_blend from d_out [rows][Hkv][d] fp32:
+ *   d_layer = (1 - alpha) d_out,  d_last = alpha d_out,
+ *   d_alpha[g] = sum over rows and dims of (x_last - x_layer) d_out  (fixed-order sum).
+ * d_layer, d_last: device [rows][Hkv][d] fp32, either may be NULL (not formed); d_alpha:
+ * device [Hkv] fp32.  accumulate 0: written; 1: added.
+ */
+int rr_lastkv_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                        const void* x_layer, const void* x_last, const float* d_out, float* d_layer,
+                        float* d_last, float* d_alpha, int32_t accumulate, void* stream);
 
 /* Update-boundary accumulator for G serially replayed members.
    Source: networkfinds.com/long-context-rl-is-a-state-lifetime-problem, sections

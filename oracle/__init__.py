@@ -20,4 +20,4 @@ other than itself (torch's CPU fp64 scaled_dot_product_attention and autograd, f
 differences, closed forms, brute-force enumeration, hand-derived fixtures under
 tests/golden/).  No function here is "parity unpinned".
 """
-from . import dense, sparse  # noqa: F401
+from . import dense, lastkv, sparse  # noqa: F401

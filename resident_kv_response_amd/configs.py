@@ -72,7 +72,14 @@ LATENT_P1M = Workload("bf16_latent_P1048576_R4096_top2048", P=1048576, R=4096, H
                       d_qk=576, d_v=512, chunk=65536, block=2048, dtype="bf16", seed=1005,
                       topk=2048, idx_dim=128, latent=True)
 
-ALL = [TINY_F32, GQA_P128K, SHARE_P256K, FULL_P2M, LATENT_P1M]
+# LastKV chunk recurrence (zefan-cai.github.io/en/blog/lastkv-rl, section "LastKV: making
+# recurrence boundaries part of the policy"): one layer's current chunk of R = 8192
+# positions after P = 2,097,152 positions of history (256 completed chunks: last-layer K/V
+# of the older ones, the blended previous chunk), the 2M configuration's heads.
+LASTKV_P2M = Workload("bf16_lastkv_P2097152_C8192", P=2097152, R=8192, Hq=24, Hkv=4, d_qk=128,
+                      d_v=128, chunk=131072, block=2048, dtype="bf16", seed=1006)
+
+ALL = [TINY_F32, GQA_P128K, SHARE_P256K, FULL_P2M, LATENT_P1M, LASTKV_P2M]
 BY_NAME = {w.name: w for w in ALL}
 
 

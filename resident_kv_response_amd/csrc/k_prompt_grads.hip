@@ -268,9 +268,10 @@ __device__ __forceinline__ void pg_issue_stats(uint32_t tile_lds, const char* ba
 
 }  // namespace
 
+// Keys [key_lo, key_lo + n_keys) of the resident K/V; outputs indexed from key_lo.
 template <int D>
 __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
-    PgGeom pg, int64_t P, int Hkv, float tau, float c2, const uint16_t* __restrict__ k_p,
+    PgGeom pg, int64_t key_lo, int64_t n_keys, int Hkv, float tau, float c2, const uint16_t* __restrict__ k_p,
     const uint16_t* __restrict__ v_p, const uint16_t* __restrict__ qs, const uint16_t* __restrict__ os,
     const float* __restrict__ sts, float* __restrict__ dk_p, float* __restrict__ dv_p, int accumulate) {
   using C = PgCfg<D>;
@@ -293,19 +294,20 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
   char* const OT[4] = {ot0, ot1, ot2, ot3};
   float* const SB[4] = {sb0, sb1, sb2, sb3};
 
-  const int64_t n_kt = (P + C::KEYS - 1) / C::KEYS;
+  const int64_t n_kt = (n_keys + C::KEYS - 1) / C::KEYS;
   const int64_t idx = xcd_work_index((int64_t)Hkv * n_kt);
   if (idx < 0) return;
   const int64_t kt = idx % n_kt;
   const int gh = (int)(idx / n_kt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const int64_t key = kt * C::KEYS + wave * 32 + col;
-  const bool kvalid = key < P;
+  const int64_t key = kt * C::KEYS + wave * 32 + col;   // relative to key_lo
+  const bool kvalid = key < n_keys;
 
   // this wave's K and V rows (B operands): key `key`, dims 16 ks + 8 hl .. +8
   bf16x8 kf[KS], vf[KS];
-  const int64_t kvrow = (kvalid ? key : 0) * Hkv + gh;
+  const int64_t kvrow = (key_lo + (kvalid ? key : 0)) * Hkv + gh;   // resident row
+  const int64_t outrow = (kvalid ? key : 0) * Hkv + gh;             // output row
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(k_p + kvrow * D + ks * 16 + hl * 8)
@@ -429,8 +431,8 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
   wait_vmcnt0();
 
   if (!kvalid) return;
-  float* dkq = dk_p + kvrow * D;
-  float* dvq = dv_p + kvrow * D;
+  float* dkq = dk_p + outrow * D;
+  float* dvq = dv_p + outrow * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -461,7 +463,8 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
 // 64 / (D / 64) keys of one KV head, each key split over D / 64 threads (64 dims each, dot
 // products combined across the halves).  Stream rows are staged 16 at a time in LDS.
 template <int D>
-__global__ __launch_bounds__(64) void prompt_dkdv_f32(PgGeom pg, int64_t P, int Hkv, float tau, float c2,
+__global__ __launch_bounds__(64) void prompt_dkdv_f32(PgGeom pg, int64_t key_lo, int64_t n_keys, int Hkv,
+                                                      float tau, float c2,
                                                       const float* __restrict__ k_p,
                                                       const float* __restrict__ v_p,
                                                       const float* __restrict__ qs,
@@ -471,14 +474,15 @@ __global__ __launch_bounds__(64) void prompt_dkdv_f32(PgGeom pg, int64_t P, int 
                                                       int accumulate) {
   constexpr int SPLIT = D / 64, KEYS = 64 / SPLIT, ROWS = 16;
   __shared__ float qrow[ROWS][D], orow[ROWS][D], l2s[ROWS], nds[ROWS];
-  const int64_t n_kt = (P + KEYS - 1) / KEYS;
+  const int64_t n_kt = (n_keys + KEYS - 1) / KEYS;
   const int64_t kt = blockIdx.x % n_kt;
   const int gh = (int)(blockIdx.x / n_kt);
   const int t = threadIdx.x;
   const int part = t / KEYS;   // which 64 dims
-  const int64_t key = kt * KEYS + t % KEYS;
-  const bool kvalid = key < P;
-  const int64_t kvrow = (kvalid ? key : 0) * Hkv + gh;
+  const int64_t key = kt * KEYS + t % KEYS;   // relative to key_lo
+  const bool kvalid = key < n_keys;
+  const int64_t kvrow = (key_lo + (kvalid ? key : 0)) * Hkv + gh;
+  const int64_t outrow = (kvalid ? key : 0) * Hkv + gh;
   float kk[64], vv[64], dk[64], dv[64];
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
@@ -525,7 +529,7 @@ __global__ __launch_bounds__(64) void prompt_dkdv_f32(PgGeom pg, int64_t P, int 
   if (!kvalid) return;
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
-    const int64_t at = kvrow * D + part * 64 + e;
+    const int64_t at = outrow * D + part * 64 + e;
     const float a = dk[e] * tau, b = dv[e];
     dk_p[at] = accumulate ? dk_p[at] + a : a;
     dv_p[at] = accumulate ? dv_p[at] + b : b;
@@ -554,30 +558,32 @@ hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void
 }
 
 hipError_t launch_prompt_dkdv(const Geom& g, const PgGeom& pg, int dtype, const void* k_p, const void* v_p,
-                              const void* qs, const void* os, const float* sts, float* dk_p, float* dv_p,
-                              int accumulate, hipStream_t s) {
+                              const void* qs, const void* os, const float* sts, int64_t key_lo, int64_t key_hi,
+                              float* dk_p, float* dv_p, int accumulate, hipStream_t s) {
+  const int64_t n_keys = key_hi - key_lo;
+  if (n_keys <= 0) return hipSuccess;
   if (dtype == RR_BF16) {
-    const int64_t n = (int64_t)g.Hkv * ((g.P + PgCfg<128>::KEYS - 1) / PgCfg<128>::KEYS);
+    const int64_t n = (int64_t)g.Hkv * ((n_keys + PgCfg<128>::KEYS - 1) / PgCfg<128>::KEYS);
     const dim3 grid((unsigned)xcd_grid(n)), block(64 * PgCfg<128>::WAVES);
     const uint16_t *kp = (const uint16_t*)k_p, *vp = (const uint16_t*)v_p;
     const uint16_t *q16 = (const uint16_t*)qs, *o16 = (const uint16_t*)os;
     if (g.dqk == 64)
-      hipLaunchKernelGGL(prompt_dkdv_bf16<64>, grid, block, 0, s, pg, g.P, g.Hkv, g.tau, g.c2, kp, vp, q16, o16,
-                         sts, dk_p, dv_p, accumulate);
+      hipLaunchKernelGGL(prompt_dkdv_bf16<64>, grid, block, 0, s, pg, key_lo, n_keys, g.Hkv, g.tau, g.c2, kp, vp,
+                         q16, o16, sts, dk_p, dv_p, accumulate);
     else
-      hipLaunchKernelGGL(prompt_dkdv_bf16<128>, grid, block, 0, s, pg, g.P, g.Hkv, g.tau, g.c2, kp, vp, q16, o16,
-                         sts, dk_p, dv_p, accumulate);
+      hipLaunchKernelGGL(prompt_dkdv_bf16<128>, grid, block, 0, s, pg, key_lo, n_keys, g.Hkv, g.tau, g.c2, kp, vp,
+                         q16, o16, sts, dk_p, dv_p, accumulate);
   } else {
     const float *kp = (const float*)k_p, *vp = (const float*)v_p;
     const float *q32 = (const float*)qs, *o32 = (const float*)os;
     if (g.dqk == 64) {
-      const int64_t n = (int64_t)g.Hkv * ((g.P + 63) / 64);
-      hipLaunchKernelGGL(prompt_dkdv_f32<64>, dim3((unsigned)n), dim3(64), 0, s, pg, g.P, g.Hkv, g.tau, g.c2, kp,
-                         vp, q32, o32, sts, dk_p, dv_p, accumulate);
+      const int64_t n = (int64_t)g.Hkv * ((n_keys + 63) / 64);
+      hipLaunchKernelGGL(prompt_dkdv_f32<64>, dim3((unsigned)n), dim3(64), 0, s, pg, key_lo, n_keys, g.Hkv, g.tau,
+                         g.c2, kp, vp, q32, o32, sts, dk_p, dv_p, accumulate);
     } else {
-      const int64_t n = (int64_t)g.Hkv * ((g.P + 31) / 32);
-      hipLaunchKernelGGL(prompt_dkdv_f32<128>, dim3((unsigned)n), dim3(64), 0, s, pg, g.P, g.Hkv, g.tau, g.c2, kp,
-                         vp, q32, o32, sts, dk_p, dv_p, accumulate);
+      const int64_t n = (int64_t)g.Hkv * ((n_keys + 31) / 32);
+      hipLaunchKernelGGL(prompt_dkdv_f32<128>, dim3((unsigned)n), dim3(64), 0, s, pg, key_lo, n_keys, g.Hkv, g.tau,
+                         g.c2, kp, vp, q32, o32, sts, dk_p, dv_p, accumulate);
     }
   }
   return hipGetLastError();

@@ -73,12 +73,21 @@ hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, fl
 
 // Full-sequence differential mode (k_prompt_grads.hip): pack the rows of each KV head into
 // the prompt-gradient stream (qs, os: [Hkv][n_rows][d]; sts: per 64-row stage lse*log2(e)
-// then -D), then dk_p, dv_p (= or +=) over every stream row.
+// then -D), then dk_p, dv_p of resident keys [key_lo, key_hi) (= or +=) over every stream
+// row.
 hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void* q, const float* o,
                           const float* lse, const void* d_o, void* qs, void* os, float* sts, hipStream_t s);
 hipError_t launch_prompt_dkdv(const Geom& g, const PgGeom& pg, int dtype, const void* k_p, const void* v_p,
-                              const void* qs, const void* os, const float* sts, float* dk_p, float* dv_p,
-                              int accumulate, hipStream_t s);
+                              const void* qs, const void* os, const float* sts, int64_t key_lo, int64_t key_hi,
+                              float* dk_p, float* dv_p, int accumulate, hipStream_t s);
+
+// LastKV previous-chunk blending (k_lastkv.hip): x_out = (1 - alpha_g) x_layer + alpha_g x_last
+// over [rows][Hkv][d]; and its backward (d_layer, d_last optional; d_alpha [Hkv]).
+hipError_t launch_lastkv_blend(int64_t rows, int Hkv, int d, int dtype, const float* alpha, const void* x_layer,
+                               const void* x_last, void* x_out, hipStream_t s);
+hipError_t launch_lastkv_blend_bwd(int64_t rows, int Hkv, int d, int dtype, const float* alpha,
+                                   const void* x_layer, const void* x_last, const float* d_out, float* d_layer,
+                                   float* d_last, float* d_alpha, int accumulate, hipStream_t s);
 
 // acc[e] += scale * g[e], e < n.
 hipError_t launch_axpy(float* acc, const float* g, int64_t n, float scale, hipStream_t s);

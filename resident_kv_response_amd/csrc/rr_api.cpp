@@ -265,10 +265,12 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
 }
 
 int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q, const int32_t* r_len,
-                         const float* o, const float* lse, const void* d_o, float* dk_p, float* dv_p,
-                         int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+                         const float* o, const float* lse, const void* d_o, int64_t key_lo, int64_t key_hi,
+                         float* dk_p, float* dv_p, int32_t accumulate, void* ws, size_t ws_bytes,
+                         void* stream) {
   clear_error();
-  int rc = validate_prompt_grads(p, kv, q, r_len, o, lse, d_o, dk_p, dv_p, accumulate, ws, ws_bytes);
+  int rc = validate_prompt_grads(p, kv, q, r_len, o, lse, d_o, key_lo, key_hi, dk_p, dv_p, accumulate, ws,
+                                 ws_bytes);
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
@@ -283,10 +285,38 @@ int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void*
   if ((e = timed("pg_pack", s, [&] { return launch_pg_pack(g, pg, p->dtype, q, o, lse, d_o, qs, os, sts, s); })))
     return hip_fail(e, "pg_pack");
   if ((e = timed("prompt_dkdv", s, [&] {
-         return launch_prompt_dkdv(g, pg, p->dtype, kv->k_p, kv->v_p, qs, os, sts, dk_p, dv_p, accumulate, s);
+         return launch_prompt_dkdv(g, pg, p->dtype, kv->k_p, kv->v_p, qs, os, sts, key_lo, key_hi, dk_p, dv_p,
+                                   accumulate, s);
        })))
     return hip_fail(e, "prompt_dkdv");
   return RR_OK;
+}
+
+int rr_lastkv_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha, const void* x_layer,
+                    const void* x_last, void* x_out, void* stream) {
+  clear_error();
+  int rc = validate_blend(rows, Hkv, d, dtype, alpha, x_layer, x_last, x_out);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("lastkv_blend", s, [&] {
+    return launch_lastkv_blend(rows, Hkv, d, dtype, alpha, x_layer, x_last, x_out, s);
+  });
+  return e != hipSuccess ? hip_fail(e, "lastkv_blend") : RR_OK;
+}
+
+int rr_lastkv_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                        const void* x_layer, const void* x_last, const float* d_out, float* d_layer,
+                        float* d_last, float* d_alpha, int32_t accumulate, void* stream) {
+  clear_error();
+  int rc = validate_blend_bwd(rows, Hkv, d, dtype, alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha,
+                              accumulate);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("lastkv_blend_bwd", s, [&] {
+    return launch_lastkv_blend_bwd(rows, Hkv, d, dtype, alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha,
+                                   accumulate, s);
+  });
+  return e != hipSuccess ? hip_fail(e, "lastkv_blend_bwd") : RR_OK;
 }
 
 int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version, const float* const* grads,

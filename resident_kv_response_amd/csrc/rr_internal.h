@@ -59,11 +59,16 @@ struct PgGeom {
   int32_t off[RR_MAX_K + 1];
 };
 PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len);
+int validate_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                   const void* x_layer, const void* x_last, const void* x_out);
+int validate_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                       const void* x_layer, const void* x_last, const float* d_out, const float* d_layer,
+                       const float* d_last, const float* d_alpha, int32_t accumulate);
 size_t ws_prompt_bytes(const rr_problem* p);
 int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
                           const int32_t* r_len, const float* o, const float* lse, const void* d_o,
-                          const float* dk_p, const float* dv_p, int32_t accumulate, const void* ws,
-                          size_t ws_bytes);
+                          int64_t key_lo, int64_t key_hi, const float* dk_p, const float* dv_p,
+                          int32_t accumulate, const void* ws, size_t ws_bytes);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

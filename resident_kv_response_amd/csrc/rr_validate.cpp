@@ -27,7 +27,7 @@ const char* last_error() { return g_err; }
 
 int validate_problem(const rr_problem* p) {
   if (!p) return set_error(RR_E_NULL, "problem is NULL");
-  if (p->P < 1) return set_error(RR_E_SHAPE, "P must be >= 1 (got %lld)", (long long)p->P);
+  if (p->P < 0) return set_error(RR_E_SHAPE, "P must be >= 0 (got %lld)", (long long)p->P);
   if (p->R_max < 1) return set_error(RR_E_SHAPE, "R_max must be >= 1 (got %d)", p->R_max);
   if (p->K < 1 || p->K > RR_MAX_K)
     return set_error(RR_E_SHAPE, "K must be in [1, %d] (got %d)", RR_MAX_K, p->K);
@@ -134,7 +134,8 @@ static int check_r_len(const rr_problem* p, const int32_t* r_len) {
 
 static int check_resident(const rr_problem* p, const rr_resident* kv) {
   if (!kv) return set_error(RR_E_NULL, "resident is NULL");
-  if (!kv->k_p || (!kv->v_p && !p->latent)) return set_error(RR_E_NULL, "resident k_p / v_p is NULL");
+  if (p->P > 0 && (!kv->k_p || (!kv->v_p && !p->latent)))
+    return set_error(RR_E_NULL, "resident k_p / v_p is NULL");
   if (kv->P != p->P)
     return set_error(RR_E_SHAPE, "resident P (%lld) != problem P (%lld)", (long long)kv->P,
                      (long long)p->P);
@@ -206,8 +207,8 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
 
 int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q,
                           const int32_t* r_len, const float* o, const float* lse, const void* d_o,
-                          const float* dk_p, const float* dv_p, int32_t accumulate, const void* ws,
-                          size_t ws_bytes) {
+                          int64_t key_lo, int64_t key_hi, const float* dk_p, const float* dv_p,
+                          int32_t accumulate, const void* ws, size_t ws_bytes) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (p->latent) return set_error(RR_E_UNSUPPORTED, "prompt gradients are built for dense K/V pages");
@@ -216,6 +217,9 @@ int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void
     return set_error(RR_E_NULL, "q / o / lse / d_o / dk_p / dv_p is NULL");
   if ((rc = check_r_len(p, r_len))) return rc;
   if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
+  if (key_lo < 0 || key_lo > key_hi || key_hi > p->P)
+    return set_error(RR_E_SHAPE, "key range [%lld, %lld) outside [0, P=%lld]", (long long)key_lo,
+                     (long long)key_hi, (long long)p->P);
   if ((rc = check_aligned("q / k_p / v_p / o / d_o / dk_p / dv_p / ws",
                           {q, kv->k_p, kv->v_p, o, d_o, dk_p, dv_p, ws})))
     return rc;
@@ -240,6 +244,35 @@ PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len) {
   for (int k = p->K; k <= RR_MAX_K; ++k) pg.off[k] = (int32_t)at;
   pg.n_rows = (int32_t)at;
   return pg;
+}
+
+static int blend_shape(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype) {
+  if (rows < 0 || Hkv < 1 || d < 8 || d % 8 != 0 || d > 4096)
+    return set_error(RR_E_SHAPE, "blend needs rows >= 0, Hkv >= 1, d a multiple of 8 in [8, 4096] "
+                     "(got %lld, %d, %d)", (long long)rows, Hkv, d);
+  if (dtype != RR_F32 && dtype != RR_BF16) return set_error(RR_E_SHAPE, "dtype must be RR_F32 or RR_BF16");
+  if (rows * Hkv * (int64_t)d > ((int64_t)1 << 40)) return set_error(RR_E_SHAPE, "blend too large");
+  return RR_OK;
+}
+
+int validate_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                   const void* x_layer, const void* x_last, const void* x_out) {
+  int rc = blend_shape(rows, Hkv, d, dtype);
+  if (rc) return rc;
+  if (!alpha || ((!x_layer || !x_last || !x_out) && rows > 0))
+    return set_error(RR_E_NULL, "alpha / x_layer / x_last / x_out is NULL");
+  return check_aligned("x_layer / x_last / x_out", {x_layer, x_last, x_out});
+}
+
+int validate_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
+                       const void* x_layer, const void* x_last, const float* d_out, const float* d_layer,
+                       const float* d_last, const float* d_alpha, int32_t accumulate) {
+  int rc = blend_shape(rows, Hkv, d, dtype);
+  if (rc) return rc;
+  if (!alpha || !d_alpha || ((!x_layer || !x_last || !d_out) && rows > 0))
+    return set_error(RR_E_NULL, "alpha / d_alpha / x_layer / x_last / d_out is NULL");
+  if (accumulate != 0 && accumulate != 1) return set_error(RR_E_SHAPE, "accumulate must be 0 or 1");
+  return check_aligned("x_layer / x_last / d_out / d_layer / d_last", {x_layer, x_last, d_out, d_layer, d_last});
 }
 
 int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,

@@ -26,7 +26,7 @@ RR_MAX_K, RR_MAX_ACC = 64, 8
 RR_FLAG_SHARD_NO_RESPONSE = 1
 
 EXPORTS = ["rr_workspace_bytes", "rr_num_parts", "rr_attn_fwd", "rr_lse_merge", "rr_attn_bwd",
-           "rr_attn_prompt_grads", "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
+           "rr_attn_prompt_grads", "rr_lastkv_blend", "rr_lastkv_blend_bwd", "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
            "rr_profile_end"]
 
 
@@ -84,8 +84,13 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         L.rr_attn_bwd.restype = ctypes.c_int
         L.rr_attn_prompt_grads.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp,
-                                           ctypes.POINTER(i32), vp, vp, vp, vp, vp, i32, vp, sz, vp]
+                                           ctypes.POINTER(i32), vp, vp, vp, i64, i64, vp, vp, i32, vp, sz,
+                                           vp]
         L.rr_attn_prompt_grads.restype = ctypes.c_int
+        L.rr_lastkv_blend.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.rr_lastkv_blend.restype = ctypes.c_int
+        L.rr_lastkv_blend_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+        L.rr_lastkv_blend_bwd.restype = ctypes.c_int
         L.rr_grad_accum.argtypes = [ctypes.POINTER(CAccum), i32, ctypes.c_uint64,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.c_float, vp]
         L.rr_grad_accum.restype = ctypes.c_int
@@ -207,14 +212,40 @@ def rr_attn_bwd(p: Problem, kv: CResident, q, k_r, v_r, r_len, o, lse, d_o, dq, 
 
 
 def rr_attn_prompt_grads(p: Problem, kv: CResident, q, r_len, o, lse, d_o, dk_p, dv_p,
-                         accumulate: int = 0, ws=None, stream=None) -> None:
-    """Full-sequence differential mode: dk_p, dv_p [P][Hkv][d] fp32, the prompt-side term
+                         accumulate: int = 0, key_range=None, ws=None, stream=None) -> None:
+    """Full-sequence differential mode: dk_p, dv_p [key_hi - key_lo][Hkv][d] fp32 of the
+    resident positions in key_range (default: the whole prompt), the prompt-side term
     that rr_attn_bwd drops."""
     cp = p.c()
+    lo, hi = key_range if key_range is not None else (0, p.P)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _r_len(r_len),
-                                      _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dk_p), _ptr(dv_p),
-                                      int(accumulate), _ptr(ws), nbytes, _stream(stream)))
+                                      _ptr(o), _ptr(lse), _ptr(d_o), int(lo), int(hi), _ptr(dk_p),
+                                      _ptr(dv_p), int(accumulate), _ptr(ws), nbytes, _stream(stream)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RR_BF16
+    if t.dtype == torch.float32:
+        return RR_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def rr_lastkv_blend(alpha, x_layer, x_last, x_out, stream=None) -> None:
+    """x_out = (1 - alpha_g) x_layer + alpha_g x_last over [rows][Hkv][d] (LastKV
+    previous-chunk blending)."""
+    rows, Hkv, d = x_layer.shape
+    _check(lib().rr_lastkv_blend(rows, Hkv, d, _dtype_code(x_layer), _ptr(alpha), _ptr(x_layer),
+                                 _ptr(x_last), _ptr(x_out), _stream(stream)))
+
+
+def rr_lastkv_blend_bwd(alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha, accumulate: int = 0,
+                        stream=None) -> None:
+    rows, Hkv, d = x_layer.shape
+    _check(lib().rr_lastkv_blend_bwd(rows, Hkv, d, _dtype_code(x_layer), _ptr(alpha), _ptr(x_layer),
+                                     _ptr(x_last), _ptr(d_out), _ptr(d_layer), _ptr(d_last), _ptr(d_alpha),
+                                     int(accumulate), _stream(stream)))
 
 
 class Accum:

@@ -19,7 +19,9 @@ import numpy as np
 
 from .configs import Workload
 
-STREAMS = ["q", "k_p", "v_p", "k_r", "v_r", "d_o", "q_idx", "k_idx", "r_len", "rows"]
+# new names go at the end: a stream's seed depends on its index only
+STREAMS = ["q", "k_p", "v_p", "k_r", "v_r", "d_o", "q_idx", "k_idx", "r_len", "rows", "k_layer", "v_layer",
+           "alpha"]
 BLOCK = 1 << 22
 
 
@@ -110,6 +112,36 @@ def member(w: Workload, g: int = 0, R: Optional[int] = None) -> Dict[str, np.nda
         out["k_r"] = normal(seed, "k_r", (R, w.Hkv, w.d_qk), w.dtype)
         out["v_r"] = normal(seed, "v_r", (R, w.Hkv, w.d_v), w.dtype)
     return out
+
+
+def lastkv_sequence(seed: int, N: int, Hq: int, Hkv: int, d: int, dtype: str) -> Dict[str, np.ndarray]:
+    """Inputs of one layer of a LastKV chunk recurrence over N positions: Q and dO
+    [N][Hq][d], the layer's own K/V and the last layer's K/V [N][Hkv][d] (N(0,1), stored in
+    `dtype`), and the layer's gates alpha [Hkv] (fp32, uniform in [0.05, 0.95])."""
+    g = np.random.Generator(np.random.PCG64(_stream_seed(seed, "alpha")))
+    return {"q": normal(seed, "q", (N, Hq, d), dtype), "d_o": normal(seed, "d_o", (N, Hq, d), dtype),
+            "k_layer": normal(seed, "k_layer", (N, Hkv, d), dtype),
+            "v_layer": normal(seed, "v_layer", (N, Hkv, d), dtype),
+            "k_last": normal(seed, "k_p", (N, Hkv, d), dtype), "v_last": normal(seed, "v_p", (N, Hkv, d), dtype),
+            "alpha": g.uniform(0.05, 0.95, Hkv).astype(np.float32)}
+
+
+def lastkv_chunk(w: Workload) -> Dict[str, np.ndarray]:
+    """The current chunk of a LastKV workload (w.R positions, after w.P positions of
+    history): the last layer's K/V of the whole history [P][Hkv][d], this layer's K/V of the
+    previous chunk (the history's last R positions), and Q, K/V, dO of the current chunk;
+    gates alpha [Hkv]."""
+    C = w.R
+    g = np.random.Generator(np.random.PCG64(_stream_seed(w.seed, "alpha")))
+    return {"k_last": normal(w.seed, "k_p", (w.P, w.Hkv, w.d_qk), w.dtype),
+            "v_last": normal(w.seed, "v_p", (w.P, w.Hkv, w.d_v), w.dtype),
+            "k_prev_layer": normal(w.seed, "k_layer", (C, w.Hkv, w.d_qk), w.dtype),
+            "v_prev_layer": normal(w.seed, "v_layer", (C, w.Hkv, w.d_v), w.dtype),
+            "q": normal(w.seed, "q", (C, w.Hq, w.d_qk), w.dtype),
+            "k_cur": normal(w.seed, "k_r", (C, w.Hkv, w.d_qk), w.dtype),
+            "v_cur": normal(w.seed, "v_r", (C, w.Hkv, w.d_v), w.dtype),
+            "d_o": normal(w.seed, "d_o", (C, w.Hq, w.d_v), w.dtype),
+            "alpha": g.uniform(0.05, 0.95, w.Hkv).astype(np.float32)}
 
 
 def sample_rows(seed: int, R: int, n: int, block: int) -> np.ndarray:

@@ -49,7 +49,7 @@ def _fwd(p, r_len=(256,), q=FAKE, kv=None, o=FAKE, lse=FAKE, part_o=None, part_l
 
 @pytest.mark.parametrize("kw,code,frag", [
     (dict(Hq=5, Hkv=2), R.RR_E_SHAPE, "multiple"),
-    (dict(P=0), R.RR_E_SHAPE, "P must"),
+    (dict(P=-1), R.RR_E_SHAPE, "P must"),
     (dict(R_max=0), R.RR_E_SHAPE, "R_max"),
     (dict(K=0), R.RR_E_SHAPE, "K must"),
     (dict(K=65), R.RR_E_SHAPE, "K must"),
@@ -106,14 +106,18 @@ def test_prompt_grads_rejects_bad_arguments():
     p = _prob()
     kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
 
-    def call(prob=p, r_len=(256,), accumulate=0, ws=FAKE, ws_bytes=1 << 40, dk_p=FAKE, kv_=kv):
+    def call(prob=p, r_len=(256,), accumulate=0, ws=FAKE, ws_bytes=1 << 40, dk_p=FAKE, kv_=kv, keys=None):
         cp = prob.c()
         arr = (ctypes.c_int32 * len(r_len))(*r_len)
-        return L.rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv_), FAKE, arr, FAKE, FAKE, FAKE,
+        lo, hi = keys if keys is not None else (0, prob.P)
+        return L.rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv_), FAKE, arr, FAKE, FAKE, FAKE, lo, hi,
                                       dk_p, FAKE, accumulate, ws, ws_bytes, None)
 
     assert call(r_len=(257,)) == R.RR_E_SHAPE
     assert call(accumulate=2) == R.RR_E_SHAPE
+    assert call(keys=(-1, 10)) == R.RR_E_SHAPE
+    assert call(keys=(10, 9)) == R.RR_E_SHAPE
+    assert call(keys=(0, p.P + 1)) == R.RR_E_SHAPE
     assert call(dk_p=None) == R.RR_E_NULL
     assert call(dk_p=FAKE + 4) == R.RR_E_SHAPE                      # misaligned
     assert call(ws=None) == R.RR_E_WORKSPACE
@@ -245,3 +249,25 @@ def test_latent_fwd_arguments_and_workspace():
     # small rows use the exact full-row path and need no candidate buffers
     small = _latent(P=3000, R_max=96, topk=256)
     assert R.rr_workspace_bytes(small, R.RR_OP_FWD) == up(96 * 3000 * 4)
+
+
+def test_blend_rejects_bad_arguments():
+    L = R.lib()
+    assert L.rr_lastkv_blend(10, 2, 12, R.RR_BF16, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE   # d % 8
+    assert L.rr_lastkv_blend(-1, 2, 16, R.RR_BF16, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lastkv_blend(10, 2, 16, 5, FAKE, FAKE, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lastkv_blend(10, 2, 16, R.RR_BF16, None, FAKE, FAKE, FAKE, None) == R.RR_E_NULL
+    assert L.rr_lastkv_blend(10, 2, 16, R.RR_BF16, FAKE, FAKE + 2, FAKE, FAKE, None) == R.RR_E_SHAPE
+    assert L.rr_lastkv_blend_bwd(10, 2, 16, R.RR_F32, FAKE, FAKE, FAKE, FAKE, None, None, None, 0,
+                                 None) == R.RR_E_NULL                                   # d_alpha
+    assert L.rr_lastkv_blend_bwd(10, 2, 16, R.RR_F32, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 3,
+                                 None) == R.RR_E_SHAPE                                  # accumulate
+
+
+def test_empty_prompt_is_accepted_without_resident_pointers():
+    # P = 0: rows attend to their own causal keys only; k_p / v_p may be NULL
+    p = _prob(P=0)
+    assert R.rr_num_parts(p) == 1
+    kv = R.CResident(k_p=None, v_p=None, k_idx=None, P=0, version=0)
+    rc, msg = _fwd(p, kv=kv, ws=None, ws_bytes=0)
+    assert rc == R.RR_E_WORKSPACE, msg          # passes every check up to the workspace
