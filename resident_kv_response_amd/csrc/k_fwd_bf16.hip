@@ -133,8 +133,9 @@ __device__ __forceinline__ void ring_scale(f32x16 (&acc)[D / 32], float alpha) {
 // One pipelined block, laid out by hand as NSLOT slots separated by scheduling
 // barriers.  Slot i issues the LDS reads of slot i+RR_AHEAD's fragment, then the NT MFMAs
 // of its own fragment, then a fixed share of the softmax of subtile u for every tile: the
-// exponentials p = 2^(S c2 - m) against the current reference maximum m, in pairs, each
-// pair packed to bf16 and added to the lane's partial row sum ls at once.  With PV, even
+// exponentials p = 2^(S c2 - m) against the current reference maximum m, one per slot (a
+// pair in every other slot measured 0.7 % slower), each pair packed to bf16 and added to
+// the lane's partial row sum ls at the slot of its second element.  With PV, even
 // slots hold the K fragments of subtile u+1's scores and odd slots the V^T fragments of
 // subtile u-1's PV.  The caller accepts the subtile when every lane's ls is at most
 // kRingSumLimit (then every p is at most that, since all p >= 0); otherwise it redoes the
@@ -159,6 +160,7 @@ __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrag
 #pragma unroll
   for (int i = 0; i < RR_AHEAD && i < NSLOT; ++i) frag[i] = load(i);
   uint32_t w[NT][8];
+  float pe[NT][16];
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int t = 0; t < NT; ++t) ls[t] = 0.0f;
@@ -180,15 +182,21 @@ __device__ __forceinline__ void ring_block_body(const Frag<D>& fr, const FarFrag
         sn[t] = mfma32x32x16(frag[i], qf[t][ks], sn[t]);
       }
     }
-    // this slot's share of the softmax, for every tile
+    // this slot's share of the softmax, for every tile: one exponential per slot (in
+    // order), and each pair packed and summed at the slot of its second element
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (i == (e * NSLOT) / 16) {
+          pe[t][e] = fast_exp2(fmaf(s[t][e], c2, -m_run[t]));
+          asm volatile("" ::"v"(pe[t][e]));
+        }
+      }
+#pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (i == (k * NSLOT) / 8) {
-          const float p0 = fast_exp2(fmaf(s[t][2 * k], c2, -m_run[t]));
-          const float p1 = fast_exp2(fmaf(s[t][2 * k + 1], c2, -m_run[t]));
-          w[t][k] = pack_bf16x2(p0, p1);
+        if (i == ((2 * k + 1) * NSLOT) / 16) {
+          w[t][k] = pack_bf16x2(pe[t][2 * k], pe[t][2 * k + 1]);
           ls[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[t][k]), one, ls[t], false);
         }
       }
