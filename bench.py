@@ -96,8 +96,8 @@ def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
 KERNEL_SOURCES = {
     "fwd_partials": ["k_fwd_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
     "dq_partials": ["k_dq_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "dkdv": ["k_bwd_bf16.hip", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "prompt_dkdv": ["k_prompt_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "dkdv": ["k_kv_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "prompt_dkdv": ["k_kv_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
 }
 
 
@@ -273,10 +273,23 @@ def run_dense(a, w) -> int:
     for k in per_kernel_flops:
         if k in kernels:
             kernels[k]["tflops"] = round(per_kernel_flops[k] / (kernels[k]["ms_per_step"] * 1e-3) / 1e12, 2)
-    if "lse_merge" in kernels:   # bytes: read n_parts partials (O and lse), write O and lse
-        nb = sum((w.n_chunks + 1) * int(rg) * w.Hq * (w.d_v + 1) * 4 + int(rg) * w.Hq * (w.d_v + 1) * 4
-                 for rg in lens)
-        kernels["lse_merge"]["gbs"] = round(nb / (kernels["lse_merge"]["ms_per_step"] * 1e-3) / 1e9, 1)
+    # HBM-bound phases: algorithmic bytes per step / device time, against 8 TB/s
+    n_rows = float(sum(int(rg) for rg in lens)) * w.Hq    # (row, head) pairs of the group
+    hbm_bytes = {
+        # read every part's partial (O and lse), write O and lse
+        "lse_merge": n_rows * (w.n_chunks + 2) * (w.d_v + 1) * 4,
+        # read O (fp32) and dO (bf16), write D
+        "bwd_pre": n_rows * (w.d_v * 6 + 4),
+        # read every part's dQ partial, write dQ
+        "dq_reduce": n_rows * (w.n_chunks + 2) * w.d_qk * 4,
+        # read the member's dQ, dK, dV and the accumulators, write the accumulators
+        "grad_accum": 12.0 * sum(int(rg) * (w.Hq * w.d_qk + w.Hkv * (w.d_qk + w.d_v)) for rg in lens),
+    }
+    for k, nb in hbm_bytes.items():
+        if k in kernels and kernels[k]["ms_per_step"] > 0:
+            gbs = nb / (kernels[k]["ms_per_step"] * 1e-3) / 1e9
+            kernels[k]["gbs"] = round(gbs, 1)
+            kernels[k]["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 3)
 
     # CPU baseline: the oracle on the machine's host cores, bounded sample of member 0
     cpu = None

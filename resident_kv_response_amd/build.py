@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librr_attn.so")
 SOURCES = ["rr_validate.cpp", "rr_api.cpp", "k_small.hip", "k_f32.hip", "k_fwd_bf16.hip", "k_dq_bf16.hip",
-           "k_bwd_bf16.hip", "k_topk.hip", "k_sparse.hip", "k_prompt_grads.hip", "k_lastkv.hip"]
+           "k_topk.hip", "k_sparse.hip", "k_kv_grads.hip", "k_lastkv.hip"]
 ARCH = "gfx950"
 
 

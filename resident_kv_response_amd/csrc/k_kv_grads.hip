@@ -76,8 +76,9 @@ __global__ __launch_bounds__(256) void pg_pack(Geom g, PgGeom pg, const void* __
   const int n = (int)(wid % pg.n_rows);
   int k = 0;
   while (k + 1 < g.K && n >= pg.off[k + 1]) ++k;
-  const int m = n - pg.off[k];
-  const bool valid = m < g.r_len[k] * g.grp;
+  const int m = pg.m_lo + (n - pg.off[k]);   // flattened row r * grp + hh of response k
+  const int r_hi = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
+  const bool valid = m < r_hi * g.grp && m >= g.row_lo * g.grp;
   const int r = valid ? m / g.grp : 0, hh = valid ? m % g.grp : 0;
   const int64_t src = ((int64_t)k * g.R + r) * g.Hq + gh * g.grp + hh;
   const int64_t dst = (int64_t)gh * pg.n_rows + n;
@@ -458,6 +459,270 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
     }
 }
 
+// ---- response keys: the causal dK_r, dV_r of the launch's rows ------------------------------
+// One workgroup per (response k, KV head g, 128 response keys j0 ..), four waves of 32 keys,
+// over the stream rows of response k that can see a key of the tile (rows r >= j0; the
+// stream holds the launch's rows [row_lo, row_hi), so keys from row_hi on are untouched).  The
+// stages run from the response's last stream stage down to the one holding row j0, and
+// each stage's two subtiles upper first, so rows decrease along the sequence: every
+// subtile before n_full holds only rows r >= j0 + 127, which see every key of the tile
+// (the pipelined blocks, as in the prompt kernel); the rest, near the causal diagonal, run
+// unpipelined with p = 0 wherever key > row.  Results are added to dk_r, dv_r.
+template <int D>
+__global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
+    Geom g, PgGeom pg, const uint16_t* __restrict__ k_r, const uint16_t* __restrict__ v_r,
+    const uint16_t* __restrict__ qs, const uint16_t* __restrict__ os, const float* __restrict__ sts,
+    float* __restrict__ dk_r, float* __restrict__ dv_r) {
+  using C = PgCfg<D>;
+  constexpr int KS = C::KS, DT = C::DT;
+  __shared__ __attribute__((aligned(1024))) char qt0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char qt1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char qt2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char qt3[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char ot0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char ot1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char ot2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char ot3[C::TILE];
+  __shared__ __attribute__((aligned(16))) float sb0[2 * kPgStage];
+  __shared__ __attribute__((aligned(16))) float sb1[2 * kPgStage];
+  __shared__ __attribute__((aligned(16))) float sb2[2 * kPgStage];
+  __shared__ __attribute__((aligned(16))) float sb3[2 * kPgStage];
+  char* const QT[4] = {qt0, qt1, qt2, qt3};
+  char* const OT[4] = {ot0, ot1, ot2, ot3};
+  float* const SB[4] = {sb0, sb1, sb2, sb3};
+
+  // work item: (k, g) outer, key tiles inner (heaviest first); plain block order, so every
+  // XCD receives a mix of long and short tiles
+  int64_t idx = blockIdx.x;
+  int k = 0, gh = 0, kt = 0;
+  {
+    bool found = false;
+    for (int kk = 0; kk < g.K && !found; ++kk) {
+      const int kmax_k = g.r_len[kk] < g.row_hi ? g.r_len[kk] : g.row_hi;
+      const int64_t nt = (kmax_k + C::KEYS - 1) / C::KEYS;
+      if (idx < nt * g.Hkv) {
+        k = kk;
+        gh = (int)(idx / nt);
+        kt = (int)(idx % nt);
+        found = true;
+      } else {
+        idx -= nt * g.Hkv;
+      }
+    }
+    if (!found) return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;   // keys the rows can see
+  const int j0 = kt * C::KEYS;
+  const int key = j0 + wave * 32 + col;
+  const bool kvalid = key < kmax;
+  const int64_t kvrow = ((int64_t)k * g.R + (kvalid ? key : 0)) * g.Hkv + gh;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(k_r + kvrow * D + ks * 16 + hl * 8)
+                              : make_uint4(0, 0, 0, 0));
+    vf[ks] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(v_r + kvrow * D + ks * 16 + hl * 8)
+                              : make_uint4(0, 0, 0, 0));
+  }
+
+  // stream stages of response k: [0, n_seg), stage s holding flattened rows m_lo + 64 s ..;
+  // those from s0 on hold a row r >= max(j0, row_lo)
+  const int grp = g.grp;
+  const int n_seg = (pg.off[k + 1] - pg.off[k]) / C::BM;
+  const int s0 = ((j0 > g.row_lo ? j0 : g.row_lo) * grp - pg.m_lo) / C::BM;
+  const int n_stages = n_seg > s0 ? n_seg - s0 : 0;
+  const int n_sub = 2 * n_stages;
+  // subtile u of the sequence: stage n_seg - 1 - u / 2, upper half first; its first row is
+  // m = m_lo + 64 n_seg - 32 (u + 1)
+  const int m_top = pg.m_lo + C::BM * n_seg;
+  const int n_full_raw = (m_top - (j0 + C::KEYS - 1) * grp) / 32;
+  const int n_full = n_full_raw < 0 ? 0 : (n_full_raw > n_sub ? n_sub : n_full_raw);
+  const int64_t row0 = (int64_t)gh * pg.n_rows + pg.off[k];
+  const char* const qb = reinterpret_cast<const char*>(qs + row0 * D);
+  const char* const ob = reinterpret_cast<const char*>(os + row0 * D);
+  const char* const sbase =
+      reinterpret_cast<const char*>(sts + ((int64_t)gh * (pg.n_rows / C::BM) + pg.off[k] / C::BM) * 2 * kPgStage);
+  DirectLoadRows<D, C::BM, C::WAVES> dl;
+  dl.init();
+  Frag<D> fr;
+  fr.init();
+  FarFrags<D> far;
+  far.template init<true, true>(fr);
+
+  // sequence stage t is stream stage n_seg - 1 - t
+  auto issue_stage = [&](int b, int t) {
+    const int st = n_seg - 1 - t;
+    const int64_t off = (int64_t)st * C::TILE;
+    dl.issue(lds_addr(QT[b]), qb + off, C::BM, (uint32_t)(D * 2));
+    dl.issue(lds_addr(OT[b]), ob + off, C::BM, (uint32_t)(D * 2));
+    pg_issue_stats(lds_addr(SB[b]), sbase + (int64_t)st * (2 * kPgStage * 4));
+  };
+  auto issue_any = [&](int t) {
+    switch (t & 3) {
+      case 0: issue_stage(0, t); break;
+      case 1: issue_stage(1, t); break;
+      case 2: issue_stage(2, t); break;
+      default: issue_stage(3, t); break;
+    }
+  };
+  int entered = -1;
+  auto enter_stage = [&](int t) {
+    if (t + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+    __syncthreads();
+    if (t + 2 < n_stages) issue_any(t + 2);
+    entered = t;
+  };
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[dt][i] = dv[dt][i] = 0.0f;
+  const float c2 = g.c2;
+
+  if (n_stages > 0) {
+    issue_any(0);
+    if (n_stages > 1) issue_any(1);
+    enter_stage(0);
+  }
+
+  if (n_full > 0) {
+    float l2[16];
+    f32x16 ndv, s, dp;
+    pg_stats(SB[0], 1, l2, ndv);
+    pg_scores<D>(fr, far, QT[0], OT[0], 1, kf, vf, ndv, s, dp);   // subtile 0: stage 0, upper half
+    bf16x8 pp[2], dsp[2];
+
+    // Block B(u), u = J mod 8 (as in the prompt kernel, with the halves of a stage in
+    // upper-first order).  The last block also forms S, dP of subtile n_full, never used.
+    auto block = [&](auto jc, auto pc, int u) {
+      constexpr int J = decltype(jc)::value;
+      constexpr bool PREV = decltype(pc)::value;
+      constexpr int SX = ((J + 7) >> 1) & 3, SUBX = 1 - ((J + 7) & 1);   // subtile u-1
+      constexpr int SY = ((J + 1) >> 1) & 3, SUBY = 1 - ((J + 1) & 1);   // subtile u+1
+      constexpr int SN = (SY + 2) & 3;
+      if (J & 1) {   // subtile u+1 starts sequence stage (u+1)/2
+        const int t = (u + 1) >> 1;
+        if (t + 1 < n_stages) wait_vmcnt_n<C::LOADS>(); else wait_vmcnt0();
+        __syncthreads();
+        if (t + 2 < n_stages) issue_stage(SN, t + 2);
+        entered = t;
+      }
+      float l2n[16];
+      f32x16 ndvn;
+      pg_stats(SB[SY], SUBY, l2n, ndvn);
+      bf16x8 pn[2], dsn[2];
+      pg_block_body<D, PREV>(fr, far, QT[SX], OT[SX], SUBX, QT[SY], OT[SY], SUBY, kf, vf, c2, l2, ndvn, pp,
+                             dsp, dk, dv, s, dp, pn, dsn);
+      pin_operands(pn, c2);
+      pin_operands(dsn, c2);
+      pp[0] = pn[0];
+      pp[1] = pn[1];
+      dsp[0] = dsn[0];
+      dsp[1] = dsn[1];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) l2[e] = l2n[e];
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    block(std::integral_constant<int, 0>{}, F{}, 0);
+    int u = 1;
+    for (; u + 8 <= n_full; u += 8) {
+      block(std::integral_constant<int, 1>{}, T{}, u);
+      block(std::integral_constant<int, 2>{}, T{}, u + 1);
+      block(std::integral_constant<int, 3>{}, T{}, u + 2);
+      block(std::integral_constant<int, 4>{}, T{}, u + 3);
+      block(std::integral_constant<int, 5>{}, T{}, u + 4);
+      block(std::integral_constant<int, 6>{}, T{}, u + 5);
+      block(std::integral_constant<int, 7>{}, T{}, u + 6);
+      block(std::integral_constant<int, 0>{}, T{}, u + 7);
+    }
+    if (u < n_full) block(std::integral_constant<int, 1>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 2>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 3>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 4>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 5>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 6>{}, T{}, u++);
+    if (u < n_full) block(std::integral_constant<int, 7>{}, T{}, u++);
+    const int ul = n_full - 1;
+    const int subl = 1 - (ul & 1);
+    switch ((ul >> 1) & 3) {
+      case 0: pg_dkdv<D>(fr, far, QT[0], OT[0], subl, pp, dsp, dk, dv); break;
+      case 1: pg_dkdv<D>(fr, far, QT[1], OT[1], subl, pp, dsp, dk, dv); break;
+      case 2: pg_dkdv<D>(fr, far, QT[2], OT[2], subl, pp, dsp, dk, dv); break;
+      default: pg_dkdv<D>(fr, far, QT[3], OT[3], subl, pp, dsp, dk, dv); break;
+    }
+  }
+
+  // Subtiles near the causal diagonal: p = 0 wherever key > row.
+  const float inv_grp = 1.0f / (float)grp;
+  for (int u = n_full; u < n_sub; ++u) {
+    const int t = u >> 1;
+    while (entered < t) enter_stage(entered + 1);
+    const int b = t & 3;
+    const int sub = 1 - (u & 1);
+    const int m_first = m_top - 32 * (u + 1);   // first flattened row of the subtile
+    const char* const qt = b == 0 ? qt0 : b == 1 ? qt1 : b == 2 ? qt2 : qt3;
+    const char* const ot = b == 0 ? ot0 : b == 1 ? ot1 : b == 2 ? ot2 : ot3;
+    const float* const sb = b == 0 ? sb0 : b == 1 ? sb1 : b == 2 ? sb2 : sb3;
+    float l2[16];
+    f32x16 ndv, s, dp;
+    pg_stats(sb, sub, l2, ndv);
+    pg_scores<D>(fr, far, qt, ot, sub, kf, vf, ndv, s, dp);
+    uint32_t wp[8], wd[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      float pv[2], dsv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int i = 2 * kk + x;
+        const int m = m_first + (i >> 2) * 8 + hl * 4 + (i & 3);
+        int r = (int)(((float)m + 0.5f) * inv_grp);   // m / grp; exact for m < 2^22
+        r -= (r * grp > m) ? 1 : 0;
+        r += ((r + 1) * grp <= m) ? 1 : 0;
+        const float p = key > r ? 0.0f : fast_exp2(fmaf(s[i], c2, -l2[i]));
+        pv[x] = p;
+        dsv[x] = p * dp[i];
+      }
+      wp[kk] = pack_bf16x2(pv[0], pv[1]);
+      wd[kk] = pack_bf16x2(dsv[0], dsv[1]);
+    }
+    bf16x8 pp[2], dsp[2];
+    pp[0] = as_bf16x8(make_uint4(wp[0], wp[1], wp[2], wp[3]));
+    pp[1] = as_bf16x8(make_uint4(wp[4], wp[5], wp[6], wp[7]));
+    dsp[0] = as_bf16x8(make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    dsp[1] = as_bf16x8(make_uint4(wd[4], wd[5], wd[6], wd[7]));
+    pg_dkdv<D>(fr, far, qt, ot, sub, pp, dsp, dk, dv);
+  }
+  // The direct loads are not tracked by the compiler: none may still be writing LDS when
+  // the workgroup ends.
+  wait_vmcnt0();
+
+  if (!kvalid) return;
+  float* dkq = dk_r + kvrow * D;
+  float* dvq = dv_r + kvrow * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = dt * 32 + i4 * 8 + hl * 4;
+      float4 a = *reinterpret_cast<const float4*>(dkq + d0);
+      float4 b = *reinterpret_cast<const float4*>(dvq + d0);
+      a.x += dk[dt][4 * i4 + 0] * g.tau;
+      a.y += dk[dt][4 * i4 + 1] * g.tau;
+      a.z += dk[dt][4 * i4 + 2] * g.tau;
+      a.w += dk[dt][4 * i4 + 3] * g.tau;
+      b.x += dv[dt][4 * i4 + 0];
+      b.y += dv[dt][4 * i4 + 1];
+      b.z += dv[dt][4 * i4 + 2];
+      b.w += dv[dt][4 * i4 + 3];
+      *reinterpret_cast<float4*>(dkq + d0) = a;
+      *reinterpret_cast<float4*>(dvq + d0) = b;
+    }
+}
+
 // ---- fp32 kernel --------------------------------------------------------------------------
 // Plain fp32 arithmetic for the fp32 configuration: a workgroup of 64 threads covers
 // 64 / (D / 64) keys of one KV head, each key split over D / 64 threads (64 dims each, dot
@@ -554,6 +819,25 @@ hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void
     else
       hipLaunchKernelGGL((pg_pack<false, 128>), grid, block, 0, s, g, pg, q, o, lse, d_o, qs, os, sts);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_resp_dkdv(const Geom& g, const PgGeom& pg, const void* k_r, const void* v_r, const void* qs,
+                            const void* os, const float* sts, float* dk_r, float* dv_r, hipStream_t s) {
+  int64_t n = 0;
+  for (int k = 0; k < g.K; ++k) {
+    const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
+    n += (int64_t)g.Hkv * ((kmax + PgCfg<128>::KEYS - 1) / PgCfg<128>::KEYS);
+  }
+  if (n == 0) return hipSuccess;
+  const uint16_t *kr = (const uint16_t*)k_r, *vr = (const uint16_t*)v_r;
+  const uint16_t *q16 = (const uint16_t*)qs, *o16 = (const uint16_t*)os;
+  if (g.dqk == 64)
+    hipLaunchKernelGGL(resp_dkdv_bf16<64>, dim3((unsigned)n), dim3(256), 0, s, g, pg, kr, vr, q16, o16, sts, dk_r,
+                       dv_r);
+  else
+    hipLaunchKernelGGL(resp_dkdv_bf16<128>, dim3((unsigned)n), dim3(256), 0, s, g, pg, kr, vr, q16, o16, sts, dk_r,
+                       dv_r);
   return hipGetLastError();
 }
 

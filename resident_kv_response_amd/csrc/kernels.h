@@ -71,12 +71,16 @@ hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, fl
                       float* part, const Geom& g, int row_lo, int row_hi, int j_hi, float alpha,
                       hipStream_t s);
 
-// Full-sequence differential mode (k_prompt_grads.hip): pack the rows of each KV head into
+// Full-sequence differential mode (k_kv_grads.hip): pack the rows of each KV head into
 // the prompt-gradient stream (qs, os: [Hkv][n_rows][d]; sts: per 64-row stage lse*log2(e)
 // then -D), then dk_p, dv_p of resident keys [key_lo, key_hi) (= or +=) over every stream
 // row.
 hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void* q, const float* o,
                           const float* lse, const void* d_o, void* qs, void* os, float* sts, hipStream_t s);
+// dk_r, dv_r += the causal response-key gradients of every row of every response (bf16),
+// over the same packed stream.
+hipError_t launch_resp_dkdv(const Geom& g, const PgGeom& pg, const void* k_r, const void* v_r, const void* qs,
+                            const void* os, const float* sts, float* dk_r, float* dv_r, hipStream_t s);
 hipError_t launch_prompt_dkdv(const Geom& g, const PgGeom& pg, int dtype, const void* k_p, const void* v_p,
                               const void* qs, const void* os, const float* sts, int64_t key_lo, int64_t key_hi,
                               float* dk_p, float* dv_p, int accumulate, hipStream_t s);

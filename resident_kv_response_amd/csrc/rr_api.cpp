@@ -17,7 +17,6 @@ hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_
 hipError_t launch_dq_partials_f32(const Geom& g, const AttnPtrs& a, hipStream_t s);
 hipError_t launch_dq_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s);
 hipError_t launch_dkdv_f32(const Geom& g, const AttnPtrs& a, int key_hi, hipStream_t s);
-hipError_t launch_dkdv_bf16(const Geom& g, const AttnPtrs& a, int key_hi, hipStream_t s);
 
 hipError_t launch_fwd_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s) {
   return dtype == RR_BF16 ? launch_fwd_partials_bf16(g, a, s) : launch_fwd_partials_f32(g, a, s);
@@ -25,8 +24,11 @@ hipError_t launch_fwd_partials(const Geom& g, int dtype, const AttnPtrs& a, hipS
 hipError_t launch_dq_partials(const Geom& g, int dtype, const AttnPtrs& a, hipStream_t s) {
   return dtype == RR_BF16 ? launch_dq_partials_bf16(g, a, s) : launch_dq_partials_f32(g, a, s);
 }
+// fp32 problems; bf16 problems take the key-parallel kernel over the packed row stream
+// (launch_resp_dkdv).
 hipError_t launch_dkdv(const Geom& g, int dtype, const AttnPtrs& a, int key_hi, hipStream_t s) {
-  return dtype == RR_BF16 ? launch_dkdv_bf16(g, a, key_hi, s) : launch_dkdv_f32(g, a, key_hi, s);
+  (void)dtype;
+  return launch_dkdv_f32(g, a, key_hi, s);
 }
 
 // ---- profiling: HIP events around every launch -----------------------------------------
@@ -252,6 +254,24 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
          })))
       return hip_fail(e, "zero_rows");
   }
+  if (p->dtype == RR_BF16) {
+    // Key-parallel over the packed stream of the launch's rows [g.row_lo, g.row_hi): the
+    // whole walk (block_idx = -1) in one launch, each key's gradient over every row that
+    // sees it (the sum the walk forms block by block), or one block of the caller's walk.
+    const PgGeom pg = make_pg_geom(p, r_len, g.row_lo, g.row_hi);
+    const size_t srows = (size_t)p->Hkv * pg.n_rows;
+    const size_t sbytes = align_up(srows * p->d_qk * 2, 256);
+    char* sbase = reinterpret_cast<char*>(carve(ws, align_up(rows * sizeof(float), 256) +
+                                                        align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256)));
+    void* qs = sbase;
+    void* os = sbase + sbytes;
+    float* sts = reinterpret_cast<float*>(sbase + 2 * sbytes);
+    if ((e = timed("pg_pack", s, [&] { return launch_pg_pack(g, pg, p->dtype, q, o, lse, d_o, qs, os, sts, s); })))
+      return hip_fail(e, "pg_pack");
+    if ((e = timed("dkdv", s, [&] { return launch_resp_dkdv(g, pg, k_r, v_r, qs, os, sts, dk_r, dv_r, s); })))
+      return hip_fail(e, "dkdv");
+    return RR_OK;
+  }
   const int b_hi = block_idx >= 0 ? block_idx : nb - 1;
   const int b_lo = block_idx >= 0 ? block_idx : 0;
   for (int b = b_hi; b >= b_lo; --b) {   // reverse block walk
@@ -274,7 +294,7 @@ int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void*
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
-  const PgGeom pg = make_pg_geom(p, r_len);
+  const PgGeom pg = make_pg_geom(p, r_len, 0, p->R_max);
   const size_t rows = (size_t)p->Hkv * pg.n_rows;
   const size_t esz = p->dtype == RR_BF16 ? 2 : 4;
   const size_t rows_bytes = align_up(rows * p->d_qk * esz, 256);

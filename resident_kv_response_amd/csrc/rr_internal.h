@@ -51,14 +51,17 @@ int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
                    const float* const* grads, const int64_t* n_elems);
 Geom make_geom(const rr_problem* p, const int32_t* r_len);
 
-// Prompt-gradient stream (full-sequence differential mode): the rows of each KV head,
-// response after response, each response's r_len[k] * grp flattened rows padded to a
-// multiple of 64.  off[k] is response k's first stream row; off[K] = n_rows.
+// Packed row stream of the key-parallel K/V-gradient kernels: the rows of each KV head,
+// response after response.  Response k contributes its flattened rows m = r * grp + hh
+// from m_lo (a multiple of 64, the stage holding row row_lo) up to min(r_len[k], row_hi) *
+// grp, padded to a multiple of 64; rows outside [row_lo, min(r_len[k], row_hi)) are empty
+// (they contribute nothing).  off[k] is response k's first stream row; off[K] = n_rows.
 struct PgGeom {
   int32_t n_rows;
+  int32_t m_lo;
   int32_t off[RR_MAX_K + 1];
 };
-PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len);
+PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len, int32_t row_lo, int32_t row_hi);
 int validate_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
                    const void* x_layer, const void* x_last, const void* x_out);
 int validate_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,

@@ -107,8 +107,10 @@ size_t ws_bwd_bytes(const rr_problem* p) {
   if (p->latent)   // D, P and dS of the response pairs, chunk partials of dK_r / dV_r
     return align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p) +
            align_up((size_t)xty_n_chunks(p->R_max) * p->K * p->R_max * p->d_qk * sizeof(float), 256);
+  // D, the dQ partials, then (bf16) the packed row stream of the response dK/dV kernel
   return align_up(rows * sizeof(float), 256) +
-         align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256);
+         align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256) +
+         (p->dtype == RR_BF16 ? ws_prompt_bytes(p) : 0);
 }
 
 // Stream rows per KV head bound for the workspace: every response at R_max rows.
@@ -232,14 +234,16 @@ int validate_prompt_grads(const rr_problem* p, const rr_resident* kv, const void
   return RR_OK;
 }
 
-PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len) {
+PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len, int32_t row_lo, int32_t row_hi) {
   PgGeom pg;
   memset(&pg, 0, sizeof(pg));
   const int64_t grp = p->Hq / p->Hkv;
+  pg.m_lo = (int32_t)((int64_t)row_lo * grp / 64 * 64);
   int64_t at = 0;
   for (int k = 0; k < p->K; ++k) {
     pg.off[k] = (int32_t)at;
-    at += ((int64_t)r_len[k] * grp + 63) / 64 * 64;
+    const int64_t m_hi = (int64_t)(r_len[k] < row_hi ? r_len[k] : row_hi) * grp;
+    if (m_hi > pg.m_lo) at += (m_hi - pg.m_lo + 63) / 64 * 64;
   }
   for (int k = p->K; k <= RR_MAX_K; ++k) pg.off[k] = (int32_t)at;
   pg.n_rows = (int32_t)at;

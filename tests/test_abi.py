@@ -153,7 +153,9 @@ def test_workspace_and_parts_formulas():
     rows = 8192 * 24
     up = lambda x: -(-x // 256) * 256
     assert R.rr_workspace_bytes(p, R.RR_OP_FWD) == up(17 * rows * 128 * 4) + up(17 * rows * 4)
-    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == up(rows * 4) + up(17 * rows * 128 * 4)
+    stream = 4 * 8192 * 6          # packed rows of the response dK/dV kernel: Hkv * R_max * grp
+    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == (up(rows * 4) + up(17 * rows * 128 * 4)
+                                                    + 2 * up(stream * 128 * 2) + up(stream * 8))
     with pytest.raises(R.RRError):
         R.rr_workspace_bytes(_prob(Hq=3, Hkv=2), R.RR_OP_FWD)
 
