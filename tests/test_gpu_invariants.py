@@ -49,22 +49,29 @@ def test_deterministic_and_prompt_untouched():
     assert torch.equal(a.v_p.view(torch.int16), vp0.view(torch.int16))
 
 
-def test_caller_driven_reverse_walk():
-    G, res, st, prob, rl = _setup()
+@pytest.mark.parametrize("block,R_list", [(128, None), (77, [520, 301, 1]), (200, [520, 77])])
+def test_caller_driven_reverse_walk(block, R_list):
+    """Blocks driven one call at a time, last first, equal the whole walk; after step b the
+    dQ, dK, dV rows of block b are final.  Block sizes whose row boundaries fall inside a
+    64-row stage of the packed stream (77 and 200 rows with 6 heads per KV head), and
+    responses that end before, inside or after a block."""
+    G, res, st, prob, rl = _setup(R_list=R_list, block=block)
     full = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl).fwd().bwd().numpy()
     run = G.Run(prob, W.dtype, res["k_p"], res["v_p"], st, rl).fwd()
     run.dq.zero_()
     run.dk.zero_()
     run.dv.zero_()
-    nb = -(-W.R // W.block)
+    R_max = max(rl)
+    nb = -(-R_max // block)
+    print(f"[walk] block={block} R={rl}", flush=True)
     for b in range(nb - 1, -1, -1):
         run.bwd(accumulate=1, block_idx=b)
         now = run.numpy()
-        lo, hi = b * W.block, min(W.R, (b + 1) * W.block)
+        lo, hi = b * block, min(R_max, (b + 1) * block)
         # after step b, the rows of block b are final
-        np.testing.assert_allclose(now["dk"][0, lo:hi], full["dk"][0, lo:hi], rtol=0, atol=1e-6)
-        np.testing.assert_allclose(now["dv"][0, lo:hi], full["dv"][0, lo:hi], rtol=0, atol=1e-6)
-        np.testing.assert_allclose(now["dq"][0, lo:hi], full["dq"][0, lo:hi], rtol=0, atol=1e-6)
+        for key in ("dk", "dv", "dq"):
+            np.testing.assert_allclose(now[key][:, lo:hi], full[key][:, lo:hi], rtol=0, atol=1e-6,
+                                       err_msg=f"{key} block {b}")
 
 
 def test_exported_partials_merge():
