@@ -205,8 +205,10 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
  *               those of the clamped selection).
  *   accumulate  0: gradients are written (=) to every row the call touches;
  *               1: they are added (+=)
- *   block_idx   -1: whole response: dq of every row, then dk_r/dv_r by walking blocks
- *               nb-1 .. 0 (nb = ceil(R_max/block)).  b >= 0: only block b's query rows:
+ *   block_idx   -1: whole response: dq of every row, then dk_r/dv_r of the whole walk
+ *               over blocks nb-1 .. 0 (nb = ceil(R_max/block); bf16 problems form the
+ *               walk's sum in one launch, fp32 problems launch per block, last first).
+ *               b >= 0: only block b's query rows:
  *               their dq, and their contributions to dk_r/dv_r of response keys
  *               [0, (b+1)*block).  A caller driving the walk itself zeroes dk_r/dv_r
  *               once and calls b = nb-1 .. 0 with accumulate = 1; after the call for b
