@@ -1,36 +1,43 @@
-// Full-sequence differential mode: gradients of the resident prompt K/V (gfx950).
+// Key-parallel K/V gradients over a packed row stream (gfx950): the response's own dK_r,
+// dV_r of the reverse block walk, and the resident prompt's dK_p, dV_p of the
+// full-sequence differential mode.
 //
-// Source: ai.thesatyajit.com/articles/longstraw-2m-rl, section "The move: change the
-// graph boundary": the full-sequence gradient is the direct response term plus a term
+// Sources: ai.thesatyajit.com/articles/longstraw-2m-rl, section "The move: change the
+// graph boundary" (the full-sequence gradient is the direct response term plus a term
 // that flows back through the prompt state; the response-only contract keeps the first
-// and drops the second.  networkfinds.com/long-context-rl-is-a-state-lifetime-problem,
-// section "Preserve gradient semantics, not just forward outputs", asks for differential
-// validation against a conventional run.  This file forms the dropped term at the
-// attention boundary, dK_p and dV_p, so that the two can be compared; the response-only
-// path never calls it.
+// and drops the second) and section "Two incompatible architectures, same transaction"
+// (response blocks replayed in reverse); networkfinds.com/long-context-rl-is-a-state-
+// lifetime-problem, section "Preserve gradient semantics, not just forward outputs"
+// (differential validation against a conventional run).  The response-only backward
+// calls only resp_dkdv_bf16; the prompt term is formed only when asked for.
 //
-// With the global statistics of row i (lse_i, and D_i = dO_i . O_i), for prompt key j of
-// KV head g and every row i of a query head of g, in every response of the call:
+// With the global statistics of row i (lse_i, and D_i = dO_i . O_i), for key j of KV head g
+// and every row i of a query head of g that sees it:
 //   p_ij = exp(tau q_i.k_j - lse_i),  ds_ij = p_ij (dO_i.v_j - D_i),
-//   dK_p[j] = tau sum_i ds_ij q_i,    dV_p[j] = sum_i p_ij dO_i.
-// Every row sees every prompt key, so there is no mask.
+//   dK[j] = tau sum_i ds_ij q_i,      dV[j] = sum_i p_ij dO_i.
+// Every row sees every prompt key; a response key j is seen by the rows i >= j of its
+// own response.
 //
-// pg_pack: the rows of KV head g, flattened per response (m = r * grp + hh) and padded
-// with empty rows to a multiple of 64, become one contiguous stream per KV head: Q and
-// dO rows, and per 64-row stage the rows' lse * log2(e) followed by their -D.  An empty
+// pg_pack: the launch's rows of KV head g, flattened per response (m = r * grp + hh) and
+// padded with empty rows to a multiple of 64, become one contiguous stream per KV head: Q
+// and dO rows, and per 64-row stage the rows' lse * log2(e) followed by their -D.  An empty
 // row has lse = +inf and contributes p = 0.
 //
-// prompt_dkdv_bf16: key-parallel, one workgroup per (KV head, 128 prompt keys), four waves
-// (one per SIMD) of 32 keys.  A wave keeps its keys' K and V rows in registers (the B
-// operands of S = Q K^T and dP = dO V^T) and its dK^T, dV^T accumulators.  The stream's
-// 64-row stages pass through a ring of four LDS buffers, loaded straight from global
-// memory two stages ahead, one barrier per stage.  Per 32-row subtile u: S, and dP - D
-// (the accumulation starts from -D); p = 2^(S c2 - lse2), dS = p (dP - D), both rounded
-// to bf16; dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read by transposing LDS
-// reads in the row order of the score tile's C registers.  Block B(u) issues the dV/dK
-// MFMAs of subtile u-1 and the S, dP MFMAs of u+1 while the vector ALUs form p and dS of
-// u; it is laid out by hand in slots (each slot's LDS reads two slots ahead of its MFMA)
-// separated by scheduling barriers.
+// prompt_dkdv_bf16: one workgroup per (KV head, 128 prompt keys), four waves (one per SIMD)
+// of 32 keys.  A wave keeps its keys' K and V rows in registers (the B operands of
+// S = Q K^T and dP = dO V^T) and its dK^T, dV^T accumulators.  The stream's 64-row stages
+// pass through a ring of four LDS buffers, loaded straight from global memory two stages
+// ahead, one barrier per stage.  Per 32-row subtile u: S, and dP - D (the accumulation
+// starts from -D); p = 2^(S c2 - lse2), dS = p (dP - D), both rounded to bf16;
+// dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read by transposing LDS reads in
+// the row order of the score tile's C registers.  Block B(u) issues the dV/dK MFMAs of
+// subtile u-1 and the S, dP MFMAs of u+1 while the vector ALUs form p and dS of u; it is
+// laid out by hand in slots (each slot's LDS reads two slots ahead of its MFMA) separated
+// by scheduling barriers.
+//
+// resp_dkdv_bf16: the same pipeline for a tile of one response's own keys, over that
+// response's rows from the tile's first key on, in decreasing row order; the subtiles
+// at the causal diagonal run unpipelined with the mask.
 #include <type_traits>
 
 #include "k_attn_tile.h"
