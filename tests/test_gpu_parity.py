@@ -64,6 +64,19 @@ def test_tiny_f32_partitions(chunk, block):
     _run_and_check(w, [w.R], chunk=chunk, block=block)
 
 
+def test_f32_head_dim_128_gqa():
+    # the fp32 kernels at d = 128 with two KV heads (the fp32 configuration itself is d = 64)
+    w = configs.TINY_F32.with_(P=1300, R=100, Hq=4, Hkv=2, d_qk=128, d_v=128, seed=2101)
+    _run_and_check(w, [100, 37], chunk=512, block=48)
+
+
+def test_empty_prompt():
+    # P = 0: the rows attend to their own causal keys only
+    for base, seed in ((configs.SHARE_P256K, 2201), (configs.TINY_F32, 2202)):
+        w = base.with_(P=0, R=150, chunk=64, block=64, seed=seed)
+        _run_and_check(w, [150, 61])
+
+
 @pytest.mark.parametrize("d,Hq,Hkv", [(128, 8, 2), (64, 8, 2), (128, 12, 2), (128, 4, 4)])
 def test_bf16_multitile_ragged(d, Hq, Hkv):
     # several row tiles, ragged chunk and block tails, causal response across tiles

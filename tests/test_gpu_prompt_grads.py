@@ -69,10 +69,11 @@ def test_bf16_every_element(d, Hq, Hkv, P, lens):
     assert_bf16_close("dv_p", dv.double().cpu().numpy(), ref_v)
 
 
-def test_f32_every_element():
-    w = configs.TINY_F32.with_(P=1500, R=90, seed=7101)
+@pytest.mark.parametrize("d,Hkv", [(64, 1), (128, 2)])
+def test_f32_every_element(d, Hkv):
+    w = configs.TINY_F32.with_(P=1500, R=90, Hkv=Hkv, d_qk=d, d_v=d, seed=7101 + d)
     lens = [90, 33]
-    print(f"[prompt_grads] f32 P={w.P} R={lens}", flush=True)
+    print(f"[prompt_grads] f32 d={d} P={w.P} R={lens}", flush=True)
     G, res, mem, st, prob, run = _setup(w, lens, chunk=512, block=32)
     dk, dv = _prompt_grads(run, prob)
     ref_k, ref_v = _oracle_sum(w, res, mem, lens)
