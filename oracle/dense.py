@@ -37,7 +37,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-_BATCH_BYTES = 1 << 28
+_BATCH_BYTES = 1 << 30
 
 
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
@@ -145,6 +145,44 @@ def attend_bwd(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Optional[Sequence[i
     if full_sequence:
         out.update(dk_p=dk_p, dv_p=dv_p)
     return out
+
+
+def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
+                heads: Sequence[int]) -> Dict[str, np.ndarray]:
+    """Forward and response-only backward of individual query rows: entry n is row rows[n]
+    of query head heads[n] (one row of that head's query matrix), with everything the
+    definition gives for it in one pass over its visible keys:
+      o [n][d_v], lse [n] (natural log), dq [n][d_qk],
+    and the contributions of these query rows to dk_r [R][Hkv][d_qk], dv_r [R][Hkv][d_v]
+    (per row and head, the formulas of attend_bwd).  Where the selection holds every head
+    of rows j0..R-1, dk_r[j0:] and dv_r[j0:] are the full response-key gradients, as only
+    those rows see response keys >= j0."""
+    R, Hq, d_qk = q.shape
+    P, Hkv, d_v = v_p.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    o = np.zeros((rows.size, d_v))
+    lse = np.zeros(rows.size)
+    dq = np.zeros((rows.size, d_qk))
+    dk_r = np.zeros((R, Hkv, d_qk))
+    dv_r = np.zeros((R, Hkv, d_v))
+    for g in range(Hkv):
+        sel = np.flatnonzero(heads // (Hq // Hkv) == g)
+        if sel.size == 0:
+            continue
+        last = int(rows[sel].max())
+        keys, vals = _visible(k_p, v_p, k_r, v_r, g, last)
+        for b in _row_batches(sel, keys.shape[0]):
+            r, h = rows[b], heads[b]
+            qb, dob = q[r, h, :], d_o[r, h, :]
+            p, lse[b] = _softmax_rows(_scores(qb, keys, r, P, tau))
+            o[b] = p @ vals
+            D = np.sum(dob * o[b], axis=1)
+            ds = p * (dob @ vals.T - D[:, None])
+            dq[b] = tau * (ds @ keys)
+            dk_r[:last + 1, g, :] += tau * (ds[:, P:].T @ qb)
+            dv_r[:last + 1, g, :] += p[:, P:].T @ dob
+    return {"o": o, "lse": lse, "dq": dq, "dk_r": dk_r, "dv_r": dv_r}
 
 
 def prompt_grads_given_stats(q, k_p, v_p, d_o, o, lse, tau: float, keys: Sequence[int]):

@@ -206,3 +206,25 @@ def test_row_subsets_equal_full_rows():
     np.testing.assert_allclose(part["dq"], full["dq"][tail], atol=1e-13)
     np.testing.assert_allclose(part["dk_r"][7:], full["dk_r"][7:], atol=1e-13)
     np.testing.assert_allclose(part["dv_r"][7:], full["dv_r"][7:], atol=1e-13)
+
+
+def test_attend_rows_matches_library_autograd():
+    """Individual (row, head) query rows: O, lse (through the probe key), dQ against torch's
+    routine and its autograd; with every head of rows 9..R-1 included, the response keys
+    from 9 on get their full gradients."""
+    P, R, Hq, Hkv, d = 31, 14, 6, 2, 8
+    x = rand_problem(12, P, R, Hq, Hkv, d)
+    tau = 0.43
+    o_ref, (q, kp, vp, kr, vr) = _sdpa(x, tau)
+    (o_ref * torch.tensor(x["d_o"])).sum().backward()
+    o_probe, _ = _sdpa(x, tau, extra_probe=True)
+    g = np.random.default_rng(5)
+    rows = np.concatenate([g.integers(0, 9, 10), np.repeat(np.arange(9, R), Hq)])
+    heads = np.concatenate([g.integers(0, Hq, 10), np.tile(np.arange(Hq), R - 9)])
+    out = dense.attend_rows(x["q"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], x["d_o"], tau, rows, heads)
+    np.testing.assert_allclose(out["o"], o_ref.detach().numpy()[rows, heads], rtol=0, atol=1e-12)
+    w = o_probe.detach().numpy()[rows, heads, -1]
+    np.testing.assert_allclose(out["lse"], np.log(1.0 / w - 1.0), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(out["dq"], q.grad[0].permute(1, 0, 2).numpy()[rows, heads], atol=1e-10, rtol=0)
+    np.testing.assert_allclose(out["dk_r"][9:], kr.grad.numpy()[9:], atol=1e-10, rtol=0)
+    np.testing.assert_allclose(out["dv_r"][9:], vr.grad.numpy()[9:], atol=1e-10, rtol=0)
