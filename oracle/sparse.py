@@ -1,4 +1,4 @@
-"""Latent-page sparse variant, fp64, step by step.  TEST INFRASTRUCTURE ONLY.
+"""Latent-page sparse variant, fp64 (index scores fp32), step by step.  TEST INFRASTRUCTURE ONLY.
 
 Source: ai.thesatyajit.com/articles/longstraw-2m-rl, section "Two incompatible
 architectures, same transaction" (GLM instantiation): resident MLA latent pages and DSA
@@ -25,8 +25,11 @@ import numpy as np
 
 
 def index_scores(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
-    """sigma [R][P] = q_idx . k_idx, fp64."""
-    return np.asarray(q_idx, dtype=np.float64) @ np.asarray(k_idx, dtype=np.float64).T
+    """sigma [R][P] = q_idx . k_idx in fp32 arithmetic.  The scores only decide the
+    selection (an integer result), and the pages give them no precision, so they are
+    taken in the precision the GPU path takes them in; the summation order still differs,
+    so near-ties may rank differently on the two sides."""
+    return np.asarray(q_idx, dtype=np.float32) @ np.asarray(k_idx, dtype=np.float32).T
 
 
 def topk_row(sigma_row: np.ndarray, k: int) -> np.ndarray:

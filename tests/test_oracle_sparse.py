@@ -34,11 +34,21 @@ def test_topk_ties_break_toward_lower_position():
 
 
 def test_index_scores_plain_dot():
+    """fp32 scores: within the dot-product error bound n u sum|q_t k_t| (u = 2^-24) of the
+    exact sum, and exact for small-integer data."""
     x = _inputs(1, 9, 4, 1, 3, 2, 5)
     s = sparse.index_scores(x["q_idx"], x["k_idx"])
+    assert s.dtype == np.float32
+    qf = x["q_idx"].astype(np.float32).astype(np.float64)
+    kf = x["k_idx"].astype(np.float32).astype(np.float64)
     for i in range(4):
         for j in range(9):
-            assert abs(s[i, j] - sum(x["q_idx"][i, t] * x["k_idx"][j, t] for t in range(5))) < 1e-12
+            terms = [qf[i, t] * kf[j, t] for t in range(5)]
+            bound = 5 * 2.0 ** -24 * sum(abs(v) for v in terms) / (1 - 5 * 2.0 ** -24)
+            assert abs(float(s[i, j]) - sum(terms)) <= bound
+    g = np.random.default_rng(3)
+    qi, ki = g.integers(-3, 4, (6, 128)), g.integers(-3, 4, (50, 128))
+    np.testing.assert_array_equal(sparse.index_scores(qi, ki), (qi @ ki.T).astype(np.float32))
 
 
 def _torch_masked(x, idx, tau, dv, grad=False):
