@@ -69,7 +69,8 @@ def _softmax_rows(s: np.ndarray):
 
 def _scores(qh, keys, rows, P, tau):
     """tau * q . k over the visible keys of each row; response key j > row is -inf."""
-    s = tau * (qh @ keys.T)
+    s = qh @ keys.T
+    s *= tau
     j = np.arange(keys.shape[0] - P)
     s[:, P:][j[None, :] > rows[:, None]] = -np.inf
     return s
@@ -175,10 +176,20 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
         for b in _row_batches(sel, keys.shape[0]):
             r, h = rows[b], heads[b]
             qb, dob = q[r, h, :], d_o[r, h, :]
-            p, lse[b] = _softmax_rows(_scores(qb, keys, r, P, tau))
+            # the softmax and dS = p (dp - D) are formed in place: these arrays hold one
+            # value per visible key and row, gigabytes at long prompts
+            p = _scores(qb, keys, r, P, tau)
+            m = p.max(axis=1, keepdims=True)
+            p -= m
+            np.exp(p, out=p)
+            den = p.sum(axis=1, keepdims=True)
+            p /= den
+            lse[b] = m[:, 0] + np.log(den[:, 0])
             o[b] = p @ vals
             D = np.sum(dob * o[b], axis=1)
-            ds = p * (dob @ vals.T - D[:, None])
+            ds = dob @ vals.T
+            ds -= D[:, None]
+            ds *= p
             dq[b] = tau * (ds @ keys)
             dk_r[:last + 1, g, :] += tau * (ds[:, P:].T @ qb)
             dv_r[:last + 1, g, :] += p[:, P:].T @ dob

@@ -144,16 +144,37 @@ def lastkv_chunk(w: Workload) -> Dict[str, np.ndarray]:
             "alpha": g.uniform(0.05, 0.95, w.Hkv).astype(np.float32)}
 
 
-def sample_rows(seed: int, R: int, n: int, block: int) -> np.ndarray:
-    """Sorted query rows to check at full size: row 0, row R-1, both sides of every block
-    boundary, the first row of a partial last block, then seeded rows without replacement."""
+def _must_rows(R: int, block: int) -> list:
+    """Row 0, row R-1 and both sides of every block boundary (the first row of a partial
+    last block among them)."""
     must = {0, R - 1}
     for b in range(block, R, block):
         must.update({b - 1, b})
-    must = sorted(r for r in must if 0 <= r < R)
+    return sorted(r for r in must if 0 <= r < R)
+
+
+def sample_rows(seed: int, R: int, n: int, block: int) -> np.ndarray:
+    """Sorted query rows to check at full size: row 0, row R-1, both sides of every block
+    boundary, the first row of a partial last block, then seeded rows without replacement."""
+    must = _must_rows(R, block)
     if len(must) >= n or len(must) >= R:
         return np.array(must[:max(n, 0)] if len(must) > n else must, dtype=np.int64)
     g = np.random.Generator(np.random.PCG64(_stream_seed(seed, "rows")))
     rest = np.setdiff1d(np.arange(R), np.array(must))
     extra = g.choice(rest, size=min(n - len(must), rest.size), replace=False)
     return np.sort(np.concatenate([np.array(must), extra])).astype(np.int64)
+
+
+def sample_query_rows(seed: int, R: int, Hq: int, n: int, block: int):
+    """n query rows of single heads to check at full size, as (positions, heads) sorted by
+    position then head: every position of _must_rows with a seeded head, then seeded
+    (position, head) pairs without replacement from the rest."""
+    g = np.random.Generator(np.random.PCG64(_stream_seed(seed, "rows")))
+    must = np.array(_must_rows(R, block), dtype=np.int64)
+    flat = must * Hq + g.integers(0, Hq, must.size)
+    k = min(n, R * Hq) - flat.size
+    if k > 0:
+        rest = np.setdiff1d(np.arange(R * Hq, dtype=np.int64), flat)
+        flat = np.concatenate([flat, g.choice(rest, size=k, replace=False)])
+    flat = np.sort(flat)
+    return flat // Hq, flat % Hq

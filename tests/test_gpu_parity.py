@@ -107,8 +107,10 @@ def test_f32_varlen_microbatch():
 @pytest.mark.parametrize("cfg", ["GQA_P128K", "SHARE_P256K", "FULL_P2M"])
 def test_full_size_sampled_rows(cfg):
     """Full-size configurations: every output of the GPU path is produced; O, lse and dQ of
-    seeded sampled rows (block boundaries included) are compared with the oracle, and
-    dK/dV of the last response keys, whose gradients only rows near the end reach."""
+    512 seeded sampled query rows (a query row is one position of one head; both sides of
+    every block boundary and the first and last rows among them) are compared with the
+    oracle, and so are dK/dV of the last 16 response keys, whose gradients only the last
+    16 positions reach (every head of those positions is added to the sample)."""
     from tests import _gpu as G
     w = getattr(configs, cfg)
     # the 2M group: its first member, at its seeded length
@@ -118,15 +120,19 @@ def test_full_size_sampled_rows(cfg):
     prob = G.problem(w.P, Rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
     print(f"[parity] {w.name} full size, R={Rg}", flush=True)
     got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [Rg]).fwd().bwd().numpy()
-    n_rows, n_tail = (24, 8) if w.P <= 262144 else (10, 4)
-    rows = synth.sample_rows(w.seed, Rg, n_rows, w.block)
+    n_tail = 16
+    rows, heads = synth.sample_query_rows(w.seed, Rg, w.Hq, 512, w.block)
     tail = np.arange(Rg - n_tail, Rg)
-    rows = np.union1d(rows, tail)
-    ref = G.oracle_member(dense, w.dtype, res["k_p"], res["v_p"], st, 0, Rg, w.tau, rows=rows)
-    assert_bf16_close("o", got["o"][0][rows], ref["o"])
-    assert_bf16_close("dq", got["dq"][0][rows], ref["dq"])
-    assert np.max(np.abs(got["lse"][0][rows] - ref["lse"])) <= 2e-2
-    # response keys j >= R-n_tail receive gradient only from rows >= R-n_tail, all included
+    flat = np.union1d(rows * w.Hq + heads, (tail[:, None] * w.Hq + np.arange(w.Hq)).ravel())
+    rows, heads = flat // w.Hq, flat % w.Hq
+    print(f"[parity] oracle over {rows.size} query rows", flush=True)
+    f = lambda x: synth.as_f64(x, w.dtype)
+    x = {n: f(st[n][0, :Rg]) for n in ("q", "k_r", "v_r", "d_o")}
+    ref = dense.attend_rows(x["q"], f(res["k_p"]), f(res["v_p"]), x["k_r"], x["v_r"], x["d_o"], w.tau,
+                            rows, heads)
+    assert_bf16_close("o", got["o"][0][rows, heads], ref["o"])
+    assert_bf16_close("dq", got["dq"][0][rows, heads], ref["dq"])
+    assert np.max(np.abs(got["lse"][0][rows, heads] - ref["lse"])) <= 2e-2
     assert_bf16_close("dk_r tail", got["dk"][0][Rg - n_tail:], ref["dk_r"][Rg - n_tail:])
     assert_bf16_close("dv_r tail", got["dv"][0][Rg - n_tail:], ref["dv_r"][Rg - n_tail:])
     assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))

@@ -2,9 +2,9 @@
 resident prompt K/V, the term the response-only contract drops, against the fp64 oracle.
 
 Small problems compare every element with the full-sequence oracle (bf16: rel-L2 <= 5e-3
-and max-abs <= 2e-2; fp32: max-abs <= 1e-5).  At the full 2,097,152-position size, sampled
-prompt positions are compared with the oracle's conditional form, fed the device's O and
-lse (which the full-size forward tests validate on sampled rows).
+and max-abs <= 2e-2; fp32: max-abs <= 1e-5).  At the full 2,097,152-position prompt,
+sampled positions of a short response are compared with the oracle, and the full-length
+member is checked through two identities of the exact gradients over all keys.
 """
 import numpy as np
 import pytest
@@ -97,25 +97,60 @@ def test_accumulate_adds_and_response_grads_unchanged():
         np.testing.assert_array_equal(a[key], b[key])
 
 
-def test_full_size_sampled_keys():
-    """The 2M configuration's first member at its seeded length: sampled prompt positions
-    (the first and last, both sides of every 128-key workgroup boundary nearby and of the
-    chunk boundaries) against the conditional oracle over every row of the response."""
-    w = configs.FULL_P2M
-    Rg = int(synth.response_lengths(w)[0])
-    print(f"[prompt_grads] {w.name} full size, R={Rg}", flush=True)
-    G, res, mem, st, prob, run = _setup(w, [Rg])
-    dk, dv = _prompt_grads(run, prob)
+def _sampled_keys(w, n):
+    """The first and last prompt positions, both sides of the 128-key workgroup boundaries
+    next to them and of every chunk boundary, and n seeded positions."""
     rng = np.random.default_rng(w.seed + 77)
-    keys = np.unique(np.concatenate([
+    return np.unique(np.concatenate([
         [0, 1, 127, 128, w.P - 129, w.P - 128, w.P - 1],
         np.arange(1, w.n_chunks) * w.chunk, np.arange(1, w.n_chunks) * w.chunk - 1,
-        rng.choice(w.P, 24, replace=False)]))
+        rng.choice(w.P, n, replace=False)]))
+
+
+def test_full_prompt_short_response_sampled_keys():
+    """Every one of the 2,097,152 prompt positions is a key of the launch; a 24-row
+    response (144 rows of the packed row stream: two full 64-row stages and a ragged one)
+    keeps the oracle's forward over all its rows and heads short.  Sampled positions are
+    compared with the oracle, whose O and lse are its own."""
+    w = configs.FULL_P2M
+    Rs = 24
+    print(f"[prompt_grads] {w.name} full prompt, R={Rs}", flush=True)
+    G, res, mem, st, prob, run = _setup(w, [Rs])
+    dk, dv = _prompt_grads(run, prob)
+    keys = _sampled_keys(w, 200)
     f = lambda x: synth.as_f64(x, w.dtype)
-    o = run.o[0, :Rg].double().cpu().numpy()
-    lse = run.lse[0, :Rg].double().cpu().numpy()
-    ref_k, ref_v = dense.prompt_grads_given_stats(f(st["q"][0, :Rg]), f(res["k_p"]), f(res["v_p"]),
-                                                  f(st["d_o"][0, :Rg]), o, lse, w.tau, keys)
+    x = {n: f(st[n][0, :Rs]) for n in ("q", "k_r", "v_r", "d_o")}
+    kp, vp = f(res["k_p"]), f(res["v_p"])
+    o, lse = dense.attend(x["q"], kp, vp, x["k_r"], x["v_r"], w.tau)
+    ref_k, ref_v = dense.prompt_grads_given_stats(x["q"], kp, vp, x["d_o"], o, lse, w.tau, keys)
     assert_bf16_close("dk_p sampled", dk[keys].double().cpu().numpy(), ref_k)
     assert_bf16_close("dv_p sampled", dv[keys].double().cpu().numpy(), ref_v)
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+def test_full_size_key_sums():
+    """The 2M configuration's first member at its seeded length, as the full-sequence
+    benchmark launches it, checked through two identities of the exact gradients that need
+    no oracle forward over 2M keys.  Per KV head g, over all keys j (prompt and response):
+      sum_j dV[j, g] = sum over rows i and heads h of g of dO[i, h]   (each row of P sums to 1)
+      sum_j dK[j, g] = 0                                              (each row of dS sums to 0)
+    The first is held to the bf16 bounds.  For the second the bf16 rounding of dS before
+    its product leaves a residue of about 1e-3 of |dK|; a term dropped over one 131,072-key
+    chunk leaves about 0.25, so the bound is 2e-2 of the norm of all dK rows."""
+    w = configs.FULL_P2M
+    Rg = int(synth.response_lengths(w)[0])
+    print(f"[prompt_grads] {w.name} key sums, R={Rg}", flush=True)
+    G, res, mem, st, prob, run = _setup(w, [Rg])
+    dk, dv = _prompt_grads(run, prob)
+    got = run.bwd().numpy()
+    grp = w.Hq // w.Hkv
+    d_o = synth.as_f64(st["d_o"][0, :Rg], w.dtype)
+    want_v = d_o.reshape(Rg, w.Hkv, grp, w.d_v).sum(axis=(0, 2))
+    sum_v = dv.double().sum(0).cpu().numpy() + got["dv"][0][:Rg].sum(0)
+    sum_k = dk.double().sum(0).cpu().numpy() + got["dk"][0][:Rg].sum(0)
+    assert_bf16_close("sum of dV over all keys", sum_v, want_v)
+    norm_k = np.sqrt(float((dk.double() ** 2).sum()) + float(np.sum(got["dk"][0][:Rg] ** 2)))
+    resid = float(np.linalg.norm(sum_k)) / norm_k
+    print(f"[prompt_grads] |sum dK| / |dK| = {resid:.2e}", flush=True)
+    assert resid <= 2e-2
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()

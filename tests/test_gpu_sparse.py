@@ -119,7 +119,9 @@ def test_sparse_latent_full_size_sampled_rows():
              q_idx=m["q_idx"], d_o=m["d_o"])
     print(f"[sparse] {w.name} full size", flush=True)
     got = _run(d, w.P, w.R, w.topk, w.block)
-    rows = np.union1d(synth.sample_rows(w.seed, w.R, 16, w.block), np.arange(w.R - 4, w.R))
+    # 512 seeded positions (every head of each: all 64 heads share a position's selection)
+    rows = np.union1d(synth.sample_rows(w.seed, w.R, 512, w.block), np.arange(w.R - 4, w.R))
+    print(f"[sparse] oracle over {rows.size} positions", flush=True)
     sel, sig, o, lse, gr = _oracle(d, w.topk, rows=rows)
     same = []
     for n, r in enumerate(rows):
