@@ -108,34 +108,44 @@ def test_f32_varlen_microbatch():
 def test_full_size_sampled_rows(cfg):
     """Full-size configurations: every output of the GPU path is produced; O, lse and dQ of
     512 seeded sampled query rows (a query row is one position of one head; both sides of
-    every block boundary and the first and last rows among them) are compared with the
-    oracle, and so are dK/dV of the last 16 response keys, whose gradients only the last
-    16 positions reach (every head of those positions is added to the sample)."""
+    every block boundary and the first and last rows of each response among them) are
+    compared with the oracle.  The 2M group spreads them over its 8 members at their seeded
+    lengths, 64 each.  dK/dV of the last 16 response keys (of the first member) are
+    compared too: only the last 16 positions reach them, and every head of those is added
+    to the sample."""
     from tests import _gpu as G
     w = getattr(configs, cfg)
-    # the 2M group: its first member, at its seeded length
-    Rg = int(synth.response_lengths(w)[0]) if w.G > 1 else w.R
-    res, mem = _inputs(w, [Rg])
-    st = G.stack_members(mem, Rg)
-    prob = G.problem(w.P, Rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
-    print(f"[parity] {w.name} full size, R={Rg}", flush=True)
-    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [Rg]).fwd().bwd().numpy()
+    lens = [int(r) for r in synth.response_lengths(w)] if w.G > 1 else [w.R]
     n_tail = 16
-    rows, heads = synth.sample_query_rows(w.seed, Rg, w.Hq, 512, w.block)
-    tail = np.arange(Rg - n_tail, Rg)
-    flat = np.union1d(rows * w.Hq + heads, (tail[:, None] * w.Hq + np.arange(w.Hq)).ravel())
-    rows, heads = flat // w.Hq, flat % w.Hq
-    print(f"[parity] oracle over {rows.size} query rows", flush=True)
+    res = synth.resident(w)
     f = lambda x: synth.as_f64(x, w.dtype)
-    x = {n: f(st[n][0, :Rg]) for n in ("q", "k_r", "v_r", "d_o")}
-    ref = dense.attend_rows(x["q"], f(res["k_p"]), f(res["v_p"]), x["k_r"], x["v_r"], x["d_o"], w.tau,
-                            rows, heads)
-    assert_bf16_close("o", got["o"][0][rows, heads], ref["o"])
-    assert_bf16_close("dq", got["dq"][0][rows, heads], ref["dq"])
-    assert np.max(np.abs(got["lse"][0][rows, heads] - ref["lse"])) <= 2e-2
-    assert_bf16_close("dk_r tail", got["dk"][0][Rg - n_tail:], ref["dk_r"][Rg - n_tail:])
-    assert_bf16_close("dv_r tail", got["dv"][0][Rg - n_tail:], ref["dv_r"][Rg - n_tail:])
-    assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))
+    kp, vp = f(res["k_p"]), f(res["v_p"])
+    got_all = {k: [] for k in ("o", "lse", "dq")}
+    ref_all = {k: [] for k in ("o", "lse", "dq")}
+    for g, Rg in enumerate(lens):
+        st = G.stack_members([synth.member(w, g, R=Rg)], Rg)
+        prob = G.problem(w.P, Rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+        print(f"[parity] {w.name} member {g} full size, R={Rg}", flush=True)
+        got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [Rg]).fwd().bwd().numpy()
+        assert np.all(np.isfinite(got["dk"])) and np.all(np.isfinite(got["dv"]))
+        rows, heads = synth.sample_query_rows(w.seed + g, Rg, w.Hq, 512 // len(lens), w.block)
+        if g == 0:
+            tail = np.arange(Rg - n_tail, Rg)
+            flat = np.union1d(rows * w.Hq + heads, (tail[:, None] * w.Hq + np.arange(w.Hq)).ravel())
+            rows, heads = flat // w.Hq, flat % w.Hq
+        print(f"[parity] oracle over {rows.size} query rows", flush=True)
+        x = {n: f(st[n][0, :Rg]) for n in ("q", "k_r", "v_r", "d_o")}
+        ref = dense.attend_rows(x["q"], kp, vp, x["k_r"], x["v_r"], x["d_o"], w.tau, rows, heads)
+        for k in got_all:
+            got_all[k].append(got[k][0][rows, heads])
+            ref_all[k].append(ref[k])
+        if g == 0:
+            assert_bf16_close("dk_r tail", got["dk"][0][Rg - n_tail:], ref["dk_r"][Rg - n_tail:])
+            assert_bf16_close("dv_r tail", got["dv"][0][Rg - n_tail:], ref["dv_r"][Rg - n_tail:])
+    cat = lambda d, k: np.concatenate(d[k])
+    assert_bf16_close("o", cat(got_all, "o"), cat(ref_all, "o"))
+    assert_bf16_close("dq", cat(got_all, "dq"), cat(ref_all, "dq"))
+    assert np.max(np.abs(cat(got_all, "lse") - cat(ref_all, "lse"))) <= 2e-2
 
 
 @pytest.mark.parametrize("slope", [6.0, 40.0, 400.0])
