@@ -148,6 +148,41 @@ def test_full_size_sampled_rows(cfg):
     assert np.max(np.abs(cat(got_all, "lse") - cat(ref_all, "lse"))) <= 2e-2
 
 
+@pytest.fixture(scope="module")
+def gqa_full():
+    """The GQA configuration (P = 131,072, R = 4096, 32/8 heads) run once through the GPU
+    path, with the oracle's fp64 inputs."""
+    from tests import _gpu as G
+    w = configs.GQA_P128K
+    res, mem = _inputs(w, [w.R])
+    st = G.stack_members(mem, w.R)
+    prob = G.problem(w.P, w.R, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+    print(f"[parity] {w.name} full run", flush=True)
+    got = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [w.R]).fwd().bwd().numpy()
+    f = lambda x: synth.as_f64(x, w.dtype)
+    x = {n: f(st[n][0]) for n in ("q", "k_r", "v_r", "d_o")}
+    x["k_p"], x["v_p"] = f(res["k_p"]), f(res["v_p"])
+    return w, x, got
+
+
+@pytest.mark.parametrize("g", range(8))
+def test_gqa_full_size_every_row(gqa_full, g):
+    """Every row of the GQA configuration, one KV head per case: O, lse and dQ of all 4096
+    positions of its 4 query heads, and, since every query row that reaches them is
+    included, the full dK_r, dV_r of that KV head."""
+    w, x, got = gqa_full
+    grp = w.Hq // w.Hkv
+    print(f"[parity] {w.name} every row of KV head {g}", flush=True)
+    rows = np.repeat(np.arange(w.R), grp)
+    heads = np.tile(np.arange(g * grp, (g + 1) * grp), w.R)
+    ref = dense.attend_rows(x["q"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], x["d_o"], w.tau, rows, heads)
+    assert_bf16_close("o", got["o"][0][rows, heads], ref["o"])
+    assert_bf16_close("dq", got["dq"][0][rows, heads], ref["dq"])
+    assert np.max(np.abs(got["lse"][0][rows, heads] - ref["lse"])) <= 2e-2
+    assert_bf16_close("dk_r", got["dk"][0][:, g], ref["dk_r"][:, g])
+    assert_bf16_close("dv_r", got["dv"][0][:, g], ref["dv_r"][:, g])
+
+
 @pytest.mark.parametrize("slope", [6.0, 40.0, 400.0])
 def test_bf16_growing_scores(slope):
     """Scores that rise along the prompt (a ramp in one key dimension that every query
