@@ -213,6 +213,10 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
  *               [0, (b+1)*block).  A caller driving the walk itself zeroes dk_r/dv_r
  *               once and calls b = nb-1 .. 0 with accumulate = 1; after the call for b
  *               the dk_r/dv_r rows of block b are final.
+ *   ws          workspace of rr_workspace_bytes(p, RR_OP_BWD) bytes.  On return its first
+ *               K * R_max * Hq floats hold D = dO . O, [K][R_max][Hq] fp32, for the rows
+ *               the call covered (0 in padding rows; the entries of other rows are
+ *               unspecified).
  */
 int rr_attn_bwd(const rr_problem* p, const rr_resident* kv,
                 const void* q, const void* k_r, const void* v_r, const int32_t* r_len,

@@ -153,7 +153,7 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
     """Forward and response-only backward of individual query rows: entry n is row rows[n]
     of query head heads[n] (one row of that head's query matrix), with everything the
     definition gives for it in one pass over its visible keys:
-      o [n][d_v], lse [n] (natural log), dq [n][d_qk],
+      o [n][d_v], lse [n] (natural log), D [n] = d_o . o, dq [n][d_qk],
     and the contributions of these query rows to dk_r [R][Hkv][d_qk], dv_r [R][Hkv][d_v]
     (per row and head, the formulas of attend_bwd).  Where the selection holds every head
     of rows j0..R-1, dk_r[j0:] and dv_r[j0:] are the full response-key gradients, as only
@@ -164,6 +164,7 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
     heads = np.asarray(heads, dtype=np.int64)
     o = np.zeros((rows.size, d_v))
     lse = np.zeros(rows.size)
+    Dv = np.zeros(rows.size)
     dq = np.zeros((rows.size, d_qk))
     dk_r = np.zeros((R, Hkv, d_qk))
     dv_r = np.zeros((R, Hkv, d_v))
@@ -187,13 +188,14 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
             lse[b] = m[:, 0] + np.log(den[:, 0])
             o[b] = p @ vals
             D = np.sum(dob * o[b], axis=1)
+            Dv[b] = D
             ds = dob @ vals.T
             ds -= D[:, None]
             ds *= p
             dq[b] = tau * (ds @ keys)
             dk_r[:last + 1, g, :] += tau * (ds[:, P:].T @ qb)
             dv_r[:last + 1, g, :] += p[:, P:].T @ dob
-    return {"o": o, "lse": lse, "dq": dq, "dk_r": dk_r, "dv_r": dv_r}
+    return {"o": o, "lse": lse, "D": Dv, "dq": dq, "dk_r": dk_r, "dv_r": dv_r}
 
 
 def prompt_grads_given_stats(q, k_p, v_p, d_o, o, lse, tau: float, keys: Sequence[int]):

@@ -37,6 +37,12 @@ def problem(P, R_max, Hq, Hkv, d, chunk, block, dtype, K=1, tau=None):
                      dtype=R.RR_BF16 if dtype == "bf16" else R.RR_F32, K=K)
 
 
+def ws_D(ws, p):
+    """D = dO . O [K][R_max][Hq] fp32, which rr_attn_bwd leaves at the head of its workspace."""
+    n = p.K * p.R_max * p.Hq
+    return ws[:4 * n].view(torch.float32).reshape(p.K, p.R_max, p.Hq).double().cpu().numpy()
+
+
 class Run:
     """Device copies of one problem's inputs plus its outputs."""
 
@@ -70,8 +76,11 @@ class Run:
         return self
 
     def numpy(self):
+        """Outputs, and D = dO . O [K][R_max][Hq] from the head of the backward's workspace."""
         torch.cuda.synchronize()
-        return {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
+        out = {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
+        out["D"] = ws_D(self.ws_b, self.p)
+        return out
 
 
 def oracle_member(dense, dtype, k_p, v_p, stacked, kk, rl, tau, rows=None, grads=True):
@@ -122,6 +131,7 @@ class LatentRun:
         torch.cuda.synchronize()
         out = {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
         out["idx"] = self.idx.cpu().numpy()
+        out["D"] = ws_D(self.ws_b, self.p)
         return out
 
 

@@ -40,3 +40,17 @@ def assert_f32_close(name, got, ref, mabs=1e-5):
     m = max_abs(got, ref)
     assert m <= mabs, f"{name}: max-abs {m:.3e} (<= {mabs})"
     return m
+
+
+def assert_D_close(name, got, ref, dtype):
+    """D = dO . O (the backward's preprocess) against the oracle's.  D is a d_v-term dot
+    product of dO with O, so it carries O's error weighted by dO: the element bound is the
+    O bound (bf16: 2e-2, fp32: 1e-5) scaled by max(1, |D|), and bf16 also keeps the
+    rel-L2 bound of 5e-3."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    tol = (2e-2 if dtype == "bf16" else 1e-5) * np.maximum(1.0, np.abs(ref))
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"{name}: worst |dD|/bound {float(np.max(err / tol)):.3f}"
+    if dtype == "bf16":
+        r = rel_l2(got, ref)
+        assert r <= 5e-3, f"{name}: rel-L2 {r:.3e}"

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import dense
 from resident_kv_response_amd import configs, synth
-from tests._helpers import assert_bf16_close, assert_f32_close
+from tests._helpers import assert_bf16_close, assert_D_close, assert_f32_close
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,15 @@ def _run_and_check(w, members_R, R_max=None, chunk=None, block=None, check_rows=
         lse_tol = 1e-5 if w.dtype == "f32" else 2e-2
         if rl > 0:
             assert np.max(np.abs(got["lse"][kk][sel] - ref["lse"])) <= lse_tol
+            # D = dO . O of the backward's preprocess, against the oracle's O
+            d_o = synth.as_f64(st["d_o"][kk, :rl], w.dtype)[sel]
+            D_ref = np.sum(d_o * ref["o"], axis=-1)
+            assert_D_close(f"D[k={kk}]", got["D"][kk][sel], D_ref, w.dtype)
         # padding rows
         assert np.all(got["o"][kk][rl:] == 0) and np.all(np.isneginf(got["lse"][kk][rl:]))
         assert np.all(got["dq"][kk][rl:] == 0)
         assert np.all(got["dk"][kk][rl:] == 0) and np.all(got["dv"][kk][rl:] == 0)
+        assert np.all(got["D"][kk][rl:] == 0)
     return got
 
 
@@ -120,8 +125,8 @@ def test_full_size_sampled_rows(cfg):
     res = synth.resident(w)
     f = lambda x: synth.as_f64(x, w.dtype)
     kp, vp = f(res["k_p"]), f(res["v_p"])
-    got_all = {k: [] for k in ("o", "lse", "dq")}
-    ref_all = {k: [] for k in ("o", "lse", "dq")}
+    got_all = {k: [] for k in ("o", "lse", "D", "dq")}
+    ref_all = {k: [] for k in ("o", "lse", "D", "dq")}
     for g, Rg in enumerate(lens):
         st = G.stack_members([synth.member(w, g, R=Rg)], Rg)
         prob = G.problem(w.P, Rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
@@ -145,6 +150,7 @@ def test_full_size_sampled_rows(cfg):
     cat = lambda d, k: np.concatenate(d[k])
     assert_bf16_close("o", cat(got_all, "o"), cat(ref_all, "o"))
     assert_bf16_close("dq", cat(got_all, "dq"), cat(ref_all, "dq"))
+    assert_D_close("D", cat(got_all, "D"), cat(ref_all, "D"), w.dtype)
     assert np.max(np.abs(cat(got_all, "lse") - cat(ref_all, "lse"))) <= 2e-2
 
 
@@ -178,6 +184,7 @@ def test_gqa_full_size_every_row(gqa_full, g):
     ref = dense.attend_rows(x["q"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], x["d_o"], w.tau, rows, heads)
     assert_bf16_close("o", got["o"][0][rows, heads], ref["o"])
     assert_bf16_close("dq", got["dq"][0][rows, heads], ref["dq"])
+    assert_D_close("D", got["D"][0][rows, heads], ref["D"], w.dtype)
     assert np.max(np.abs(got["lse"][0][rows, heads] - ref["lse"])) <= 2e-2
     assert_bf16_close("dk_r", got["dk"][0][:, g], ref["dk_r"][:, g])
     assert_bf16_close("dv_r", got["dv"][0][:, g], ref["dv_r"][:, g])

@@ -13,7 +13,7 @@ import pytest
 
 from oracle import sparse
 from resident_kv_response_amd import configs, synth
-from tests._helpers import assert_bf16_close
+from tests._helpers import assert_bf16_close, assert_D_close
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,8 @@ def test_sparse_exact_selection_every_element(P, R, topk, block):
     assert_bf16_close("dq", got["dq"][0], gr["dq"])
     assert_bf16_close("dk_r", got["dk"][0], gr["dk_r"])
     assert_bf16_close("dv_r", got["dv"][0], gr["dv_r"])
+    # D = dO . O of the backward's preprocess, against the oracle's O
+    assert_D_close("D", got["D"][0], np.sum(synth.as_f64(d["d_o"], "bf16") * o, axis=-1), "bf16")
 
 
 def test_sparse_exact_selection_large_rows_with_ties():

@@ -225,6 +225,8 @@ def test_attend_rows_matches_library_autograd():
     np.testing.assert_allclose(out["o"], o_ref.detach().numpy()[rows, heads], rtol=0, atol=1e-12)
     w = o_probe.detach().numpy()[rows, heads, -1]
     np.testing.assert_allclose(out["lse"], np.log(1.0 / w - 1.0), rtol=0, atol=1e-10)
+    D = np.sum(o_ref.detach().numpy()[rows, heads] * x["d_o"][rows, heads], axis=1)
+    np.testing.assert_allclose(out["D"], D, rtol=0, atol=1e-12)
     np.testing.assert_allclose(out["dq"], q.grad[0].permute(1, 0, 2).numpy()[rows, heads], atol=1e-10, rtol=0)
     np.testing.assert_allclose(out["dk_r"][9:], kr.grad.numpy()[9:], atol=1e-10, rtol=0)
     np.testing.assert_allclose(out["dv_r"][9:], vr.grad.numpy()[9:], atol=1e-10, rtol=0)
