@@ -45,17 +45,17 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def _row_batches(rows: np.ndarray, n_keys: int):
-    step = max(1, _BATCH_BYTES // (8 * max(1, n_keys)))
+def _row_batches(rows: np.ndarray, n_keys: int, batch_bytes: int = _BATCH_BYTES):
+    step = max(1, batch_bytes // (8 * max(1, n_keys)))
     for a in range(0, rows.size, step):
         yield rows[a:a + step]
 
 
 def _visible(k_p, v_p, k_r, v_r, g, last_row):
     """Keys and values one KV head offers to rows <= last_row: all prompt positions,
-    then response positions 0..last_row."""
-    keys = np.concatenate([k_p[:, g, :], k_r[:last_row + 1, g, :]], axis=0)
-    vals = np.concatenate([v_p[:, g, :], v_r[:last_row + 1, g, :]], axis=0)
+    then response positions 0..last_row, in fp64 (narrower inputs are widened exactly)."""
+    keys = np.concatenate([k_p[:, g, :], k_r[:last_row + 1, g, :]], axis=0, dtype=np.float64)
+    vals = np.concatenate([v_p[:, g, :], v_r[:last_row + 1, g, :]], axis=0, dtype=np.float64)
     return keys, vals
 
 
@@ -149,7 +149,7 @@ def attend_bwd(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Optional[Sequence[i
 
 
 def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
-                heads: Sequence[int]) -> Dict[str, np.ndarray]:
+                heads: Sequence[int], batch_bytes: int = _BATCH_BYTES) -> Dict[str, np.ndarray]:
     """Forward and response-only backward of individual query rows: entry n is row rows[n]
     of query head heads[n] (one row of that head's query matrix), with everything the
     definition gives for it in one pass over its visible keys:
@@ -157,7 +157,8 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
     and the contributions of these query rows to dk_r [R][Hkv][d_qk], dv_r [R][Hkv][d_v]
     (per row and head, the formulas of attend_bwd).  Where the selection holds every head
     of rows j0..R-1, dk_r[j0:] and dv_r[j0:] are the full response-key gradients, as only
-    those rows see response keys >= j0."""
+    those rows see response keys >= j0.  batch_bytes bounds the fp64 scores held at once
+    (a larger batch reads the gathered keys fewer times)."""
     R, Hq, d_qk = q.shape
     P, Hkv, d_v = v_p.shape
     rows = np.asarray(rows, dtype=np.int64)
@@ -174,7 +175,7 @@ def attend_rows(q, k_p, v_p, k_r, v_r, d_o, tau: float, rows: Sequence[int],
             continue
         last = int(rows[sel].max())
         keys, vals = _visible(k_p, v_p, k_r, v_r, g, last)
-        for b in _row_batches(sel, keys.shape[0]):
+        for b in _row_batches(sel, keys.shape[0], batch_bytes):
             r, h = rows[b], heads[b]
             qb, dob = q[r, h, :], d_o[r, h, :]
             # the softmax and dS = p (dp - D) are formed in place: these arrays hold one
