@@ -179,5 +179,30 @@ def test_microbatch_equals_single_calls(dtype):
         st1 = G.stack_members([mem[kk]], rl)
         p1 = G.problem(w.P, rl, w.Hq, w.Hkv, w.d_qk, chunk, block, w.dtype, tau=w.tau)
         one = G.Run(p1, w.dtype, res["k_p"], res["v_p"], st1, [rl]).fwd().bwd().numpy()
-        for key in ("o", "lse", "dq", "dk", "dv"):
+        for key in ("o", "lse", "dq", "dk", "dv", "D"):
             np.testing.assert_array_equal(many[key][kk][:rl], one[key][0], err_msg=f"{key}[k={kk}]")
+
+
+def test_microbatch_full_size_group():
+    """The 2M group (P = 2,097,152, members of 2159 to 7666 rows) as one call with K = 8
+    gives every member exactly the bits of its own call, D included, and zeros in each
+    member's padding rows."""
+    from tests import _gpu as G
+    w = configs.FULL_P2M
+    lens = [int(r) for r in synth.response_lengths(w)]
+    res = synth.resident(w)
+    mem = [synth.member(w, g, R=r) for g, r in enumerate(lens)]
+    st = G.stack_members(mem, w.R)
+    prob = G.problem(w.P, w.R, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, K=len(lens), tau=w.tau)
+    print(f"[microbatch] full size K={len(lens)} R={lens}", flush=True)
+    many = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, lens).fwd().bwd().numpy()
+    for kk, rl in enumerate(lens):
+        print(f"[microbatch] member {kk} alone", flush=True)
+        p1 = G.problem(w.P, rl, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
+        one = G.Run(p1, w.dtype, res["k_p"], res["v_p"], G.stack_members([mem[kk]], rl), [rl]).fwd().bwd().numpy()
+        for key in ("o", "lse", "dq", "dk", "dv", "D"):
+            np.testing.assert_array_equal(many[key][kk][:rl], one[key][0], err_msg=f"{key}[k={kk}]")
+        assert np.all(many["o"][kk][rl:] == 0) and np.all(np.isneginf(many["lse"][kk][rl:]))
+        for key in ("dq", "dk", "dv", "D"):
+            assert np.all(many[key][kk][rl:] == 0), key
+
