@@ -62,8 +62,15 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   hipEvent_t a, b;
   hipError_t e = hipEventCreate(&a);
   if (e != hipSuccess) return e;
-  if ((e = hipEventCreate(&b)) != hipSuccess) return e;
-  if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
+  if ((e = hipEventCreate(&b)) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return e;
+  }
+  if ((e = hipEventRecord(a, s)) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    return e;
+  }
   e = launch();
   const hipError_t e2 = hipEventRecord(b, s);
   {
