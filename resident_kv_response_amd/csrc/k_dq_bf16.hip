@@ -61,7 +61,7 @@ __device__ __forceinline__ void dqr_scores(const Frag<D>& fr, const FarFrags<D>&
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     s = mfma32x32x16(fr.row(Kt, sub, ks), qf[ks], s);
-    dp = mfma32x32x16(far.row(Vt, sub, ks), of[ks], dp);
+    dp = mfma32x32x16(far.row_folded(Vt, sub, ks), of[ks], dp);
   }
 }
 
@@ -94,7 +94,7 @@ __device__ __forceinline__ void dqr_block_body(const Frag<D>& fr, const FarFrags
   auto load = [&](int i) -> bf16x8 {
     if (i < NX) return fr.trans_frag(Kx, subx, i & 1, i >> 1);
     const int j = i - NX;
-    return j < KS ? fr.row(Ky, suby, j) : far.row(Vy, suby, j - KS);
+    return j < KS ? fr.row(Ky, suby, j) : far.row_folded(Vy, suby, j - KS);
   };
   float p[16];
   uint32_t w[8];

@@ -284,23 +284,14 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
     const float* __restrict__ sts, float* __restrict__ dk_p, float* __restrict__ dv_p, int accumulate) {
   using C = PgCfg<D>;
   constexpr int KS = C::KS, DT = C::DT;
-  // Q tiles of the four stages first (below 64 KiB), then the dO tiles (read through
-  // biased offsets), then the statistics.
-  __shared__ __attribute__((aligned(1024))) char qt0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt3[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot3[C::TILE];
-  __shared__ __attribute__((aligned(16))) float sb0[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb1[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb2[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb3[2 * kPgStage];
-  char* const QT[4] = {qt0, qt1, qt2, qt3};
-  char* const OT[4] = {ot0, ot1, ot2, ot3};
-  float* const SB[4] = {sb0, sb1, sb2, sb3};
+  // One array, so the layout is fixed: the Q tiles of the four stages below 64 KiB (read
+  // through plain offsets), then the dO tiles (read through biased offsets), then the
+  // statistics.
+  __shared__ __attribute__((aligned(1024))) char lds[8 * C::TILE + 4 * 2 * kPgStage * sizeof(float)];
+  char* const QT[4] = {lds, lds + C::TILE, lds + 2 * C::TILE, lds + 3 * C::TILE};
+  char* const OT[4] = {lds + 4 * C::TILE, lds + 5 * C::TILE, lds + 6 * C::TILE, lds + 7 * C::TILE};
+  float* const st0 = reinterpret_cast<float*>(lds + 8 * C::TILE);
+  float* const SB[4] = {st0, st0 + 2 * kPgStage, st0 + 4 * kPgStage, st0 + 6 * kPgStage};
 
   const int64_t n_kt = (n_keys + C::KEYS - 1) / C::KEYS;
   const int64_t idx = xcd_work_index((int64_t)Hkv * n_kt);
@@ -482,21 +473,12 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
     float* __restrict__ dk_r, float* __restrict__ dv_r) {
   using C = PgCfg<D>;
   constexpr int KS = C::KS, DT = C::DT;
-  __shared__ __attribute__((aligned(1024))) char qt0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char qt3[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char ot3[C::TILE];
-  __shared__ __attribute__((aligned(16))) float sb0[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb1[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb2[2 * kPgStage];
-  __shared__ __attribute__((aligned(16))) float sb3[2 * kPgStage];
-  char* const QT[4] = {qt0, qt1, qt2, qt3};
-  char* const OT[4] = {ot0, ot1, ot2, ot3};
-  float* const SB[4] = {sb0, sb1, sb2, sb3};
+  // the same fixed layout as prompt_dkdv_bf16
+  __shared__ __attribute__((aligned(1024))) char lds[8 * C::TILE + 4 * 2 * kPgStage * sizeof(float)];
+  char* const QT[4] = {lds, lds + C::TILE, lds + 2 * C::TILE, lds + 3 * C::TILE};
+  char* const OT[4] = {lds + 4 * C::TILE, lds + 5 * C::TILE, lds + 6 * C::TILE, lds + 7 * C::TILE};
+  float* const st0 = reinterpret_cast<float*>(lds + 8 * C::TILE);
+  float* const SB[4] = {st0, st0 + 2 * kPgStage, st0 + 4 * kPgStage, st0 + 6 * kPgStage};
 
   // work item: (k, g) outer, key tiles inner (heaviest first); plain block order, so every
   // XCD receives a mix of long and short tiles
@@ -671,9 +653,9 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
     const int b = t & 3;
     const int sub = 1 - (u & 1);
     const int m_first = m_top - 32 * (u + 1);   // first flattened row of the subtile
-    const char* const qt = b == 0 ? qt0 : b == 1 ? qt1 : b == 2 ? qt2 : qt3;
-    const char* const ot = b == 0 ? ot0 : b == 1 ? ot1 : b == 2 ? ot2 : ot3;
-    const float* const sb = b == 0 ? sb0 : b == 1 ? sb1 : b == 2 ? sb2 : sb3;
+    const char* const qt = lds + b * C::TILE;
+    const char* const ot = lds + (4 + b) * C::TILE;
+    const float* const sb = st0 + 2 * kPgStage * b;
     float l2[16];
     f32x16 ndv, s, dp;
     pg_stats(sb, sub, l2, ndv);

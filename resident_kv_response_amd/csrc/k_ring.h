@@ -46,6 +46,15 @@ struct FarFrags {
   __device__ __forceinline__ bf16x8 row(const char* tile, int sub, int ks) const {
     return *reinterpret_cast<const bf16x8*>(tile + (rows[ks] - kBias) + sub * 32 * (D * 2));
   }
+  // The same read with the tile's part of the address formed as one constant,
+  // (tile - kBias + subtile offset), added to the biased register: the compiler then puts
+  // it in the read's offset field instead of adding the tile address to an unbiased copy
+  // of the register before every read.
+  __device__ __forceinline__ bf16x8 row_folded(const char* tile, int sub, int ks) const {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    const uint32_t c = lds_addr(tile) + (uint32_t)(sub * 32 * (D * 2)) - kBias;
+    return *reinterpret_cast<lds_bf16x8*>((uintptr_t)(rows[ks] + c));
+  }
   __device__ __forceinline__ bf16x8 trans_frag(const char* tile, int sub, int h2, int dt) const {
     const int rb = (sub * 32 + 16 * h2) * (D * 2);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (trans[dt][0] - kBias) + rb));
