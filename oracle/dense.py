@@ -26,8 +26,8 @@ Sources
     memory by lifetime" (update-boundary state).
 
 Because the chunked and block-wise method reaches exactly the plain attention result,
-`attend` and `attend_bwd` compute the plain definition: no chunks, no blocks, no online
-rescaling.  `chunk_partials` and `merge` follow the method's composition step for the
+`attend`, `attend_bwd` and `attend_rows` (the same for single query rows of one head)
+compute the plain definition: no chunks, no blocks, no online rescaling.  `chunk_partials` and `merge` follow the method's composition step for the
 functions that expose it.  Rows are processed in batches only to bound memory; each row
 is computed independently, as the definition has it.
 """
