@@ -140,6 +140,8 @@ class Problem:
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("rr_attn tensors must be GPU tensors (a host pointer would fault in a kernel)")
     if not t.is_contiguous():
         raise ValueError("rr_attn tensors must be contiguous")
     return t.data_ptr()

@@ -273,3 +273,13 @@ def test_empty_prompt_is_accepted_without_resident_pointers():
     kv = R.CResident(k_p=None, v_p=None, k_idx=None, P=0, version=0)
     rc, msg = _fwd(p, kv=kv, ws=None, ws_bytes=0)
     assert rc == R.RR_E_WORKSPACE, msg          # passes every check up to the workspace
+
+
+def test_binding_rejects_host_tensors():
+    # a host pointer handed to a kernel would fault: the binding refuses it before any call
+    import torch
+    x = torch.zeros(8, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        R.resident(x, x)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        R.rr_lse_merge(torch.zeros(2, 4, 64), torch.zeros(2, 4), torch.zeros(4, 64), torch.zeros(4))
