@@ -34,7 +34,10 @@
  *     asynchronously on it; no entry point synchronises except rr_profile_end.
  *   - Every argument is validated before the first launch.  A non-zero return means
  *     nothing was launched (except RR_E_HIP, raised by a failing launch);
- *     rr_last_error() returns a thread-local message describing the failure.
+ *     rr_last_error() returns a thread-local message describing the failure.  After the
+ *     shape checks, every non-NULL tensor pointer is looked up with
+ *     hipPointerGetAttributes: memory the GPU cannot access (plain host memory) returns
+ *     RR_E_PTR instead of faulting in a kernel.  Host memory pinned through HIP passes.
  *   - Layouts (K = responses in the microbatch, R = R_max = row stride):
  *       q      [K][R][Hq][d_qk]   dtype           (latent: same)
  *       k_r    [K][R][Hkv][d_qk]  dtype           (latent: response latent rows [K][R][d_qk])
@@ -72,6 +75,7 @@ extern "C" {
 #define RR_E_STALE        -7  /* resident version differs from the window's version   */
 #define RR_E_MISSING      -8  /* a member of the window was never accumulated         */
 #define RR_E_HIP          -9  /* a HIP call failed; see rr_last_error()               */
+#define RR_E_PTR         -10  /* a tensor pointer is memory the GPU cannot access     */
 
 /* ---- enums -------------------------------------------------------------------- */
 #define RR_F32   0            /* fp32 inputs, fp32 arithmetic throughout               */

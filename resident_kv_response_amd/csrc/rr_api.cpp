@@ -3,7 +3,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -84,6 +86,22 @@ int hip_fail(hipError_t e, const char* what) {
   return set_error(RR_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Every non-NULL tensor pointer must be memory the GPU can reach (device memory, or host
+// memory pinned through HIP): a plain host pointer would fault inside a kernel.  Checked
+// after validation, before the first launch.
+int check_dev(std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (const auto& np : ptrs) {
+    if (!np.second) continue;
+    hipPointerAttribute_t a;
+    const hipError_t e = hipPointerGetAttributes(&a, np.second);
+    if (e != hipSuccess) (void)hipGetLastError();
+    if (e != hipSuccess || a.type == hipMemoryTypeUnregistered ||
+        (a.type == hipMemoryTypeHost && a.devicePointer == nullptr))
+      return set_error(RR_E_PTR, "%s is not memory the GPU can access", np.first);
+  }
+  return RR_OK;
+}
+
 float* carve(void* base, size_t offset) {
   return reinterpret_cast<float*>(static_cast<char*>(base) + offset);
 }
@@ -155,6 +173,10 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   int rc = validate_fwd(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx, ws,
                         ws_bytes);
   if (rc) return rc;
+  if ((rc = check_dev({{"k_p", kv->k_p}, {"v_p", kv->v_p}, {"k_idx", kv->k_idx}, {"q", q}, {"k_r", k_r},
+                        {"v_r", v_r}, {"q_idx", q_idx}, {"o", o}, {"lse", lse}, {"part_o", part_o},
+                        {"part_lse", part_lse}, {"topk_idx", topk_idx}, {"ws", ws}})))
+    return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
@@ -204,6 +226,7 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
   clear_error();
   int rc = validate_merge(n_parts, rows, d_v, part_o, part_lse, o, lse);
   if (rc) return rc;
+  if ((rc = check_dev({{"part_o", part_o}, {"part_lse", part_lse}, {"o", o}, {"lse", lse}}))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("lse_merge", s, [&] {
     return launch_merge(n_parts, rows, d_v, part_o, part_lse, o, lse, nullptr, s);
@@ -220,6 +243,10 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   int rc = validate_bwd(p, kv, q, k_r, v_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r, accumulate,
                         block_idx, ws, ws_bytes);
   if (rc) return rc;
+  if ((rc = check_dev({{"k_p", kv->k_p}, {"v_p", kv->v_p}, {"q", q}, {"k_r", k_r}, {"v_r", v_r},
+                        {"topk_idx", topk_idx}, {"o", o}, {"lse", lse}, {"d_o", d_o}, {"dq", dq},
+                        {"dk_r", dk_r}, {"dv_r", dv_r}, {"ws", ws}})))
+    return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
@@ -299,6 +326,9 @@ int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void*
   int rc = validate_prompt_grads(p, kv, q, r_len, o, lse, d_o, key_lo, key_hi, dk_p, dv_p, accumulate, ws,
                                  ws_bytes);
   if (rc) return rc;
+  if ((rc = check_dev({{"k_p", kv->k_p}, {"v_p", kv->v_p}, {"q", q}, {"o", o}, {"lse", lse}, {"d_o", d_o},
+                        {"dk_p", dk_p}, {"dv_p", dv_p}, {"ws", ws}})))
+    return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
   const PgGeom pg = make_pg_geom(p, r_len, 0, p->R_max);
@@ -324,6 +354,7 @@ int rr_lastkv_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const f
   clear_error();
   int rc = validate_blend(rows, Hkv, d, dtype, alpha, x_layer, x_last, x_out);
   if (rc) return rc;
+  if ((rc = check_dev({{"alpha", alpha}, {"x_layer", x_layer}, {"x_last", x_last}, {"x_out", x_out}}))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("lastkv_blend", s, [&] {
     return launch_lastkv_blend(rows, Hkv, d, dtype, alpha, x_layer, x_last, x_out, s);
@@ -338,6 +369,9 @@ int rr_lastkv_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, con
   int rc = validate_blend_bwd(rows, Hkv, d, dtype, alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha,
                               accumulate);
   if (rc) return rc;
+  if ((rc = check_dev({{"alpha", alpha}, {"x_layer", x_layer}, {"x_last", x_last}, {"d_out", d_out},
+                        {"d_layer", d_layer}, {"d_last", d_last}, {"d_alpha", d_alpha}})))
+    return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed("lastkv_blend_bwd", s, [&] {
     return launch_lastkv_blend_bwd(rows, Hkv, d, dtype, alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha,
@@ -351,6 +385,8 @@ int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version, const float
   clear_error();
   int rc = validate_accum(acc, member_g, version, grads, n_elems);
   if (rc) return rc;
+  for (int i = 0; i < acc->n_bufs; ++i)
+    if ((rc = check_dev({{"accumulator buffer", acc->buf[i]}, {"grad", grads[i]}}))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int i = 0; i < acc->n_bufs; ++i) {
     hipError_t e = timed("grad_accum", s, [&] { return launch_axpy(acc->buf[i], grads[i], n_elems[i], scale, s); });

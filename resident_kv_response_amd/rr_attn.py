@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "librr_attn.so")
 
 RR_OK = 0
 RR_E_NULL, RR_E_SHAPE, RR_E_UNSUPPORTED, RR_E_WORKSPACE = -1, -2, -3, -4
-RR_E_RANGE, RR_E_DUPLICATE, RR_E_STALE, RR_E_MISSING, RR_E_HIP = -5, -6, -7, -8, -9
+RR_E_RANGE, RR_E_DUPLICATE, RR_E_STALE, RR_E_MISSING, RR_E_HIP, RR_E_PTR = -5, -6, -7, -8, -9, -10
 RR_F32, RR_BF16 = 0, 1
 RR_OP_FWD, RR_OP_BWD, RR_OP_PROMPT_GRADS = 0, 1, 2
 RR_MAX_K, RR_MAX_ACC = 64, 8

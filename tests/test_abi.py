@@ -283,3 +283,18 @@ def test_binding_rejects_host_tensors():
         R.resident(x, x)
     with pytest.raises(ValueError, match="GPU tensors"):
         R.rr_lse_merge(torch.zeros(2, 4, 64), torch.zeros(2, 4), torch.zeros(4, 64), torch.zeros(4))
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_gpu_present(), reason="passes made-up pointers past validation; CPU hosts only")
+def test_pointer_check_runs_before_any_launch():
+    # valid shapes with pointers the GPU cannot access: the call stops at the pointer check
+    # (RR_E_PTR), never at a launch
+    p = _prob()
+    rc, msg = _fwd(p, ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_FWD))
+    assert rc == R.RR_E_PTR, (rc, msg)
+    assert "not memory the GPU can access" in msg
