@@ -194,15 +194,15 @@ def run_dense(a, w) -> int:
         gs, rls, st, prob = mbs[b]
         og, lg, dqg, dkg, dvg = outs(len(gs), prob.R_max)
         R.rr_attn_fwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, o=og, lse=lg, ws=ws_f)
-        R.rr_attn_bwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, og, lg, st["d_o"], dqg, dkg, dvg,
-                      ws=ws_b)
+        tag = R.rr_attn_bwd(prob, kv, st["q"], st["k_r"], st["v_r"], rls, og, lg, st["d_o"], dqg, dkg, dvg,
+                            ws=ws_b)
         if full:
             R.rr_attn_prompt_grads(prob, kv, st["q"], rls, og, lg, st["d_o"], dk_p, dv_p,
                                    accumulate=1 if b > 0 else 0, ws=ws_pg)
         if win is not None:
             for i, g in enumerate(gs):
                 rg = rls[i]
-                R.rr_grad_accum(win, g, 1, [dqg[i, :rg], dkg[i, :rg], dvg[i, :rg]])
+                R.rr_grad_accum(win, g, tag, [dqg[i, :rg], dkg[i, :rg], dvg[i, :rg]])
 
     def step():
         for t in acc:

@@ -72,10 +72,12 @@ extern "C" {
 #define RR_E_WORKSPACE    -4  /* ws NULL or ws_bytes below rr_workspace_bytes()       */
 #define RR_E_RANGE        -5  /* member index outside [0, G)                          */
 #define RR_E_DUPLICATE    -6  /* member already accumulated in this window (a retry)  */
-#define RR_E_STALE        -7  /* resident version differs from the window's version   */
+#define RR_E_STALE        -7  /* gradients of another model version or prompt group   */
 #define RR_E_MISSING      -8  /* a member of the window was never accumulated         */
 #define RR_E_HIP          -9  /* a HIP call failed; see rr_last_error()               */
 #define RR_E_PTR         -10  /* a tensor pointer is memory the GPU cannot access     */
+#define RR_E_POISONED    -11  /* an accumulation launch failed part-way: the window's
+                                 accumulators hold part of a member; discard the window */
 
 /* ---- enums -------------------------------------------------------------------- */
 #define RR_F32   0            /* fp32 inputs, fp32 arithmetic throughout               */
@@ -187,6 +189,21 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv,
 int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
                  const float* part_lse, float* o, float* lse, void* stream);
 
+/* Identity of the resident state a backward read, written by rr_attn_bwd and checked by
+   rr_grad_accum: a member's gradients may only enter the accumulation window of the model
+   version and prompt group they were computed against.  Source: networkfinds.com/long-
+   context-rl-is-a-state-lifetime-problem, section "Preserve gradient semantics, not just
+   forward outputs" (every resident object has an owning model version; versions never
+   mix).  Host memory; the caller passes it on unchanged. */
+typedef struct rr_grad_tag {
+  uint64_t    version;   /* rr_resident.version of the state the backward read           */
+  const void* resident;  /* rr_resident.k_p of that state (its identity)                 */
+  int64_t     P;         /* rr_resident.P                                                */
+  uint64_t    seal;      /* check value the library computes over the three fields above;
+                            a tag that no backward wrote (zero-filled, edited, assembled
+                            by hand) fails rr_grad_accum                                  */
+} rr_grad_tag;
+
 /*
  * rr_attn_bwd - response-only backward.
  *
@@ -221,12 +238,14 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
  *               K * R_max * Hq floats hold D = dO . O, [K][R_max][Hq] fp32, for the rows
  *               the call covered (0 in padding rows; the entries of other rows are
  *               unspecified).
+ *   tag         host, may be NULL: on success, the identity of kv (version, k_p, P),
+ *               sealed, for rr_grad_accum.  Untouched on failure.
  */
 int rr_attn_bwd(const rr_problem* p, const rr_resident* kv,
                 const void* q, const void* k_r, const void* v_r, const int32_t* r_len,
                 const int32_t* topk_idx, const float* o, const float* lse, const void* d_o,
                 float* dq, float* dk_r, float* dv_r, int32_t accumulate, int32_t block_idx,
-                void* ws, size_t ws_bytes, void* stream);
+                void* ws, size_t ws_bytes, rr_grad_tag* tag, void* stream);
 
 /*
  * rr_attn_prompt_grads - full-sequence differential mode: the prompt-side gradient term
@@ -309,25 +328,38 @@ typedef struct rr_accum {
   float*   buf[RR_MAX_ACC];     /* device fp32 accumulators                            */
   int64_t  n[RR_MAX_ACC];       /* elements of each accumulator                        */
   int32_t  G;                   /* members in the window, >= 1                         */
-  uint64_t version;             /* resident version the window accumulates against    */
+  uint64_t version;             /* model version the window accumulates against       */
   uint8_t* seen;                /* host [G]; seen[g] = 1 once member g is accumulated  */
+  /* Written by the library; the caller zero-initialises them when opening a window.    */
+  const void* resident;         /* resident (k_p) of the first accepted member; every
+                                   later member must have read the same one           */
+  int64_t  resident_P;          /* its P                                               */
+  int32_t  poisoned;            /* 1 after a launch failed part-way (RR_E_POISONED)    */
 } rr_accum;
 
 /*
  * rr_grad_accum - buf[i][e] += scale * grads[i][e] for e < n_elems[i], i < n_bufs.
  * Positions beyond n_elems[i] are untouched (position-aligned accumulation of members
- * with different lengths).  Rejected without any launch: member_g outside [0, G)
- * (RR_E_RANGE), a member already seen (RR_E_DUPLICATE), version != acc->version
- * (RR_E_STALE), n_elems[i] > acc->n[i] (RR_E_SHAPE).  On success sets seen[member_g].
+ * with different lengths).
+ *   tag      the rr_grad_tag that rr_attn_bwd wrote for this member's gradients
  *   grads    host array [n_bufs] of device fp32 pointers
  *   n_elems  host array [n_bufs]
+ * Rejected without any launch: a poisoned window (RR_E_POISONED); member_g outside
+ * [0, G) (RR_E_RANGE); tag NULL (RR_E_NULL); a tag that fails its seal (RR_E_STALE: no
+ * backward wrote it); tag->version != acc->version (RR_E_STALE: the gradients were
+ * computed against a resident state of another model version); a resident other than
+ * the window's first member's (RR_E_STALE: prompt groups mixed); a member already seen
+ * (RR_E_DUPLICATE, a retry); n_elems[i] > acc->n[i] (RR_E_SHAPE).  On success sets
+ * seen[member_g] (and, for the first member, acc->resident / resident_P).  If a launch
+ * fails after buffer 0 was added, the window is marked poisoned and RR_E_POISONED is
+ * returned: its accumulators hold part of the member, so no retry can make it whole.
  */
-int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version,
+int rr_grad_accum(rr_accum* acc, int32_t member_g, const rr_grad_tag* tag,
                   const float* const* grads, const int64_t* n_elems, float scale,
                   void* stream);
 
 /* RR_OK if every member 0..G-1 has been accumulated, else RR_E_MISSING naming the first
-   missing member (a dropped branch).  Host only. */
+   missing member (a dropped branch), or RR_E_POISONED.  Host only. */
 int rr_accum_check_complete(const rr_accum* acc);
 
 /* Thread-local description of the last failure on this thread ("" if none). */

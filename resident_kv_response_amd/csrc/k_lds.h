@@ -19,6 +19,7 @@
 // T[base + j][c0 + r] for j = 0..3: four consecutive rows of its own column.
 #pragma once
 
+#include "k_addr.h"
 #include "k_common.h"
 
 namespace rr {
@@ -31,9 +32,7 @@ template <int D>
 struct Swz {
   static constexpr int G = D / 8;        // granules per row
   static constexpr int ROW_BYTES = D * 2;
-  static __device__ __forceinline__ int f(int r) {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
-  }
+  static __device__ __forceinline__ int f(int r) { return swz(D, r); }
   // byte offset of logical granule g of row r
   static __device__ __forceinline__ int off(int r, int g) { return r * ROW_BYTES + ((g ^ f(r)) << 4); }
 };
@@ -51,43 +50,22 @@ struct DirectLoad {
   static_assert(GRAN % (64 * WAVES) == 0, "tile must split evenly over the waves");
   static_assert(RPI == 4 || RPI == 8, "D must be 128 or 64");
 
-  uint32_t voff[4];     // lane byte offsets by instruction index mod 4 (row within the
-                        // instruction and swizzled granule): the swizzle depends on the row
-                        // mod 16 and 4 instructions advance 4 * RPI rows, a multiple of 16
-  int row0;             // first tile row of this wave
+  TileLoadPre pre;      // per-lane constants (k_addr.h)
 
   __device__ __forceinline__ void init(int64_t stride_bytes) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    row0 = wave * PER_WAVE * RPI;
-#pragma unroll
-    for (int par = 0; par < 4; ++par) {
-      const int r = row0 + RPI * par + lane / G;
-      const int g = (lane % G) ^ Swz<D>::f(r);
-      voff[par] = (uint32_t)((lane / G) * stride_bytes + g * 16);
-    }
+    pre = tile_load_pre(D, N_ROWS, WAVES, threadIdx.x >> 6, threadIdx.x & 63, stride_bytes);
   }
   // tile rows [0, N_ROWS) <- rows src_row0 .. of the stream; rows at or past row_end are
   // redirected to row_end - 1 (their values are masked by the caller).  Requires
-  // src_row0 < row_end.
+  // src_row0 < row_end.  Addresses from tile_load_at (k_addr.h).
   __device__ __forceinline__ void issue(char* tile, const uint16_t* stream, int64_t src_row0,
                                         int64_t row_end, int64_t stride_bytes) const {
-    const int lane = threadIdx.x & 63;
     const char* sbytes = reinterpret_cast<const char*>(stream);
     const bool full = src_row0 + N_ROWS <= row_end;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int p0 = (row0 / RPI + i) * 64;           // first granule of this instruction
-      const int64_t r_first = src_row0 + row0 + RPI * i;
-      const char* gp;
-      if (full) {
-        gp = sbytes + r_first * stride_bytes + voff[i & 3];
-      } else {
-        const int r_lane = lane / G;
-        const int64_t row = min(r_first + r_lane, row_end - 1);
-        const uint32_t gran = voff[i & 3] - (uint32_t)(r_lane * stride_bytes);   // g * 16
-        gp = sbytes + row * stride_bytes + gran;
-      }
-      __builtin_amdgcn_global_load_lds(gp, (lds_void*)(tile + p0 * 16), 16, 0, 0);
+      const TileLoadAt a = tile_load_at(pre, D, i, src_row0, row_end, stride_bytes, full);
+      __builtin_amdgcn_global_load_lds(sbytes + a.src_off, (lds_void*)(tile + a.lds_base), 16, 0, 0);
     }
   }
 };
@@ -96,7 +74,8 @@ struct DirectLoad {
 // a stream whose row 0 starts at the wave-uniform address `base`; rows at or past
 // `rows_valid` (>= 1) re-read row rows_valid - 1 (their values are masked by the caller).
 // Only the base is 64-bit; lane offsets are 32-bit, so N_ROWS * stride_bytes must stay
-// below 2^31.  The destination is a LDS byte address (see lds_addr).
+// below 2^31.  The destination is a LDS byte address (see lds_addr).  Addresses from
+// rows_load_pre / rows_load_at (k_addr.h).
 //
 // The loads are issued from inline assembly (M0 = the wave's LDS destination, then
 // global_load_lds_dwordx4 with a scalar base and a 32-bit lane offset).  The compiler
@@ -109,36 +88,24 @@ template <int D, int N_ROWS, int WAVES>
 struct DirectLoadRows {
   using DL = DirectLoad<D, N_ROWS, WAVES>;
   static constexpr int G = DL::G, RPI = DL::RPI, PER_WAVE = DL::PER_WAVE;
-  uint32_t gran[4];     // swizzled granule byte offset, by instruction index mod 4
-  int row0;             // first tile row of this wave
-  int r_lane;           // row of this lane inside an instruction
-  uint32_t lds0;        // byte offset of this wave's first granule in the tile (uniform)
+  RowsLoadPre pre;      // per-lane constants (k_addr.h)
 
   __device__ __forceinline__ void init() {
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    row0 = wave * PER_WAVE * RPI;
-    r_lane = lane / G;
-    lds0 = (uint32_t)(row0 / RPI) * 64u * 16u;
-#pragma unroll
-    for (int par = 0; par < 4; ++par) {
-      const int r = row0 + RPI * par + r_lane;
-      gran[par] = (uint32_t)(((lane % G) ^ Swz<D>::f(r)) << 4);
-    }
+    pre = rows_load_pre(D, N_ROWS, WAVES, wave, threadIdx.x & 63);
   }
   __device__ __forceinline__ void issue(uint32_t tile_lds, const char* base, int rows_valid,
                                         uint32_t stride_bytes) const {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int row = min(row0 + RPI * i + r_lane, rows_valid - 1);
-      const uint32_t off = (uint32_t)row * stride_bytes + gran[i & 3];
-      const uint32_t lds = tile_lds + lds0 + (uint32_t)i * 64u * 16u;
+      const RowsLoadAt a = rows_load_at(pre, D, i, rows_valid, stride_bytes);
+      const uint32_t lds = tile_lds + a.lds_base;
       asm volatile(
           "s_mov_b32 m0, %0\n\t"
           "s_nop 0\n\t"
           "global_load_lds_dwordx4 %1, %2"
           :
-          : "s"(lds), "v"(off), "s"(base)
+          : "s"(lds), "v"(a.src_off), "s"(base)
           : "memory", "m0");
     }
   }

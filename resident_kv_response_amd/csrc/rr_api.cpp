@@ -89,14 +89,26 @@ int hip_fail(hipError_t e, const char* what) {
 // Every non-NULL tensor pointer must be memory the GPU can reach (device memory, or host
 // memory pinned through HIP): a plain host pointer would fault inside a kernel.  Checked
 // after validation, before the first launch.
+PtrKind ptr_kind(hipMemoryType t) {
+  switch (t) {
+    case hipMemoryTypeUnregistered: return PtrKind::Unregistered;
+    case hipMemoryTypeHost: return PtrKind::Host;
+    case hipMemoryTypeDevice: return PtrKind::Device;
+    case hipMemoryTypeManaged: return PtrKind::Managed;
+    case hipMemoryTypeArray: return PtrKind::Array;
+    case hipMemoryTypeUnified: return PtrKind::Unified;
+    default: return PtrKind::Unknown;
+  }
+}
+
 int check_dev(std::initializer_list<std::pair<const char*, const void*>> ptrs) {
   for (const auto& np : ptrs) {
     if (!np.second) continue;
     hipPointerAttribute_t a;
+    memset(&a, 0, sizeof(a));
     const hipError_t e = hipPointerGetAttributes(&a, np.second);
     if (e != hipSuccess) (void)hipGetLastError();
-    if (e != hipSuccess || a.type == hipMemoryTypeUnregistered ||
-        (a.type == hipMemoryTypeHost && a.devicePointer == nullptr))
+    if (!ptr_accessible(e == hipSuccess, ptr_kind(a.type), a.devicePointer != nullptr))
       return set_error(RR_E_PTR, "%s is not memory the GPU can access", np.first);
   }
   return RR_OK;
@@ -238,8 +250,23 @@ int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o
 int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
                 const void* v_r, const int32_t* r_len, const int32_t* topk_idx, const float* o,
                 const float* lse, const void* d_o, float* dq, float* dk_r, float* dv_r,
-                int32_t accumulate, int32_t block_idx, void* ws, size_t ws_bytes, void* stream) {
+                int32_t accumulate, int32_t block_idx, void* ws, size_t ws_bytes, rr_grad_tag* tag,
+                void* stream) {
   clear_error();
+  int rc = rr_attn_bwd_impl(p, kv, q, k_r, v_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r, accumulate,
+                            block_idx, ws, ws_bytes, stream);
+  if (rc == RR_OK && tag) write_tag(kv, tag);
+  return rc;
+}
+
+}  // extern "C"
+
+namespace rr {
+
+int rr_attn_bwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                     const void* v_r, const int32_t* r_len, const int32_t* topk_idx, const float* o,
+                     const float* lse, const void* d_o, float* dq, float* dk_r, float* dv_r,
+                     int32_t accumulate, int32_t block_idx, void* ws, size_t ws_bytes, void* stream) {
   int rc = validate_bwd(p, kv, q, k_r, v_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r, accumulate,
                         block_idx, ws, ws_bytes);
   if (rc) return rc;
@@ -318,6 +345,10 @@ int rr_attn_bwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   return RR_OK;
 }
 
+}  // namespace rr
+
+extern "C" {
+
 int rr_attn_prompt_grads(const rr_problem* p, const rr_resident* kv, const void* q, const int32_t* r_len,
                          const float* o, const float* lse, const void* d_o, int64_t key_lo, int64_t key_hi,
                          float* dk_p, float* dv_p, int32_t accumulate, void* ws, size_t ws_bytes,
@@ -380,17 +411,27 @@ int rr_lastkv_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, con
   return e != hipSuccess ? hip_fail(e, "lastkv_blend_bwd") : RR_OK;
 }
 
-int rr_grad_accum(rr_accum* acc, int32_t member_g, uint64_t version, const float* const* grads,
+int rr_grad_accum(rr_accum* acc, int32_t member_g, const rr_grad_tag* tag, const float* const* grads,
                   const int64_t* n_elems, float scale, void* stream) {
   clear_error();
-  int rc = validate_accum(acc, member_g, version, grads, n_elems);
+  int rc = validate_accum(acc, member_g, tag, grads, n_elems);
   if (rc) return rc;
   for (int i = 0; i < acc->n_bufs; ++i)
     if ((rc = check_dev({{"accumulator buffer", acc->buf[i]}, {"grad", grads[i]}}))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int i = 0; i < acc->n_bufs; ++i) {
     hipError_t e = timed("grad_accum", s, [&] { return launch_axpy(acc->buf[i], grads[i], n_elems[i], scale, s); });
-    if (e != hipSuccess) return hip_fail(e, "grad_accum");
+    if (e != hipSuccess) {
+      if (i == 0) return hip_fail(e, "grad_accum");
+      // buffers 0 .. i-1 already hold this member: no retry can make the window whole
+      acc->poisoned = 1;
+      return set_error(RR_E_POISONED, "grad_accum: launch for buffer %d failed after %d buffers were added (%s); "
+                       "the window is poisoned", i, i, hipGetErrorString(e));
+    }
+  }
+  if (!acc->resident) {
+    acc->resident = tag->resident;
+    acc->resident_P = tag->P;
   }
   acc->seen[member_g] = 1;
   return RR_OK;

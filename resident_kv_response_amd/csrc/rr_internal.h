@@ -47,9 +47,20 @@ int validate_bwd(const rr_problem* p, const rr_resident* kv, const void* q, cons
                  const void* ws, size_t ws_bytes);
 int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
                    const float* part_lse, const float* o, const float* lse);
-int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
+int validate_accum(const rr_accum* acc, int32_t member_g, const rr_grad_tag* tag,
                    const float* const* grads, const int64_t* n_elems);
+uint64_t tag_seal(const rr_grad_tag* t);
+void write_tag(const rr_resident* kv, rr_grad_tag* t);
+
+// Kinds of memory a pointer lookup can report (the HIP runtime's memory types, mapped in
+// rr_api.cpp), and whether a kernel may dereference such a pointer.
+enum class PtrKind { Unregistered, Host, Device, Managed, Array, Unified, Unknown };
+bool ptr_accessible(bool query_ok, PtrKind kind, bool has_device_ptr);
 Geom make_geom(const rr_problem* p, const int32_t* r_len);
+int rr_attn_bwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                     const void* v_r, const int32_t* r_len, const int32_t* topk_idx, const float* o,
+                     const float* lse, const void* d_o, float* dq, float* dk_r, float* dv_r,
+                     int32_t accumulate, int32_t block_idx, void* ws, size_t ws_bytes, void* stream);
 
 // Packed row stream of the key-parallel K/V-gradient kernels: the rows of each KV head,
 // response after response.  Response k contributes its flattened rows m = r * grp + hh

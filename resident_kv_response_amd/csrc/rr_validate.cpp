@@ -62,6 +62,9 @@ int validate_problem(const rr_problem* p) {
   if (p->d_qk != p->d_v || (p->d_qk != 64 && p->d_qk != 128))
     return set_error(RR_E_UNSUPPORTED, "dense head dims must be d_qk == d_v in {64, 128} (got %d, %d)",
                      p->d_qk, p->d_v);
+  // 32-bit lane offsets of a 64-key stage of K/V rows ([P][Hkv][d] bf16 or fp32)
+  if ((int64_t)p->Hkv * p->d_qk >= ((int64_t)1 << 22))
+    return set_error(RR_E_SHAPE, "Hkv*d_qk must be below 2^22 (got %lld)", (long long)p->Hkv * p->d_qk);
   // 32-bit index products inside kernels: rows * heads * dims per response tensor
   const int64_t row_elems = (int64_t)p->K * p->R_max * p->Hq * (int64_t)p->d_qk;
   if (row_elems > (int64_t)1 << 31)
@@ -291,18 +294,49 @@ int validate_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part
   return RR_OK;
 }
 
-int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
+// Seal of a gradient tag: a 64-bit mix (splitmix64 finaliser) of the tag's fields and a
+// library constant.  It tells a tag that rr_attn_bwd wrote from one that it did not
+// (zero-filled, edited, assembled by hand); it is a consistency check, not a secret.
+static uint64_t mix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+uint64_t tag_seal(const rr_grad_tag* t) {
+  uint64_t h = mix64(0x7272617474616731ull ^ t->version);
+  h = mix64(h ^ (uint64_t)(uintptr_t)t->resident);
+  return mix64(h ^ (uint64_t)t->P);
+}
+
+void write_tag(const rr_resident* kv, rr_grad_tag* t) {
+  t->version = kv->version;
+  t->resident = kv->k_p;
+  t->P = kv->P;
+  t->seal = tag_seal(t);
+}
+
+int validate_accum(const rr_accum* acc, int32_t member_g, const rr_grad_tag* tag,
                    const float* const* grads, const int64_t* n_elems) {
   if (!acc) return set_error(RR_E_NULL, "accumulator is NULL");
+  if (acc->poisoned)
+    return set_error(RR_E_POISONED, "the window holds part of a member after a failed launch; discard it");
   if (acc->n_bufs < 1 || acc->n_bufs > RR_MAX_ACC)
     return set_error(RR_E_SHAPE, "n_bufs must be in [1, %d] (got %d)", RR_MAX_ACC, acc->n_bufs);
   if (acc->G < 1) return set_error(RR_E_SHAPE, "G must be >= 1");
   if (!acc->seen) return set_error(RR_E_NULL, "seen mask is NULL");
   if (member_g < 0 || member_g >= acc->G)
     return set_error(RR_E_RANGE, "member %d outside [0, G=%d)", member_g, acc->G);
-  if (version != acc->version)
+  if (!tag) return set_error(RR_E_NULL, "gradient tag is NULL");
+  if (tag->seal != tag_seal(tag))
+    return set_error(RR_E_STALE, "member %d: the gradient tag was not written by rr_attn_bwd", member_g);
+  if (tag->version != acc->version)
     return set_error(RR_E_STALE, "member %d computed against resident version %llu, window is at %llu",
-                     member_g, (unsigned long long)version, (unsigned long long)acc->version);
+                     member_g, (unsigned long long)tag->version, (unsigned long long)acc->version);
+  if (acc->resident && (tag->resident != acc->resident || tag->P != acc->resident_P))
+    return set_error(RR_E_STALE, "member %d computed against another resident prompt state than the window's",
+                     member_g);
   if (acc->seen[member_g])
     return set_error(RR_E_DUPLICATE, "member %d already accumulated in this window", member_g);
   if (!grads || !n_elems) return set_error(RR_E_NULL, "grads / n_elems is NULL");
@@ -314,6 +348,20 @@ int validate_accum(const rr_accum* acc, int32_t member_g, uint64_t version,
       return set_error(RR_E_NULL, "buffer %d: gradient or accumulator pointer is NULL", i);
   }
   return RR_OK;
+}
+
+bool ptr_accessible(bool query_ok, PtrKind kind, bool has_device_ptr) {
+  if (!query_ok) return false;
+  switch (kind) {
+    case PtrKind::Device:
+    case PtrKind::Managed:
+    case PtrKind::Unified:
+      return true;
+    case PtrKind::Host:        // host memory the GPU reaches only if it was pinned through HIP
+      return has_device_ptr;
+    default:                   // unregistered (plain host memory), arrays, unknown kinds
+      return false;
+  }
 }
 
 Geom make_geom(const rr_problem* p, const int32_t* r_len) {
@@ -365,6 +413,8 @@ int32_t rr_num_parts(const rr_problem* p) {
 
 int rr_accum_check_complete(const rr_accum* acc) {
   if (!acc || !acc->seen) return rr::set_error(RR_E_NULL, "accumulator or seen mask is NULL");
+  if (acc->poisoned)
+    return rr::set_error(RR_E_POISONED, "the window holds part of a member after a failed launch; discard it");
   for (int g = 0; g < acc->G; ++g)
     if (!acc->seen[g]) return rr::set_error(RR_E_MISSING, "member %d of %d was never accumulated", g, acc->G);
   return RR_OK;

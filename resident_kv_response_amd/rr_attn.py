@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "librr_attn.so")
 RR_OK = 0
 RR_E_NULL, RR_E_SHAPE, RR_E_UNSUPPORTED, RR_E_WORKSPACE = -1, -2, -3, -4
 RR_E_RANGE, RR_E_DUPLICATE, RR_E_STALE, RR_E_MISSING, RR_E_HIP, RR_E_PTR = -5, -6, -7, -8, -9, -10
+RR_E_POISONED = -11
 RR_F32, RR_BF16 = 0, 1
 RR_OP_FWD, RR_OP_BWD, RR_OP_PROMPT_GRADS = 0, 1, 2
 RR_MAX_K, RR_MAX_ACC = 64, 8
@@ -49,10 +50,16 @@ class CResident(ctypes.Structure):
                 ("P", ctypes.c_int64), ("version", ctypes.c_uint64)]
 
 
+class CGradTag(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_uint64), ("resident", ctypes.c_void_p), ("P", ctypes.c_int64),
+                ("seal", ctypes.c_uint64)]
+
+
 class CAccum(ctypes.Structure):
     _fields_ = [("n_bufs", ctypes.c_int32), ("buf", ctypes.c_void_p * RR_MAX_ACC),
                 ("n", ctypes.c_int64 * RR_MAX_ACC), ("G", ctypes.c_int32),
-                ("version", ctypes.c_uint64), ("seen", ctypes.POINTER(ctypes.c_uint8))]
+                ("version", ctypes.c_uint64), ("seen", ctypes.POINTER(ctypes.c_uint8)),
+                ("resident", ctypes.c_void_p), ("resident_P", ctypes.c_int64), ("poisoned", ctypes.c_int32)]
 
 
 class CProfileEntry(ctypes.Structure):
@@ -81,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.rr_lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp]
         L.rr_lse_merge.restype = ctypes.c_int
         L.rr_attn_bwd.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp, vp, vp,
-                                  ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+                                  ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz,
+                                  ctypes.POINTER(CGradTag), vp]
         L.rr_attn_bwd.restype = ctypes.c_int
         L.rr_attn_prompt_grads.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp,
                                            ctypes.POINTER(i32), vp, vp, vp, i64, i64, vp, vp, i32, vp, sz,
@@ -91,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.rr_lastkv_blend.restype = ctypes.c_int
         L.rr_lastkv_blend_bwd.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         L.rr_lastkv_blend_bwd.restype = ctypes.c_int
-        L.rr_grad_accum.argtypes = [ctypes.POINTER(CAccum), i32, ctypes.c_uint64,
+        L.rr_grad_accum.argtypes = [ctypes.POINTER(CAccum), i32, ctypes.POINTER(CGradTag),
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.c_float, vp]
         L.rr_grad_accum.restype = ctypes.c_int
         L.rr_accum_check_complete.argtypes = [ctypes.POINTER(CAccum)]
@@ -147,6 +155,74 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need(name: str, t: Optional[torch.Tensor], dtype: torch.dtype, numel: int) -> None:
+    """Refuse a tensor whose dtype differs from the layout the library reads or writes for
+    it (include/rr_attn.h), or that holds fewer elements than the layout: a kernel would
+    read or write past its end.  NULL (None) is left to the library's own checks."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"rr_attn: {name} has dtype {t.dtype}, the layout needs {dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"rr_attn: {name} has {t.numel()} elements, the layout needs {numel}")
+
+
+def _elem(p: "Problem") -> torch.dtype:
+    return torch.bfloat16 if p.dtype == RR_BF16 else torch.float32
+
+
+def _need_r_len(p: "Problem", r_len) -> None:
+    if len(r_len) != p.K:
+        raise ValueError(f"rr_attn: r_len has {len(r_len)} entries, the problem has K = {p.K}")
+
+
+def _need_resident(p: "Problem", kv: "CResident") -> None:
+    """Resident tensors built by resident(): element type and row width against p."""
+    meta = getattr(kv, "_meta", None)
+    if meta is None:
+        return
+    rows = max(int(kv.P), 0)
+
+    def need(name, got, dtype, n):
+        if got is not None and (got[0] != dtype or got[1] < n):
+            raise ValueError(f"rr_attn: resident {name} has {got[1]} elements of {got[0]}, "
+                             f"the layout needs {n} of {dtype}")
+
+    need("k_p", meta[0], _elem(p), rows * (p.d_qk if p.latent else p.Hkv * p.d_qk))
+    if not p.latent:
+        need("v_p", meta[1], _elem(p), rows * p.Hkv * p.d_v)
+    if p.topk > 0:
+        need("k_idx", meta[2], torch.float32, rows * p.idx_dim)
+
+
+def _need_rows(p: "Problem", q=None, k_r=None, v_r=None, d_o=None, o=None, lse=None, dq=None, dk_r=None,
+               dv_r=None, q_idx=None, topk_idx=None) -> None:
+    KR = p.K * p.R_max
+    et = _elem(p)
+    kw = p.d_qk if p.latent else p.Hkv * p.d_qk
+    vw = p.d_v if p.latent else p.Hkv * p.d_v
+    _need("q", q, et, KR * p.Hq * p.d_qk)
+    _need("k_r", k_r, et, KR * kw)
+    if not p.latent:
+        _need("v_r", v_r, et, KR * vw)
+    _need("d_o", d_o, et, KR * p.Hq * p.d_v)
+    _need("o", o, torch.float32, KR * p.Hq * p.d_v)
+    _need("lse", lse, torch.float32, KR * p.Hq)
+    _need("dq", dq, torch.float32, KR * p.Hq * p.d_qk)
+    _need("dk_r", dk_r, torch.float32, KR * kw)
+    _need("dv_r", dv_r, torch.float32, KR * vw)
+    _need("q_idx", q_idx, torch.float32, KR * p.idx_dim)
+    _need("topk_idx", topk_idx, torch.int32, KR * p.topk)
+
+
+def _need_ws(ws: Optional[torch.Tensor]) -> int:
+    if ws is None:
+        return 0
+    if ws.dtype != torch.uint8:
+        raise ValueError(f"rr_attn: workspace has dtype {ws.dtype}, expected torch.uint8")
+    return ws.numel()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -160,8 +236,10 @@ def _r_len(r_len: Sequence[int]):
 
 def resident(k_p: torch.Tensor, v_p: Optional[torch.Tensor], version: int = 0,
              k_idx: Optional[torch.Tensor] = None) -> CResident:
-    return CResident(k_p=_ptr(k_p), v_p=_ptr(v_p), k_idx=_ptr(k_idx), P=k_p.shape[0],
-                     version=version)
+    kv = CResident(k_p=_ptr(k_p), v_p=_ptr(v_p), k_idx=_ptr(k_idx), P=k_p.shape[0], version=version)
+    kv._meta = ((k_p.dtype, k_p.numel()), None if v_p is None else (v_p.dtype, v_p.numel()),
+                None if k_idx is None else (k_idx.dtype, k_idx.numel()))
+    return kv
 
 
 def rr_workspace_bytes(p: Problem, op: int) -> int:
@@ -188,29 +266,47 @@ def workspace(p: Problem, op: int, device) -> torch.Tensor:
 
 def rr_attn_fwd(p: Problem, kv: CResident, q, k_r, v_r, r_len, o=None, lse=None, part_o=None,
                 part_lse=None, q_idx=None, topk_idx=None, ws=None, stream=None) -> None:
+    _need_r_len(p, r_len)
+    _need_resident(p, kv)
+    _need_rows(p, q=q, k_r=k_r, v_r=v_r, o=o, lse=lse, q_idx=q_idx, topk_idx=topk_idx)
+    if part_o is not None or part_lse is not None:
+        n = rr_num_parts(p) * p.K * p.R_max * p.Hq
+        _need("part_o", part_o, torch.float32, n * p.d_v)
+        _need("part_lse", part_lse, torch.float32, n)
     cp = p.c()
-    wsp = _ptr(ws)
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    nbytes = _need_ws(ws)
     _check(lib().rr_attn_fwd(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _ptr(k_r), _ptr(v_r),
                              _r_len(r_len), _ptr(q_idx), _ptr(o), _ptr(lse), _ptr(part_o),
-                             _ptr(part_lse), _ptr(topk_idx), wsp, nbytes, _stream(stream)))
+                             _ptr(part_lse), _ptr(topk_idx), _ptr(ws), nbytes, _stream(stream)))
 
 
 def rr_lse_merge(part_o, part_lse, o, lse, stream=None) -> None:
     n_parts, rows, d_v = part_o.shape[0], part_lse[0].numel(), part_o.shape[-1]
+    _need("part_o", part_o, torch.float32, n_parts * rows * d_v)
+    _need("part_lse", part_lse, torch.float32, n_parts * rows)
+    _need("o", o, torch.float32, rows * d_v)
+    _need("lse", lse, torch.float32, rows)
     _check(lib().rr_lse_merge(n_parts, rows, d_v, _ptr(part_o), _ptr(part_lse), _ptr(o), _ptr(lse),
                               _stream(stream)))
 
 
 def rr_attn_bwd(p: Problem, kv: CResident, q, k_r, v_r, r_len, o, lse, d_o, dq, dk_r, dv_r,
                 accumulate: int = 0, block_idx: int = -1, topk_idx=None, ws=None,
-                stream=None) -> None:
+                stream=None) -> CGradTag:
+    """Response-only backward.  Returns the gradient tag (the identity of kv) that
+    rr_grad_accum checks against its window."""
+    _need_r_len(p, r_len)
+    _need_resident(p, kv)
+    _need_rows(p, q=q, k_r=k_r, v_r=v_r, d_o=d_o, o=o, lse=lse, dq=dq, dk_r=dk_r, dv_r=dv_r,
+               topk_idx=topk_idx)
     cp = p.c()
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    nbytes = _need_ws(ws)
+    tag = CGradTag()
     _check(lib().rr_attn_bwd(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _ptr(k_r), _ptr(v_r),
                              _r_len(r_len), _ptr(topk_idx), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq),
                              _ptr(dk_r), _ptr(dv_r), int(accumulate), int(block_idx), _ptr(ws),
-                             nbytes, _stream(stream)))
+                             nbytes, ctypes.byref(tag), _stream(stream)))
+    return tag
 
 
 def rr_attn_prompt_grads(p: Problem, kv: CResident, q, r_len, o, lse, d_o, dk_p, dv_p,
@@ -218,9 +314,14 @@ def rr_attn_prompt_grads(p: Problem, kv: CResident, q, r_len, o, lse, d_o, dk_p,
     """Full-sequence differential mode: dk_p, dv_p [key_hi - key_lo][Hkv][d] fp32 of the
     resident positions in key_range (default: the whole prompt), the prompt-side term
     that rr_attn_bwd drops."""
-    cp = p.c()
+    _need_r_len(p, r_len)
+    _need_resident(p, kv)
+    _need_rows(p, q=q, d_o=d_o, o=o, lse=lse)
     lo, hi = key_range if key_range is not None else (0, p.P)
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _need("dk_p", dk_p, torch.float32, max(hi - lo, 0) * p.Hkv * p.d_qk)
+    _need("dv_p", dv_p, torch.float32, max(hi - lo, 0) * p.Hkv * p.d_v)
+    cp = p.c()
+    nbytes = _need_ws(ws)
     _check(lib().rr_attn_prompt_grads(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _r_len(r_len),
                                       _ptr(o), _ptr(lse), _ptr(d_o), int(lo), int(hi), _ptr(dk_p),
                                       _ptr(dv_p), int(accumulate), _ptr(ws), nbytes, _stream(stream)))
@@ -238,6 +339,10 @@ def rr_lastkv_blend(alpha, x_layer, x_last, x_out, stream=None) -> None:
     """x_out = (1 - alpha_g) x_layer + alpha_g x_last over [rows][Hkv][d] (LastKV
     previous-chunk blending)."""
     rows, Hkv, d = x_layer.shape
+    n = rows * Hkv * d
+    _need("alpha", alpha, torch.float32, Hkv)
+    _need("x_last", x_last, x_layer.dtype, n)
+    _need("x_out", x_out, x_layer.dtype, n)
     _check(lib().rr_lastkv_blend(rows, Hkv, d, _dtype_code(x_layer), _ptr(alpha), _ptr(x_layer),
                                  _ptr(x_last), _ptr(x_out), _stream(stream)))
 
@@ -245,6 +350,13 @@ def rr_lastkv_blend(alpha, x_layer, x_last, x_out, stream=None) -> None:
 def rr_lastkv_blend_bwd(alpha, x_layer, x_last, d_out, d_layer, d_last, d_alpha, accumulate: int = 0,
                         stream=None) -> None:
     rows, Hkv, d = x_layer.shape
+    n = rows * Hkv * d
+    _need("alpha", alpha, torch.float32, Hkv)
+    _need("x_last", x_last, x_layer.dtype, n)
+    _need("d_out", d_out, torch.float32, n)
+    _need("d_layer", d_layer, torch.float32, n)
+    _need("d_last", d_last, torch.float32, n)
+    _need("d_alpha", d_alpha, torch.float32, Hkv)
     _check(lib().rr_lastkv_blend_bwd(rows, Hkv, d, _dtype_code(x_layer), _ptr(alpha), _ptr(x_layer),
                                      _ptr(x_last), _ptr(d_out), _ptr(d_layer), _ptr(d_last), _ptr(d_alpha),
                                      int(accumulate), _stream(stream)))
@@ -264,14 +376,28 @@ class Accum:
         self.c.G = G
         self.c.version = version
         self.c.seen = ctypes.cast(self.seen, ctypes.POINTER(ctypes.c_uint8))
+        for b in self.bufs:
+            if b.dtype != torch.float32:
+                raise ValueError(f"rr_accum buffers must be torch.float32 (got {b.dtype})")
 
 
-def rr_grad_accum(acc: Accum, member_g: int, version: int, grads: Sequence[torch.Tensor],
+def rr_grad_accum(acc: Accum, member_g: int, tag: CGradTag, grads: Sequence[torch.Tensor],
                   scale: float = 1.0, n_elems: Optional[Sequence[int]] = None, stream=None) -> None:
+    """acc += scale * grads of member member_g; tag is what rr_attn_bwd returned for them."""
     n = len(grads)
+    if n != acc.c.n_bufs:
+        raise ValueError(f"rr_grad_accum: {n} gradients for a window of {acc.c.n_bufs} buffers")
+    if n_elems is not None and len(n_elems) != n:
+        raise ValueError(f"rr_grad_accum: {len(n_elems)} element counts for {n} gradients")
+    for i, g in enumerate(grads):
+        if g.dtype != torch.float32:
+            raise ValueError(f"rr_grad_accum: gradient {i} has dtype {g.dtype}, expected torch.float32")
+        if n_elems is not None and not 0 <= int(n_elems[i]) <= g.numel():
+            raise ValueError(f"rr_grad_accum: n_elems[{i}] = {n_elems[i]} outside [0, {g.numel()}]")
     ptrs = (ctypes.c_void_p * n)(*[_ptr(g) for g in grads])
-    ns = (ctypes.c_int64 * n)(*[(g.numel() if n_elems is None else n_elems[i]) for i, g in enumerate(grads)])
-    _check(lib().rr_grad_accum(ctypes.byref(acc.c), member_g, version, ptrs, ns, scale, _stream(stream)))
+    ns = (ctypes.c_int64 * n)(*[(g.numel() if n_elems is None else int(n_elems[i])) for i, g in enumerate(grads)])
+    _check(lib().rr_grad_accum(ctypes.byref(acc.c), member_g, ctypes.byref(tag) if tag is not None else None,
+                               ptrs, ns, scale, _stream(stream)))
 
 
 def rr_accum_check_complete(acc: Accum) -> None:

@@ -91,7 +91,7 @@ def test_bwd_rejects_bad_arguments():
 
     def call(accumulate=0, block_idx=-1, ws=FAKE, ws_bytes=1 << 40, dq=FAKE):
         return L.rr_attn_bwd(ctypes.byref(cp), ctypes.byref(kv), FAKE, FAKE, FAKE, arr, None, FAKE,
-                             FAKE, FAKE, dq, FAKE, FAKE, accumulate, block_idx, ws, ws_bytes, None)
+                             FAKE, FAKE, dq, FAKE, FAKE, accumulate, block_idx, ws, ws_bytes, None, None)
 
     assert call(block_idx=1) == R.RR_E_SHAPE          # one block of 256 rows only
     assert call(block_idx=-2) == R.RR_E_SHAPE
@@ -171,28 +171,94 @@ def _accum(G=8, version=5):
     return acc, seen
 
 
-def _accum_call(acc, g, version, n=(100, 50)):
+def _accum_call(acc, g, tag, n=(100, 50)):
     L = R.lib()
     ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
     ns = (ctypes.c_int64 * 2)(*n)
-    return L.rr_grad_accum(ctypes.byref(acc), g, version, ptrs, ns, 1.0, None)
+    return L.rr_grad_accum(ctypes.byref(acc), g, ctypes.byref(tag) if tag is not None else None, ptrs, ns,
+                           1.0, None)
 
 
 def test_accumulator_hazards_are_rejected_before_launch():
+    # Only rr_attn_bwd writes a valid tag (sealed over the resident's version, k_p and P);
+    # here every tag is hand-made, so each call stops at a check before any launch.  The
+    # accepting path, the version and the prompt-group checks with real tags are covered by
+    # tests/native/host_checks.cpp and tests/test_gpu_invariants.py.
     acc, seen = _accum()
-    assert _accum_call(acc, 8, 5) == R.RR_E_RANGE           # member outside the window
-    assert _accum_call(acc, -1, 5) == R.RR_E_RANGE
-    assert _accum_call(acc, 3, 6) == R.RR_E_STALE           # mixed versions
-    seen[3] = 1                                              # member 3 already accumulated
-    assert _accum_call(acc, 3, 5) == R.RR_E_DUPLICATE       # a retry must not count twice
-    assert bytes(seen) == bytes([0, 0, 0, 1, 0, 0, 0, 0])   # rejections leave the mask alone
-    assert _accum_call(acc, 2, 5, n=(101, 50)) == R.RR_E_SHAPE
+    tag = R.CGradTag(version=5, resident=FAKE, P=4096, seal=1234)
+    assert _accum_call(acc, 8, tag) == R.RR_E_RANGE            # member outside the window
+    assert _accum_call(acc, -1, tag) == R.RR_E_RANGE
+    assert _accum_call(acc, 3, None) == R.RR_E_NULL            # no tag
     L = R.lib()
+    assert _accum_call(acc, 3, tag) == R.RR_E_STALE            # a tag no backward wrote
+    assert "not written by rr_attn_bwd" in L.rr_last_error().decode()
+    assert bytes(seen) == bytes(8)                              # rejections leave the mask alone
     assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_E_MISSING
     assert "member 0" in L.rr_last_error().decode()
     for g in range(8):
         seen[g] = 1
     assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_OK
+    acc.poisoned = 1                                            # after a failed partial launch
+    assert _accum_call(acc, 3, tag) == R.RR_E_POISONED
+    assert L.rr_accum_check_complete(ctypes.byref(acc)) == R.RR_E_POISONED
+
+
+def test_binding_checks_layouts_before_any_call():
+    """The binding refuses tensors whose dtype or element count differs from the layout
+    of include/rr_attn.h before calling the library (host tensors reach this check first,
+    so no GPU is needed; a correctly shaped host tensor is then refused as a host
+    pointer)."""
+    import torch
+    p = _prob(P=64, R_max=16, Hq=4, Hkv=1, d_qk=64, d_v=64, chunk=32, block=16, dtype=R.RR_BF16)
+    kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
+    bf = lambda *sh: torch.zeros(*sh, dtype=torch.bfloat16)
+    f32 = lambda *sh: torch.zeros(*sh, dtype=torch.float32)
+    q, kr, vr = bf(1, 16, 4, 64), bf(1, 16, 1, 64), bf(1, 16, 1, 64)
+    o, lse = f32(1, 16, 4, 64), f32(1, 16, 4)
+    with pytest.raises(ValueError, match="q has dtype"):
+        R.rr_attn_fwd(p, kv, f32(1, 16, 4, 64), kr, vr, [16], o=o, lse=lse)
+    with pytest.raises(ValueError, match="k_r has 512 elements"):
+        R.rr_attn_fwd(p, kv, q, bf(1, 8, 1, 64), vr, [16], o=o, lse=lse)
+    with pytest.raises(ValueError, match="o has 2048 elements"):
+        R.rr_attn_fwd(p, kv, q, kr, vr, [16], o=f32(1, 16, 4, 32), lse=lse)
+    with pytest.raises(ValueError, match="lse has dtype"):
+        R.rr_attn_fwd(p, kv, q, kr, vr, [16], o=o, lse=bf(1, 16, 4))
+    with pytest.raises(ValueError, match="r_len has 2 entries"):
+        R.rr_attn_fwd(p, kv, q, kr, vr, [16, 16], o=o, lse=lse)
+    with pytest.raises(ValueError, match="workspace has dtype"):
+        R.rr_attn_fwd(p, kv, q, kr, vr, [16], o=o, lse=lse, ws=f32(10))
+    with pytest.raises(ValueError, match="dq has 2048 elements"):
+        R.rr_attn_bwd(p, kv, q, kr, vr, [16], o, lse, bf(1, 16, 4, 64), f32(1, 8, 4, 64), f32(1, 16, 1, 64),
+                      f32(1, 16, 1, 64))
+    with pytest.raises(ValueError, match="d_o has dtype"):
+        R.rr_attn_bwd(p, kv, q, kr, vr, [16], o, lse, f32(1, 16, 4, 64), f32(1, 16, 4, 64), f32(1, 16, 1, 64),
+                      f32(1, 16, 1, 64))
+    with pytest.raises(ValueError, match="dk_p has"):
+        R.rr_attn_prompt_grads(p, kv, q, [16], o, lse, bf(1, 16, 4, 64), f32(63, 1, 64), f32(64, 1, 64))
+    with pytest.raises(ValueError, match="part_lse has"):
+        R.rr_lse_merge(f32(3, 16, 64), f32(2, 16), f32(16, 64), f32(16))
+    with pytest.raises(ValueError, match="x_out has"):
+        R.rr_lastkv_blend(f32(2), bf(8, 2, 16), bf(8, 2, 16), bf(7, 2, 16))
+    with pytest.raises(ValueError, match="d_alpha has"):
+        R.rr_lastkv_blend_bwd(f32(2), bf(8, 2, 16), bf(8, 2, 16), f32(8, 2, 16), None, None, f32(1))
+    # a correctly laid out call gets past the layout checks and stops at the host pointer
+    with pytest.raises(ValueError, match="GPU tensors"):
+        R.rr_attn_fwd(p, kv, q, kr, vr, [16], o=o, lse=lse)
+
+
+def test_binding_accumulator_arguments():
+    import torch
+    acc = R.Accum.__new__(R.Accum)           # a window handle without device buffers
+    acc.c = R.CAccum()
+    acc.c.n_bufs = 3
+    g = [torch.zeros(10)] * 2
+    with pytest.raises(ValueError, match="2 gradients for a window of 3"):
+        R.rr_grad_accum(acc, 0, R.CGradTag(), g)
+    acc.c.n_bufs = 2
+    with pytest.raises(ValueError, match="n_elems"):
+        R.rr_grad_accum(acc, 0, R.CGradTag(), g, n_elems=[10, 11])
+    with pytest.raises(ValueError, match="dtype"):
+        R.rr_grad_accum(acc, 0, R.CGradTag(), [torch.zeros(10, dtype=torch.float64)] * 2)
 
 
 def _latent(**kw):
