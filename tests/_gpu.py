@@ -13,6 +13,38 @@ from resident_kv_response_amd.synth import as_f64
 DEV = "cuda"
 
 
+GUARD = 64 << 10        # bytes of canary before and after every guarded output
+CANARY = 0xA5
+
+
+class Guarded:
+    """Output buffers placed between canary regions: each tensor is a view into a larger
+    byte buffer whose GUARD bytes before and after it hold CANARY.  check() fails if any
+    kernel wrote outside its output."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def alloc(self, name, shape, dtype, fill=None):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        t = raw[GUARD:GUARD + n].view(dtype).view(shape)
+        if fill is not None:
+            t.fill_(fill)
+        self.bufs.append((name, raw, n))
+        return t
+
+    def workspace(self, p, op):
+        return self.alloc(f"ws{op}", (max(1, R.rr_workspace_bytes(p, op)),), torch.uint8)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for name, raw, n in self.bufs:
+            head, tail = raw[:GUARD], raw[GUARD + n:]
+            assert bool(torch.all(head == CANARY)) and bool(torch.all(tail == CANARY)), \
+                f"a kernel wrote outside {name}"
+
+
 def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
@@ -46,23 +78,27 @@ def ws_D(ws, p):
 class Run:
     """Device copies of one problem's inputs plus its outputs."""
 
-    def __init__(self, prob: R.Problem, dtype: str, k_p, v_p, stacked, r_len, version=0):
+    def __init__(self, prob: R.Problem, dtype: str, k_p, v_p, stacked, r_len, version=0, dev_resident=None):
         self.p, self.dtype, self.r_len = prob, dtype, [int(x) for x in r_len]
-        self.k_p, self.v_p = to_dev(k_p, dtype), to_dev(v_p, dtype)
+        if dev_resident is not None:     # device copies shared with other runs (one prompt group)
+            self.k_p, self.v_p = dev_resident
+        else:
+            self.k_p, self.v_p = to_dev(k_p, dtype), to_dev(v_p, dtype)
         self.q = to_dev(stacked["q"], dtype)
         self.k_r = to_dev(stacked["k_r"], dtype)
         self.v_r = to_dev(stacked["v_r"], dtype)
         self.d_o = to_dev(stacked["d_o"], dtype)
         self.kv = R.resident(self.k_p, self.v_p, version=version)
         K, Rm, Hq, d = prob.K, prob.R_max, prob.Hq, prob.d_qk
-        f = dict(device=DEV, dtype=torch.float32)
-        self.o = torch.full((K, Rm, Hq, prob.d_v), float("nan"), **f)
-        self.lse = torch.full((K, Rm, Hq), float("nan"), **f)
-        self.dq = torch.full((K, Rm, Hq, d), float("nan"), **f)
-        self.dk = torch.full((K, Rm, prob.Hkv, d), float("nan"), **f)
-        self.dv = torch.full((K, Rm, prob.Hkv, prob.d_v), float("nan"), **f)
-        self.ws_f = R.workspace(prob, R.RR_OP_FWD, DEV)
-        self.ws_b = R.workspace(prob, R.RR_OP_BWD, DEV)
+        self.guard = gd = Guarded()
+        nan, f = float("nan"), torch.float32
+        self.o = gd.alloc("o", (K, Rm, Hq, prob.d_v), f, nan)
+        self.lse = gd.alloc("lse", (K, Rm, Hq), f, nan)
+        self.dq = gd.alloc("dq", (K, Rm, Hq, d), f, nan)
+        self.dk = gd.alloc("dk_r", (K, Rm, prob.Hkv, d), f, nan)
+        self.dv = gd.alloc("dv_r", (K, Rm, prob.Hkv, prob.d_v), f, nan)
+        self.ws_f = gd.workspace(prob, R.RR_OP_FWD)
+        self.ws_b = gd.workspace(prob, R.RR_OP_BWD)
 
     def fwd(self, **kw):
         R.rr_attn_fwd(self.p, self.kv, self.q, self.k_r, self.v_r, self.r_len, o=self.o, lse=self.lse,
@@ -70,14 +106,15 @@ class Run:
         return self
 
     def bwd(self, accumulate=0, block_idx=-1):
-        R.rr_attn_bwd(self.p, self.kv, self.q, self.k_r, self.v_r, self.r_len, self.o, self.lse,
-                      self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate,
-                      block_idx=block_idx, ws=self.ws_b)
+        self.tag = R.rr_attn_bwd(self.p, self.kv, self.q, self.k_r, self.v_r, self.r_len, self.o, self.lse,
+                                 self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate,
+                                 block_idx=block_idx, ws=self.ws_b)
         return self
 
     def numpy(self):
-        """Outputs, and D = dO . O [K][R_max][Hq] from the head of the backward's workspace."""
-        torch.cuda.synchronize()
+        """Outputs, and D = dO . O [K][R_max][Hq] from the head of the backward's workspace;
+        first checks that no kernel wrote outside an output or a workspace."""
+        self.guard.check()
         out = {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
         out["D"] = ws_D(self.ws_b, self.p)
         return out
@@ -106,15 +143,16 @@ class LatentRun:
         self.q_idx = to_dev(q_idx, "f32")
         self.kv = R.resident(self.latent_p, None, version=0, k_idx=self.k_idx)
         K, Rm = prob.K, prob.R_max
-        f = dict(device=DEV, dtype=torch.float32)
-        self.o = torch.full((K, Rm, prob.Hq, prob.d_v), float("nan"), **f)
-        self.lse = torch.full((K, Rm, prob.Hq), float("nan"), **f)
-        self.idx = torch.full((K, Rm, prob.topk), -7, device=DEV, dtype=torch.int32)
-        self.dq = torch.full((K, Rm, prob.Hq, prob.d_qk), float("nan"), **f)
-        self.dk = torch.full((K, Rm, prob.d_qk), float("nan"), **f)
-        self.dv = torch.full((K, Rm, prob.d_v), float("nan"), **f)
-        self.ws_f = R.workspace(prob, R.RR_OP_FWD, DEV)
-        self.ws_b = R.workspace(prob, R.RR_OP_BWD, DEV)
+        self.guard = gd = Guarded()
+        nan, f = float("nan"), torch.float32
+        self.o = gd.alloc("o", (K, Rm, prob.Hq, prob.d_v), f, nan)
+        self.lse = gd.alloc("lse", (K, Rm, prob.Hq), f, nan)
+        self.idx = gd.alloc("topk_idx", (K, Rm, prob.topk), torch.int32, -7)
+        self.dq = gd.alloc("dq", (K, Rm, prob.Hq, prob.d_qk), f, nan)
+        self.dk = gd.alloc("dk_r", (K, Rm, prob.d_qk), f, nan)
+        self.dv = gd.alloc("dv_r", (K, Rm, prob.d_v), f, nan)
+        self.ws_f = gd.workspace(prob, R.RR_OP_FWD)
+        self.ws_b = gd.workspace(prob, R.RR_OP_BWD)
 
     def fwd(self):
         R.rr_attn_fwd(self.p, self.kv, self.q, self.latent_r, None, self.r_len, o=self.o, lse=self.lse,
@@ -122,13 +160,13 @@ class LatentRun:
         return self
 
     def bwd(self, accumulate=0, block_idx=-1):
-        R.rr_attn_bwd(self.p, self.kv, self.q, self.latent_r, None, self.r_len, self.o, self.lse,
-                      self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate, block_idx=block_idx,
-                      topk_idx=self.idx, ws=self.ws_b)
+        self.tag = R.rr_attn_bwd(self.p, self.kv, self.q, self.latent_r, None, self.r_len, self.o, self.lse,
+                                 self.d_o, self.dq, self.dk, self.dv, accumulate=accumulate,
+                                 block_idx=block_idx, topk_idx=self.idx, ws=self.ws_b)
         return self
 
     def numpy(self):
-        torch.cuda.synchronize()
+        self.guard.check()
         out = {k: getattr(self, k).double().cpu().numpy() for k in ("o", "lse", "dq", "dk", "dv")}
         out["idx"] = self.idx.cpu().numpy()
         out["D"] = ws_D(self.ws_b, self.p)

@@ -112,49 +112,119 @@ def test_merge_handles_empty_parts():
     np.testing.assert_allclose(lse.cpu().numpy()[:4], rl_[:4], atol=1e-6)
 
 
-def test_serial_group_accumulation():
-    """G = 8 members replayed one at a time, accumulated into position-aligned fp32
-    buffers; equals the oracle's sum of 8 independent replays.  A retried member is
-    rejected, a stale version is rejected, a missing member is reported."""
+def _group_runs(w, seed_version=7):
+    """The members of a small group, each replayed against one shared resident prompt
+    state (one device copy of K_p, V_p with one version), plus the oracle's gradients."""
     from tests import _gpu as G
-    w = configs.FULL_P2M.with_(P=2048, R=192, r_min=64, chunk=512, block=64, seed=6001)
     res = synth.resident(w)
-    lens = synth.response_lengths(w)
-    Rm = w.R
-    acc_dq = torch.zeros(Rm, w.Hq, w.d_qk, device="cuda")
-    acc_dk = torch.zeros(Rm, w.Hkv, w.d_qk, device="cuda")
-    acc_dv = torch.zeros(Rm, w.Hkv, w.d_v, device="cuda")
-    win = R.Accum([acc_dq, acc_dk, acc_dv], G=w.G, version=7)
-    refs = {"dq": [], "dk_r": [], "dv_r": []}
-    peak = []
-    for g in range(w.G):
-        rg = int(lens[g])
+    lens = [int(x) for x in synth.response_lengths(w)]
+    shared = (G.to_dev(res["k_p"], w.dtype), G.to_dev(res["v_p"], w.dtype))
+    runs, refs = [], []
+    f = lambda x: synth.as_f64(x, w.dtype)
+    for g, rg in enumerate(lens):
         m = synth.member(w, g, R=rg)
         st = G.stack_members([m], rg)
         prob = G.problem(w.P, rg, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, tau=w.tau)
-        run = G.Run(prob, w.dtype, res["k_p"], res["v_p"], st, [rg], version=7).fwd().bwd()
-        R.rr_grad_accum(win, g, 7, [run.dq[0], run.dk[0], run.dv[0]])
+        runs.append(G.Run(prob, w.dtype, None, None, st, [rg], version=seed_version, dev_resident=shared))
+        refs.append(dense.attend_bwd(f(m["q"]), f(res["k_p"]), f(res["v_p"]), f(m["k_r"]), f(m["v_r"]),
+                                     f(m["d_o"]), w.tau))
+    return res, lens, shared, runs, refs
+
+
+def _window(w, Rm, version=7):
+    bufs = [torch.zeros(Rm, w.Hq, w.d_qk, device="cuda"), torch.zeros(Rm, w.Hkv, w.d_qk, device="cuda"),
+            torch.zeros(Rm, w.Hkv, w.d_v, device="cuda")]
+    return bufs, R.Accum(bufs, G=w.G, version=version)
+
+
+def test_serial_group_accumulation():
+    """G = 8 members replayed one at a time against one resident prompt state, accumulated
+    into position-aligned fp32 buffers; equals the oracle's sum of 8 independent replays.
+    Rejected before any launch: a retried member, gradients computed against a resident
+    of another model version, gradients computed against another prompt group's resident,
+    a tag that no backward wrote; a missing member is reported."""
+    from tests import _gpu as G
+    w = configs.FULL_P2M.with_(P=2048, R=192, r_min=64, chunk=512, block=64, seed=6001)
+    res, lens, shared, runs, refs = _group_runs(w)
+    bufs, win = _window(w, w.R)
+    for g, run in enumerate(runs):
+        run.fwd().bwd()
+        grads = [run.dq[0], run.dk[0], run.dv[0]]
+        R.rr_grad_accum(win, g, run.tag, grads)
         if g == 0:
             with pytest.raises(R.RRError) as e:
-                R.rr_grad_accum(win, 0, 7, [run.dq[0], run.dk[0], run.dv[0]])
+                R.rr_grad_accum(win, 0, run.tag, grads)
             assert e.value.code == R.RR_E_DUPLICATE
             with pytest.raises(R.RRError) as e:
                 R.rr_accum_check_complete(win)
             assert e.value.code == R.RR_E_MISSING
         if g == 1:
+            # the same member recomputed against the resident of a newer model version
+            st2 = G.stack_members([synth.member(w, 2, R=lens[2])], lens[2])
+            newer = G.Run(runs[2].p, w.dtype, None, None, st2, [lens[2]], version=8, dev_resident=shared)
+            newer.fwd().bwd()
             with pytest.raises(R.RRError) as e:
-                R.rr_grad_accum(win, 2, 8, [run.dq[0], run.dk[0], run.dv[0]])
+                R.rr_grad_accum(win, 2, newer.tag, [newer.dq[0], newer.dk[0], newer.dv[0]])
+            assert e.value.code == R.RR_E_STALE and "version" in str(e.value)
+            # ... against another prompt group's resident state (same version, other buffers)
+            other = G.Run(runs[2].p, w.dtype, res["k_p"], res["v_p"], st2, [lens[2]], version=7)
+            other.fwd().bwd()
+            with pytest.raises(R.RRError) as e:
+                R.rr_grad_accum(win, 2, other.tag, [other.dq[0], other.dk[0], other.dv[0]])
+            assert e.value.code == R.RR_E_STALE and "resident" in str(e.value)
+            # ... and a tag no backward wrote
+            forged = R.CGradTag(version=7, resident=run.tag.resident, P=run.tag.P, seal=0)
+            with pytest.raises(R.RRError) as e:
+                R.rr_grad_accum(win, 2, forged, [other.dq[0], other.dk[0], other.dv[0]])
             assert e.value.code == R.RR_E_STALE
-        f = lambda x: synth.as_f64(x, w.dtype)
-        gr = dense.attend_bwd(f(m["q"]), f(res["k_p"]), f(res["v_p"]), f(m["k_r"]), f(m["v_r"]),
-                              f(m["d_o"]), w.tau)
-        for key in refs:
-            refs[key].append(gr[key])
+            assert bytes(win.seen) == bytes([1, 1] + [0] * (w.G - 2))   # rejections leave the mask alone
     R.rr_accum_check_complete(win)
     torch.cuda.synchronize()
-    assert_bf16_close("acc dq", acc_dq.cpu().numpy(), dense.accumulate(refs["dq"], Rm))
-    assert_bf16_close("acc dk", acc_dk.cpu().numpy(), dense.accumulate(refs["dk_r"], Rm))
-    assert_bf16_close("acc dv", acc_dv.cpu().numpy(), dense.accumulate(refs["dv_r"], Rm))
+    assert_bf16_close("acc dq", bufs[0].cpu().numpy(), dense.accumulate([r["dq"] for r in refs], w.R))
+    assert_bf16_close("acc dk", bufs[1].cpu().numpy(), dense.accumulate([r["dk_r"] for r in refs], w.R))
+    assert_bf16_close("acc dv", bufs[2].cpu().numpy(), dense.accumulate([r["dv_r"] for r in refs], w.R))
+
+
+def test_accumulation_replay_order_and_microbatch():
+    """The update-boundary sum does not depend on the schedule that produced it: the same
+    G = 8 members replayed in a permuted order, and replayed as two microbatches of
+    K = 4 stacked responses each (other call sizes, other padding), accumulate to the
+    in-order serial result up to fp32 addition order, and to the oracle's sum."""
+    from tests import _gpu as G
+    w = configs.FULL_P2M.with_(P=2048, R=192, r_min=64, chunk=512, block=64, seed=6002)
+    res, lens, shared, runs, refs = _group_runs(w)
+    bufs_a, win_a = _window(w, w.R)
+    for g, run in enumerate(runs):
+        run.fwd().bwd()
+        R.rr_grad_accum(win_a, g, run.tag, [run.dq[0], run.dk[0], run.dv[0]])
+    order = [5, 2, 7, 0, 3, 6, 1, 4]
+    bufs_b, win_b = _window(w, w.R)
+    for g in order:
+        run = runs[g].fwd().bwd()
+        R.rr_grad_accum(win_b, g, run.tag, [run.dq[0], run.dk[0], run.dv[0]])
+    bufs_c, win_c = _window(w, w.R)
+    for b0 in (4, 0):                       # the later microbatch first
+        gs = list(range(b0, b0 + 4))
+        rm = max(lens[g] for g in gs)
+        mem = [synth.member(w, g, R=lens[g]) for g in gs]
+        prob = G.problem(w.P, rm, w.Hq, w.Hkv, w.d_qk, w.chunk, w.block, w.dtype, K=4, tau=w.tau)
+        mb = G.Run(prob, w.dtype, None, None, G.stack_members(mem, rm), [lens[g] for g in gs], version=7,
+                   dev_resident=shared).fwd().bwd()
+        for i, g in enumerate(gs):
+            rg = lens[g]
+            R.rr_grad_accum(win_c, g, mb.tag, [mb.dq[i, :rg], mb.dk[i, :rg], mb.dv[i, :rg]])
+    for win in (win_a, win_b, win_c):
+        R.rr_accum_check_complete(win)
+    torch.cuda.synchronize()
+    for n, key in enumerate(("dq", "dk_r", "dv_r")):
+        a = bufs_a[n].double().cpu().numpy()
+        scale = max(1.0, float(np.abs(a).max()))
+        for other in (bufs_b, bufs_c):
+            assert np.max(np.abs(other[n].double().cpu().numpy() - a)) <= 1e-5 * scale, key
+        assert_bf16_close(f"permuted acc {key}", bufs_b[n].cpu().numpy(),
+                          dense.accumulate([r[key] for r in refs], w.R))
+        assert_bf16_close(f"microbatch acc {key}", bufs_c[n].cpu().numpy(),
+                          dense.accumulate([r[key] for r in refs], w.R))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
