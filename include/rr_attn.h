@@ -362,6 +362,27 @@ int rr_grad_accum(rr_accum* acc, int32_t member_g, const rr_grad_tag* tag,
    missing member (a dropped branch), or RR_E_POISONED.  Host only. */
 int rr_accum_check_complete(const rr_accum* acc);
 
+/* ---- entry point for callers that cannot allocate --------------------------------- */
+/*
+ * rr_attn_fwd_static - rr_attn_fwd for callers that cannot allocate device memory or size
+ * a workspace at call time: code under HIP graph capture that must not allocate, tight
+ * serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments and results as rr_attn_fwd without ws / ws_bytes: the workspace is a
+ * static device array of RR_STATIC_SCRATCH_BYTES bytes that the library holds on each GPU
+ * it runs on until the process ends.  Calls no hipMalloc or hipFree.  A problem with
+ * rr_workspace_bytes(p, RR_OP_FWD) > RR_STATIC_SCRATCH_BYTES (and no partials export)
+ * returns RR_E_WORKSPACE before any launch.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (several streams or host threads) race on
+ * it, and the caller must order them.  The array keeps the last call's contents; nothing
+ * in it needs to start at zero.
+ */
+#define RR_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int rr_attn_fwd_static(const rr_problem* p, const rr_resident* kv,
+                       const void* q, const void* k_r, const void* v_r, const int32_t* r_len,
+                       const float* q_idx, float* o, float* lse, float* part_o, float* part_lse,
+                       int32_t* topk_idx, void* stream);
+
 /* Thread-local description of the last failure on this thread ("" if none). */
 const char* rr_last_error(void);
 

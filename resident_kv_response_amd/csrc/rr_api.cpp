@@ -120,6 +120,43 @@ float* carve(void* base, size_t offset) {
 
 }  // namespace
 
+}  // namespace rr
+
+// Workspace of rr_attn_fwd_static, for callers that cannot allocate: each GPU the library
+// runs on holds its own copy (in that device's code object) until the process ends.  In
+// host code `scratch` names a host-side stand-in; its device address on the current
+// device comes from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) char scratch[RR_STATIC_SCRATCH_BYTES];
+
+namespace rr {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call there).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return set_error(RR_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return RR_OK;
+}
+
+}  // namespace
+
 // Latent-page backward: D, then per-row dQ (which also writes the response pairs' P and dS),
 // then dK_r = tau dS^T Q and dV_r = P^T dO over the query rows of each block, last block
 // first.
@@ -182,12 +219,43 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const
                 float* part_o, float* part_lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
                 void* stream) {
   clear_error();
+  return rr_attn_fwd_impl(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx, ws, ws_bytes,
+                          stream, false);
+}
+
+int rr_attn_fwd_static(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                       const void* v_r, const int32_t* r_len, const float* q_idx, float* o, float* lse,
+                       float* part_o, float* part_lse, int32_t* topk_idx, void* stream) {
+  clear_error();
+  // every argument check first, against a stand-in workspace of the scratch's size, so an
+  // invalid call touches no device state
+  int rc = validate_fwd(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx,
+                        reinterpret_cast<void*>(static_cast<uintptr_t>(256)), RR_STATIC_SCRATCH_BYTES);
+  if (rc == RR_E_WORKSPACE)
+    return set_error(RR_E_WORKSPACE, "the problem needs %zu bytes of workspace; the static scratch holds %zu",
+                     ws_fwd_bytes(p, part_o != nullptr), (size_t)RR_STATIC_SCRATCH_BYTES);
+  if (rc) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  return rr_attn_fwd_impl(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx, ws,
+                          RR_STATIC_SCRATCH_BYTES, stream, true);
+}
+
+}  // extern "C"
+
+namespace rr {
+
+int rr_attn_fwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                     const void* v_r, const int32_t* r_len, const float* q_idx, float* o, float* lse,
+                     float* part_o, float* part_lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                     void* stream, bool ws_is_scratch) {
   int rc = validate_fwd(p, kv, q, k_r, v_r, r_len, q_idx, o, lse, part_o, part_lse, topk_idx, ws,
                         ws_bytes);
   if (rc) return rc;
+  // the static scratch is the library's own device memory: not looked up
   if ((rc = check_dev({{"k_p", kv->k_p}, {"v_p", kv->v_p}, {"k_idx", kv->k_idx}, {"q", q}, {"k_r", k_r},
                         {"v_r", v_r}, {"q_idx", q_idx}, {"o", o}, {"lse", lse}, {"part_o", part_o},
-                        {"part_lse", part_lse}, {"topk_idx", topk_idx}, {"ws", ws}})))
+                        {"part_lse", part_lse}, {"topk_idx", topk_idx}, {"ws", ws_is_scratch ? nullptr : ws}})))
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Geom g = make_geom(p, r_len);
@@ -232,6 +300,10 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv, const void* q, const
   }
   return RR_OK;
 }
+
+}  // namespace rr
+
+extern "C" {
 
 int rr_lse_merge(int32_t n_parts, int64_t rows, int32_t d_v, const float* part_o,
                  const float* part_lse, float* o, float* lse, void* stream) {

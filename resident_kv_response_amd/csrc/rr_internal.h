@@ -57,6 +57,10 @@ void write_tag(const rr_resident* kv, rr_grad_tag* t);
 enum class PtrKind { Unregistered, Host, Device, Managed, Array, Unified, Unknown };
 bool ptr_accessible(bool query_ok, PtrKind kind, bool has_device_ptr);
 Geom make_geom(const rr_problem* p, const int32_t* r_len);
+int rr_attn_fwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
+                     const void* v_r, const int32_t* r_len, const float* q_idx, float* o, float* lse,
+                     float* part_o, float* part_lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                     void* stream, bool ws_is_scratch);
 int rr_attn_bwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, const void* k_r,
                      const void* v_r, const int32_t* r_len, const int32_t* topk_idx, const float* o,
                      const float* lse, const void* d_o, float* dq, float* dk_r, float* dv_r,

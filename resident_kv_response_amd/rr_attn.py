@@ -26,8 +26,11 @@ RR_OP_FWD, RR_OP_BWD, RR_OP_PROMPT_GRADS = 0, 1, 2
 RR_MAX_K, RR_MAX_ACC = 64, 8
 RR_FLAG_SHARD_NO_RESPONSE = 1
 
+RR_STATIC_SCRATCH_BYTES = 64 << 20
+
 EXPORTS = ["rr_workspace_bytes", "rr_num_parts", "rr_attn_fwd", "rr_lse_merge", "rr_attn_bwd",
-           "rr_attn_prompt_grads", "rr_lastkv_blend", "rr_lastkv_blend_bwd", "rr_grad_accum", "rr_accum_check_complete", "rr_last_error", "rr_profile_begin",
+           "rr_attn_prompt_grads", "rr_lastkv_blend", "rr_lastkv_blend_bwd", "rr_grad_accum",
+           "rr_accum_check_complete", "rr_attn_fwd_static", "rr_last_error", "rr_profile_begin",
            "rr_profile_end"]
 
 
@@ -85,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.rr_attn_fwd.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp, vp, vp,
                                   ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rr_attn_fwd.restype = ctypes.c_int
+        L.rr_attn_fwd_static.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp, vp, vp,
+                                         ctypes.POINTER(i32), vp, vp, vp, vp, vp, vp, vp]
+        L.rr_attn_fwd_static.restype = ctypes.c_int
         L.rr_lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp]
         L.rr_lse_merge.restype = ctypes.c_int
         L.rr_attn_bwd.argtypes = [ctypes.POINTER(CProblem), ctypes.POINTER(CResident), vp, vp, vp,
@@ -278,6 +284,23 @@ def rr_attn_fwd(p: Problem, kv: CResident, q, k_r, v_r, r_len, o=None, lse=None,
     _check(lib().rr_attn_fwd(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _ptr(k_r), _ptr(v_r),
                              _r_len(r_len), _ptr(q_idx), _ptr(o), _ptr(lse), _ptr(part_o),
                              _ptr(part_lse), _ptr(topk_idx), _ptr(ws), nbytes, _stream(stream)))
+
+
+def rr_attn_fwd_static(p: Problem, kv: CResident, q, k_r, v_r, r_len, o=None, lse=None, part_o=None,
+                       part_lse=None, q_idx=None, topk_idx=None, stream=None) -> None:
+    """rr_attn_fwd with the library's static device scratch as workspace (allocates
+    nothing; problems whose workspace exceeds RR_STATIC_SCRATCH_BYTES are refused)."""
+    _need_r_len(p, r_len)
+    _need_resident(p, kv)
+    _need_rows(p, q=q, k_r=k_r, v_r=v_r, o=o, lse=lse, q_idx=q_idx, topk_idx=topk_idx)
+    if part_o is not None or part_lse is not None:
+        n = rr_num_parts(p) * p.K * p.R_max * p.Hq
+        _need("part_o", part_o, torch.float32, n * p.d_v)
+        _need("part_lse", part_lse, torch.float32, n)
+    cp = p.c()
+    _check(lib().rr_attn_fwd_static(ctypes.byref(cp), ctypes.byref(kv), _ptr(q), _ptr(k_r), _ptr(v_r),
+                                    _r_len(r_len), _ptr(q_idx), _ptr(o), _ptr(lse), _ptr(part_o),
+                                    _ptr(part_lse), _ptr(topk_idx), _stream(stream)))
 
 
 def rr_lse_merge(part_o, part_lse, o, lse, stream=None) -> None:

@@ -364,3 +364,21 @@ def test_pointer_check_runs_before_any_launch():
     rc, msg = _fwd(p, ws_bytes=R.rr_workspace_bytes(p, R.RR_OP_FWD))
     assert rc == R.RR_E_PTR, (rc, msg)
     assert "not memory the GPU can access" in msg
+
+
+def test_static_scratch_forward_refuses_oversized_problems():
+    # the workspace check runs before the scratch is looked up: no device is touched
+    L = R.lib()
+    p = _prob(P=131072, R_max=4096, Hq=32, Hkv=8, d_qk=128, d_v=128, chunk=8192, dtype=R.RR_BF16)
+    assert R.rr_workspace_bytes(p, R.RR_OP_FWD) > R.RR_STATIC_SCRATCH_BYTES
+    kv = R.CResident(k_p=FAKE, v_p=FAKE, k_idx=None, P=p.P, version=0)
+    cp = p.c()
+    arr = (ctypes.c_int32 * 1)(4096)
+    rc = L.rr_attn_fwd_static(ctypes.byref(cp), ctypes.byref(kv), FAKE, FAKE, FAKE, arr, None, FAKE, FAKE,
+                              None, None, None, None)
+    assert rc == R.RR_E_WORKSPACE
+    assert "static scratch" in L.rr_last_error().decode()
+    cp = _prob(R_max=0).c()          # invalid problems are refused the same way as rr_attn_fwd
+    rc = L.rr_attn_fwd_static(ctypes.byref(cp), ctypes.byref(kv), FAKE, FAKE, FAKE, arr, None, FAKE, FAKE,
+                              None, None, None, None)
+    assert rc == R.RR_E_SHAPE
