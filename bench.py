@@ -359,8 +359,7 @@ def run_dense(a, w) -> int:
 
 
 LATENT_SOURCES = {
-    "index_scores": ["k_topk.hip", "k_common.h"],
-    "topk_select": ["k_topk.hip", "k_common.h"],
+    "topk_select": ["k_topk.hip", "k_common.h", "k_lds.h", "k_addr.h"],
     "sparse_fwd": ["k_sparse.hip", "k_lds.h", "k_common.h"],
     "sparse_dq": ["k_sparse.hip", "k_lds.h", "k_common.h"],
     "xty_dk": ["k_sparse.hip", "k_lds.h", "k_common.h"],
@@ -378,9 +377,11 @@ def latent_kernel_model(w, R: int) -> dict:
     row = dk * 2
     q_b, do_b = R * H * dk * 2, R * H * dv * 2
     return {
-        "index_scores": {"flops": 2.0 * di * R * P, "peak": PEAK_F32_TFLOPS,
-                         "bytes": P * di * 4 + R * di * 4 + R * P * 4},
-        "topk_select": {"flops": 0.0, "peak": None, "bytes": R * P * 4 + R * k * 4},
+        # the index contraction (2 di flops per score) runs as three bf16 products per
+        # element on the matrix cores (hi/lo split), so its peak is a third of bf16's;
+        # bytes: the index keys and queries once, the selection out
+        "topk_select": {"flops": 2.0 * di * R * P, "peak": PEAK_BF16_TFLOPS / 3.0,
+                        "bytes": P * di * 4 + R * di * 4 + R * k * 4},
         "sparse_fwd": {"flops": H * (2.0 * dk + 2.0 * dv) * (n_p + n_r), "peak": PEAK_BF16_TFLOPS,
                        "bytes": n_p * row + R * row + q_b + R * H * (dv + 1) * 4 + R * k * 4},
         "sparse_dq": {"flops": H * (4.0 * dk + 2.0 * dv) * (n_p + n_r), "peak": PEAK_BF16_TFLOPS,

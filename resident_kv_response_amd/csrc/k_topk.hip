@@ -1,111 +1,78 @@
-// Sparse selection of the latent-page variant (gfx950): fp32 index scores and an exact
-// per-query top-k.
+// Sparse selection of the latent-page variant (gfx950): exact per-query top-k by fp32
+// index scores, with no score matrix.
 //
 // Source: ai.thesatyajit.com/articles/longstraw-2m-rl, section "Two incompatible
 // architectures, same transaction": DSA index-key pages are kept resident and the sparse
-// selection is rebuilt before attention.  Each query row i scores every prompt position
-// j by sigma_ij = q_idx_i . k_idx_j (fp32) and keeps the top k positions; equal scores
-// are ordered by position (lower first).
+// selection is rebuilt, across the owners of the prompt pages, before attention.  Query row
+// i scores prompt position j by sigma_ij = q_idx_i . k_idx_j and keeps the top k positions;
+// equal scores are ordered by position (lower first).
 //
-// index_scores_f32: sigma = q_idx k_idx^T on fp32 MFMA (v_mfma_f32_32x32x2_f32), written
-// to the caller's workspace with row stride ld.  A wave owns 32 query rows (their q_idx
-// fragments stay in registers) and streams 32-key tiles of k_idx straight from global
-// memory; lanes 0-31 contract index dims 0..63 and lanes 32-63 dims 64..127, so each
-// lane's operand is one contiguous 256-byte half row; the next tile's keys load while the
-// current tile's 64 MFMAs run.
+// The fp32 score.  sigma is one fixed-order chain of fused multiply-adds over the 128 index
+// dims (score_f32); every selection decision compares such scores.
 //
-// topk_select: one workgroup per query row; scores are mapped to order-preserving
-// unsigned keys.  Fast path (large rows): the key of a fixed descending rank in a sample
-// of 64 evenly spread runs of 128 scores is a threshold that keeps about 3k positions;
-// one pass over the row appends every position at or above it to a candidate list (one
-// LDS atomic per wave and store), a radix select over the candidates finds the k-th
-// largest key T and how many keys equal to T are taken, and the chosen positions are
-// sorted in LDS.  The threshold only decides how much work the row takes, never which
-// positions are chosen: a row whose candidate count falls outside [k, cap] (or with too
-// many keys equal to T) runs the exact full-row path, radix passes over the whole row
-// followed by a pass over contiguous per-thread ranges that writes positions in order.
-#include "k_common.h"
+// Fast path (P >= kScreenMinP), four launches:
+//   idx_screen<true>   scores of kTopkSample sample positions per row (64 runs of 128);
+//   idx_thresh         per row, the sample score of a fixed descending rank: a threshold
+//                      t expected to keep about 3k positions;
+//   idx_screen<false>  every (row, position) screened by the bf16 products
+//                      s~ = qh.kh + qh.kl + ql.kh (qh, ql: bf16 hi and lo parts of the fp32
+//                      values, bf16 MFMA, fp32 accumulation); each key range (an owner of
+//                      prompt pages) appends its positions with s~ >= t to the row's
+//                      candidate list, and records the largest key norm it saw;
+//   idx_select         per row, the exact selection among the candidates.
+// The bound.  |s~ - sigma| <= C ||q_i|| max_j ||k_j|| with C = 1e-4 (the hi/lo split leaves
+// terms of at most 3 * 2^-18 |q||k|, the fp32 accumulation of 384 bf16 products at most
+// 408 * 2^-23, the fp32 chain of sigma itself 128 * 2^-24, all relative to
+// sum |q_d k_d| <= ||q|| ||k||: 6.8e-5 in all).  Let s_k be the k-th largest s~ among the
+// candidates.  If t <= s_k - 2B (B the bound of the row), then every position with
+// s~ >= s_k - 2B is a candidate, sigma_(k) (the k-th largest sigma) lies in
+// [s_k - B, s_k + B], positions with s~ > s_k + 2B are chosen, positions with s~ < s_k - 2B
+// are not, and the positions in between (the band) are scored in fp32 and ranked by
+// (sigma, position) for the remaining places.  The result is exactly the top k by sigma.
+// A row with fewer than k or more than cap candidates, t > s_k - 2B, or more than
+// kTopkSortMax positions in the band takes the exact full-row path: radix passes over
+// sigma of every position, computed on the fly.  The threshold and the screen decide only
+// how much work a row takes, never which positions it gets.
+#include "k_lds.h"
 #include "kernels.h"
 
 namespace rr {
 
 constexpr int kIdxDim = 128;
 constexpr int kTopkThreads = 512, kTopkWaves = kTopkThreads / 64;
-constexpr int kEqMax = kTopkSample - kTopkSortMax;   // positions tied at T kept for sorting
+constexpr float kScreenBoundC = 1.0e-4f;     // |s~ - sigma| <= C ||q|| max ||k|| (see above)
+constexpr int kSampleRuns = 64, kSampleRunKeys = 128;
+constexpr int kSampleTiles = kTopkSample / kScreenKeys;   // 256 sample tiles of 32 keys
 
-__global__ __launch_bounds__(256) void index_scores_f32(const float* __restrict__ q_idx,
-                                                        const float* __restrict__ k_idx,
-                                                        float* __restrict__ sigma, int64_t ld,
-                                                        int rows, int64_t P, int key_tiles_per_wg) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, col = lane & 31;
-  const int n_row_tiles = (rows + 127) / 128;
-  const int rt = blockIdx.x % n_row_tiles;
-  const int64_t kt0 = (int64_t)(blockIdx.x / n_row_tiles) * key_tiles_per_wg;
-  const int64_t n_kt = (P + 31) / 32;
-  const int row0 = rt * 128 + wave * 32;
-  if (row0 >= rows) return;
+// The fp32 index score: fused multiply-adds over dims 0..127 in order.  q in LDS or
+// registers (read 128 times), k a row of the resident index keys.
+__device__ __forceinline__ float score_f32(const float* q, const float* krow) {
+  const float4* k4 = reinterpret_cast<const float4*>(krow);
+  float s = 0.0f;
+#pragma unroll 8
+  for (int v = 0; v < kIdxDim / 4; ++v) {
+    const float4 x = k4[v];
+    s = fmaf(q[4 * v + 0], x.x, s);
+    s = fmaf(q[4 * v + 1], x.y, s);
+    s = fmaf(q[4 * v + 2], x.z, s);
+    s = fmaf(q[4 * v + 3], x.w, s);
+  }
+  return s;
+}
 
-  // A fragments: q_idx[row0 + col][64h + s], s = 0..63
-  float qa[64];
-  {
-    const int r = min(row0 + col, rows - 1);
-    const float4* src = reinterpret_cast<const float4*>(q_idx + (int64_t)r * kIdxDim + 64 * h);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float4 x = src[v];
-      qa[4 * v + 0] = x.x;
-      qa[4 * v + 1] = x.y;
-      qa[4 * v + 2] = x.z;
-      qa[4 * v + 3] = x.w;
-    }
-  }
-  const int64_t kt_end = min(n_kt, kt0 + key_tiles_per_wg);
-  const bool full_rows = row0 + 32 <= rows;
-  // B fragments of key tile kt: k_idx[kt*32 + col][64h + s], s = 0..63 (a 256-byte half
-  // row per lane); keys past P are redirected to P - 1 and not stored
-  auto load_keys = [&](int64_t kt, float (&kb)[64]) {
-    const int64_t key = kt * 32 + col;
-    const int64_t kk = key < P ? key : P - 1;
-    const float4* src = reinterpret_cast<const float4*>(k_idx + kk * kIdxDim + 64 * h);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float4 x = src[v];
-      kb[4 * v + 0] = x.x;
-      kb[4 * v + 1] = x.y;
-      kb[4 * v + 2] = x.z;
-      kb[4 * v + 3] = x.w;
-    }
-  };
-  // scores of tile kt from kb while the next tile's keys load into kn
-  auto tile = [&](int64_t kt, const float (&kb)[64], float (&kn)[64]) {
-    if (kt + 1 < kt_end) load_keys(kt + 1, kn);
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 64; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s], kb[s], acc, 0, 0, 0);
-    const int64_t key = kt * 32 + col;
-    if (key < P) {
-      float* dst = sigma + (int64_t)row0 * ld + key;
-      if (full_rows) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(int64_t)((i >> 2) * 8 + 4 * h + (i & 3)) * ld] = acc[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i >> 2) * 8 + 4 * h + (i & 3);
-          if (row0 + r < rows) dst[(int64_t)r * ld] = acc[i];
-        }
-      }
-    }
-  };
-  float ka[64], kb2[64];
-  if (kt0 < kt_end) load_keys(kt0, ka);
-  for (int64_t kt = kt0; kt < kt_end; kt += 2) {
-    tile(kt, ka, kb2);
-    if (kt + 1 < kt_end) tile(kt + 1, kb2, ka);
-  }
+// First key of sample tile v: run v / 4 (64 runs of 128 keys spread over [0, P)),
+// tile v % 4 of the run.  Runs start on 32-key boundaries and end below P.
+__device__ __forceinline__ int64_t sample_tile_key0(int v, int64_t P) {
+  const int run = v >> 2;
+  const int64_t start = ((int64_t)run * (P - kSampleRunKeys) / (kSampleRuns - 1)) & ~(int64_t)(kScreenKeys - 1);
+  return start + (int64_t)(v & 3) * kScreenKeys;
+}
+
+// fp32 -> bf16 hi part (round to nearest even) and the bf16 rounding of the remainder.
+__device__ __forceinline__ void split_bf16(float x, float& hi, float& lo) {
+  const uint32_t b = pack_bf16x2(x, 0.0f);
+  hi = __uint_as_float(b << 16);
+  lo = x - hi;   // exact in fp32
 }
 
 // Order-preserving map of an fp32 score to an unsigned key (larger score -> larger key);
@@ -114,6 +81,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t b = __float_as_uint(f);
   if ((b & 0x7FFFFFFFu) == 0) return 0x80000000u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Inverse of order_key (the score a key stands for; both zeros map to +0).
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // Exclusive scan over the workgroup's threads (in thread order); returns the exclusive
@@ -145,6 +117,7 @@ struct TopkShared {
   int n_cand, n_gt, n_eq;
   uint32_t cmax;
 };
+
 
 // The `rank`-th largest (1-based) of n keys whose values lie below 2^nbits, by radix
 // passes of up to 11 bits from the top: returns it in T and, in need, how many keys equal
@@ -219,38 +192,6 @@ __device__ __forceinline__ int pow2_ceil(int n) {
   return p;
 }
 
-// Exact selection over the whole row: radix passes, then a pass over contiguous
-// per-thread ranges (a block-wide scan gives each thread its output offset) that writes
-// the chosen positions in ascending order.
-__device__ void full_row_select(const float* srow, int64_t P, int k, int32_t* out, TopkShared& sh) {
-  const int tid = threadIdx.x;
-  uint32_t T;
-  int need;
-  radix_kth([&](int64_t j) { return order_key(srow[j]); }, P, k, 32, sh, T, need);
-  const int64_t chunk = (P + kTopkThreads - 1) / kTopkThreads;
-  const int64_t j0 = min(P, chunk * tid), j1 = min(P, j0 + chunk);
-  int n_gt = 0, n_eq = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t u = order_key(srow[j]);
-    n_gt += u > T;
-    n_eq += u == T;
-  }
-  int tot;
-  const int eq_base = block_exclusive_scan(n_eq, sh.scan, &tot);
-  const int eq_take = max(0, min(n_eq, need - eq_base));
-  const int out_base = block_exclusive_scan(n_gt + eq_take, sh.scan, &tot);
-  int pos = out_base, eq_seen = 0;
-  for (int64_t j = j0; j < j1 && pos < out_base + n_gt + eq_take && pos < k; ++j) {
-    const uint32_t u = order_key(srow[j]);
-    if (u > T) {
-      out[pos++] = (int32_t)j;
-    } else if (u == T) {
-      if (eq_seen < eq_take) out[pos++] = (int32_t)j;
-      ++eq_seen;
-    }
-  }
-}
-
 // Wave-aggregated append: lanes with pred set get consecutive slots from *counter.
 __device__ __forceinline__ int wave_append_slot(bool pred, int* counter) {
   const int lane = threadIdx.x & 63;
@@ -261,180 +202,387 @@ __device__ __forceinline__ int wave_append_slot(bool pred, int* counter) {
   return base + __popcll(m & ((1ull << lane) - 1));
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_select(const float* __restrict__ sigma, int64_t ld,
-                                                            int64_t P, int k, Geom g,
-                                                            int32_t* __restrict__ idx_out,
-                                                            uint32_t* __restrict__ cand_key,
-                                                            int32_t* __restrict__ cand_pos, int fast,
-                                                            int sample_rank, int cap) {
+
+// The screen.  One workgroup = 256 query rows (8 waves of 32) x a range of 32-key tiles.
+// Per tile: the fp32 index keys are loaded (thread t: key t / 16, dims 8 (t % 16) .. +8),
+// split into bf16 hi and lo parts and stored in two swizzled LDS tiles; each wave forms
+// s~^T = Kh Qh^T + Kl Qh^T + Kh Ql^T (keys x rows, 24 MFMAs), its lanes holding one row
+// each.  SAMPLE: writes s~ of the sample tiles to samp[row][32 v + key].  Otherwise:
+// appends (order key of s~, position) of every s~ >= thr[row] to the row's candidates (one
+// atomic add per lane with a pass), and the key range's largest key norm to knorm[split]
+// (row tile 0 only).
+template <bool SAMPLE>
+__global__ __launch_bounds__(512, 1) void idx_screen(const float* __restrict__ q_idx, const float* __restrict__ k_idx,
+                                                     int64_t P, int rows, int n_row_tiles, int n_groups,
+                                                     int64_t tiles_per_group, Geom g, const float* __restrict__ thr,
+                                                     int* __restrict__ cnt, uint32_t* __restrict__ cand_key,
+                                                     int32_t* __restrict__ cand_pos, int cap,
+                                                     float* __restrict__ samp, float* __restrict__ knorm) {
+  __shared__ __attribute__((aligned(1024))) char kh0[kScreenKeys * kIdxDim * 2];
+  __shared__ __attribute__((aligned(1024))) char kh1[kScreenKeys * kIdxDim * 2];
+  __shared__ __attribute__((aligned(1024))) char kl0[kScreenKeys * kIdxDim * 2];
+  __shared__ __attribute__((aligned(1024))) char kl1[kScreenKeys * kIdxDim * 2];
+  __shared__ float wmax[16];
+  const int64_t item = xcd_work_index((int64_t)n_row_tiles * n_groups);
+  if (item < 0) return;
+  const int rt = (int)(item % n_row_tiles);
+  const int grp = (int)(item / n_row_tiles);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, col = lane & 31;
+  const int row = rt * kScreenRows + wave * 32 + col;
+  bool live = row < rows;
+  if (live) {
+    const int kk = row / g.R, r = row % g.R;
+    live = r < g.r_len[kk];
+  }
+  // B operands: q[row][16 ks + 8 h .. +8], hi and lo parts
+  bf16x8 qh[8], ql[8];
+  {
+    const float* qr = q_idx + (int64_t)(live ? row : 0) * kIdxDim;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qr + 16 * ks + 8 * hl);
+      const float4 b = *reinterpret_cast<const float4*>(qr + 16 * ks + 8 * hl + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      float h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        split_bf16(live ? x[e] : 0.0f, h[e], l[e]);
+      }
+      qh[ks] = as_bf16x8(make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                                    pack_bf16x2(h[6], h[7])));
+      ql[ks] = as_bf16x8(make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]), pack_bf16x2(l[4], l[5]),
+                                    pack_bf16x2(l[6], l[7])));
+    }
+  }
+  const float t_row = SAMPLE || !live ? INFINITY : thr[row];
+  const int64_t u0 = (int64_t)grp * tiles_per_group;
+  const int64_t n_tiles_all = SAMPLE ? kSampleTiles : (P + kScreenKeys - 1) / kScreenKeys;
+  const int64_t u1 = min(n_tiles_all, u0 + tiles_per_group);
+  const bool norms = !SAMPLE && rt == 0;
+  const int ld_key = tid >> 4, ld_g = tid & 15;       // this thread's key and 8-dim group
+  auto key0_of = [&](int64_t u) -> int64_t { return SAMPLE ? sample_tile_key0((int)u, P) : u * kScreenKeys; };
+  float4 ka, kb;
+  auto load = [&](int64_t u) {
+    const int64_t key = min(key0_of(u) + ld_key, P - 1);
+    const float4* src = reinterpret_cast<const float4*>(k_idx + key * kIdxDim + 8 * ld_g);
+    ka = src[0];
+    kb = src[1];
+  };
+  float nmax = 0.0f;
+  auto store = [&](char* th, char* tl, int64_t u) {
+    const float x[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    float h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_bf16(x[e], h[e], l[e]);
+    const int off = Swz<128>::off(ld_key, ld_g);
+    *reinterpret_cast<uint4*>(th + off) = make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
+                                                     pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7]));
+    *reinterpret_cast<uint4*>(tl + off) = make_uint4(pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3]),
+                                                     pack_bf16x2(l[4], l[5]), pack_bf16x2(l[6], l[7]));
+    if (norms) {
+      float n2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n2 = fmaf(x[e], x[e], n2);
+#pragma unroll
+      for (int off2 = 8; off2 > 0; off2 >>= 1) n2 += __shfl_xor(n2, off2, 64);   // the key's 16 threads
+      if (key0_of(u) + ld_key < P) nmax = fmaxf(nmax, n2);
+    }
+  };
+  Frag<128> fr;
+  fr.init();
+  auto tile = [&](const char* th, const char* tl, int64_t u) {
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ah = fr.row(th, 0, ks), al = fr.row(tl, 0, ks);
+      acc = mfma32x32x16(ah, qh[ks], acc);
+      acc = mfma32x32x16(al, qh[ks], acc);
+      acc = mfma32x32x16(ah, ql[ks], acc);
+    }
+    const int64_t key0 = key0_of(u);
+    if (SAMPLE) {
+      if (live) {
+        float* dst = samp + (int64_t)row * kTopkSample + u * kScreenKeys;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + 8 * q4 + 4 * hl) =
+              make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+      }
+      return;
+    }
+    uint32_t pass = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t key = key0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+      if (key < P && acc[e] >= t_row) pass |= 1u << e;
+    }
+    if (pass) {
+      const int n = __popc(pass);
+      int slot = atomicAdd(cnt + row, n);
+      uint32_t* ck = cand_key + (int64_t)row * cap;
+      int32_t* cp = cand_pos + (int64_t)row * cap;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (pass & (1u << e)) {
+          if (slot < cap) {
+            ck[slot] = order_key(acc[e]);
+            cp[slot] = (int32_t)(key0 + 8 * (e >> 2) + 4 * hl + (e & 3));
+          }
+          ++slot;
+        }
+      }
+    }
+  };
+  if (u0 < u1) {
+    load(u0);
+    store(kh0, kl0, u0);
+  }
+  __syncthreads();
+  for (int64_t u = u0; u < u1; u += 2) {
+    if (u + 1 < u1) load(u + 1);
+    tile(kh0, kl0, u);
+    if (u + 1 < u1) store(kh1, kl1, u + 1);
+    __syncthreads();
+    if (u + 1 >= u1) break;
+    if (u + 2 < u1) load(u + 2);
+    tile(kh1, kl1, u + 1);
+    if (u + 2 < u1) store(kh0, kl0, u + 2);
+    __syncthreads();
+  }
+  if (norms) {
+#pragma unroll
+    for (int off2 = 32; off2 > 0; off2 >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, off2, 64));
+    if (lane == 0) wmax[wave] = nmax;
+    __syncthreads();
+    if (tid == 0) {
+      float m = 0.0f;
+      for (int w = 0; w < 8; ++w) m = fmaxf(m, wmax[w]);
+      knorm[grp] = sqrtf(m);
+    }
+  }
+}
+
+// Per row: the threshold (sample score of descending rank `rank`) and a zero candidate
+// count.  Padding rows get +inf (no candidates).
+__global__ __launch_bounds__(kTopkThreads) void idx_thresh(const float* __restrict__ samp, Geom g, int rank,
+                                                           float* __restrict__ thr, int* __restrict__ cnt) {
   __shared__ TopkShared sh;
-  __shared__ uint32_t buf[kTopkSample];    // sample keys; later sorted positions | tied positions
-  const int row = blockIdx.x;              // (k, r) flattened
+  __shared__ uint32_t buf[kTopkSample];
+  const int row = blockIdx.x;
+  const int kk = row / g.R, r = row % g.R;
+  if (r >= g.r_len[kk] || r < g.row_lo || r >= g.row_hi) {
+    if (threadIdx.x == 0) {
+      thr[row] = INFINITY;
+      cnt[row] = 0;
+    }
+    return;
+  }
+  const float* sr = samp + (int64_t)row * kTopkSample;
+  for (int i = threadIdx.x; i < kTopkSample; i += kTopkThreads) buf[i] = order_key(sr[i]);
+  __syncthreads();
+  uint32_t T;
+  int unused;
+  radix_kth([&](int64_t i) { return buf[i]; }, kTopkSample, rank, 32, sh, T, unused);
+  if (threadIdx.x == 0) {
+    thr[row] = key_value(T);
+    cnt[row] = 0;
+  }
+}
+
+// Exact selection over the whole row, scores computed on the fly (radix passes, then a
+// pass over contiguous per-thread ranges that writes the chosen positions in order).
+__device__ void full_row_exact(const float* q, const float* __restrict__ k_idx, int64_t P, int k, int32_t* out,
+                               TopkShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t T;
+  int need;
+  radix_kth([&](int64_t j) { return order_key(score_f32(q, k_idx + j * kIdxDim)); }, P, k, 32, sh, T, need);
+  const int64_t chunk = (P + kTopkThreads - 1) / kTopkThreads;
+  const int64_t j0 = min(P, chunk * tid), j1 = min(P, j0 + chunk);
+  int n_gt = 0, n_eq = 0;
+  for (int64_t j = j0; j < j1; ++j) {
+    const uint32_t u = order_key(score_f32(q, k_idx + j * kIdxDim));
+    n_gt += u > T;
+    n_eq += u == T;
+  }
+  int tot;
+  const int eq_base = block_exclusive_scan(n_eq, sh.scan, &tot);
+  const int eq_take = max(0, min(n_eq, need - eq_base));
+  const int out_base = block_exclusive_scan(n_gt + eq_take, sh.scan, &tot);
+  int pos = out_base, eq_seen = 0;
+  for (int64_t j = j0; j < j1 && pos < out_base + n_gt + eq_take && pos < k; ++j) {
+    const uint32_t u = order_key(score_f32(q, k_idx + j * kIdxDim));
+    if (u > T) {
+      out[pos++] = (int32_t)j;
+    } else if (u == T) {
+      if (eq_seen < eq_take) out[pos++] = (int32_t)j;
+      ++eq_seen;
+    }
+  }
+}
+
+// One workgroup per row: the exact selection among the screen's candidates (see the top of
+// this file), or the exact full-row path.
+__global__ __launch_bounds__(kTopkThreads) void idx_select(const float* __restrict__ q_idx,
+                                                           const float* __restrict__ k_idx, int64_t P, int k,
+                                                           Geom g, int32_t* __restrict__ idx_out, int fast,
+                                                           const float* __restrict__ thr, const int* __restrict__ cnt,
+                                                           const uint32_t* __restrict__ cand_key,
+                                                           const int32_t* __restrict__ cand_pos, int cap,
+                                                           const float* __restrict__ knorm, int n_splits) {
+  __shared__ TopkShared sh;
+  __shared__ float qs[kIdxDim];
+  __shared__ int sel[kTopkSortMax];                 // chosen positions, then sorted
+  __shared__ int band_pos[kTopkSortMax];
+  __shared__ uint32_t band_key[kTopkSortMax];       // order keys of the band's fp32 scores
+  __shared__ int tied[kTopkSortMax];
+  __shared__ float red[kTopkWaves];
+  __shared__ int n_in, n_band, n_take, n_tie;
+  const int row = blockIdx.x;
   if (row >= g.K * g.R) return;
   const int kk = row / g.R, r = row % g.R;
   int32_t* out = idx_out + (int64_t)row * k;
   if (r < g.row_lo || r >= g.row_hi) return;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (r >= g.r_len[kk]) {                // padding row
     for (int t = tid; t < k; t += kTopkThreads) out[t] = -1;
     return;
   }
-  const float* srow = sigma + (int64_t)row * ld;
-  if (!fast) {
-    full_row_select(srow, P, k, out, sh);
-    return;
-  }
-
-  // 1. threshold from the sample: 64 runs of 128 scores, run q starting near q (P-128)/63
-  {
-    const int run = tid >> 3, off = (tid & 7) * 16;
-    const int64_t start = ((int64_t)run * (P - 128) / 63) & ~(int64_t)3;
-    const float4* src = reinterpret_cast<const float4*>(srow + start + off);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 x = src[v];
-      buf[16 * tid + 4 * v + 0] = order_key(x.x);
-      buf[16 * tid + 4 * v + 1] = order_key(x.y);
-      buf[16 * tid + 4 * v + 2] = order_key(x.z);
-      buf[16 * tid + 4 * v + 3] = order_key(x.w);
-    }
-  }
+  if (tid < kIdxDim) qs[tid] = q_idx[(int64_t)row * kIdxDim + tid];
   if (tid == 0) {
-    sh.n_cand = 0;
-    sh.n_gt = 0;
-    sh.n_eq = 0;
-    sh.cmax = 0;
+    n_in = 0;
+    n_band = 0;
+    n_take = 0;
+    n_tie = 0;
   }
   __syncthreads();
-  uint32_t t_lo;
-  {
-    int unused;
-    radix_kth([&](int64_t i) { return buf[i]; }, kTopkSample, sample_rank, 32, sh, t_lo, unused);
-  }
-
-  // 2. candidates: every position whose key is >= t_lo (slots past cap are counted only)
-  uint32_t* ck = cand_key + (int64_t)row * cap;
-  int32_t* cp = cand_pos + (int64_t)row * cap;
-  uint32_t lmax = 0;
-  auto consider = [&](bool valid, float x, int64_t j) {
-    const uint32_t u = order_key(x);
-    const bool pred = valid && u >= t_lo;
-    if (__ballot(pred)) {
-      const int slot = wave_append_slot(pred, &sh.n_cand);
-      if (pred) {
-        if (slot < cap) {
-          ck[slot] = u - t_lo;
-          cp[slot] = (int32_t)j;
-        }
-        lmax = max(lmax, u - t_lo);
-      }
-    }
-  };
-  const float4* s4 = reinterpret_cast<const float4*>(srow);
-  const int64_t n4 = P >> 2;
-  constexpr int U = 4;
-  // trip counts are uniform across the workgroup so every lane reaches each ballot
-  for (int64_t b0 = 0; b0 < n4; b0 += (int64_t)U * kTopkThreads) {
-    float4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i4 = b0 + (int64_t)u * kTopkThreads + tid;
-      x[u] = s4[i4 < n4 ? i4 : n4 - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i4 = b0 + (int64_t)u * kTopkThreads + tid;
-      const bool v = i4 < n4;
-      consider(v, x[u].x, 4 * i4 + 0);
-      consider(v, x[u].y, 4 * i4 + 1);
-      consider(v, x[u].z, 4 * i4 + 2);
-      consider(v, x[u].w, 4 * i4 + 3);
-    }
-  }
-  for (int64_t j0 = 4 * n4; j0 < P; j0 += kTopkThreads) {   // tail of P % 4 positions
-    const int64_t j = j0 + tid;
-    consider(j < P, j < P ? srow[j] : 0.0f, j);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
-  if (lane == 0) atomicMax(&sh.cmax, lmax);
-  __syncthreads();
-  const int n_c = sh.n_cand;
-  if (n_c < k || n_c > cap) {            // the sample misled this row: exact full-row path
-    full_row_select(srow, P, k, out, sh);
+  const int n_c = fast ? cnt[row] : 0;
+  if (!fast || n_c < k || n_c > cap) {
+    full_row_exact(qs, k_idx, P, k, out, sh);
     return;
   }
+  // the row's bound B = C ||q|| max ||k||
+  float part = 0.0f;
+  for (int i = tid; i < n_splits; i += kTopkThreads) part = fmaxf(part, knorm[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part = fmaxf(part, __shfl_xor(part, off, 64));
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  float kmax = 0.0f, qn2 = 0.0f;
+  for (int w = 0; w < kTopkWaves; ++w) kmax = fmaxf(kmax, red[w]);
+  for (int d = 0; d < kIdxDim; ++d) qn2 = fmaf(qs[d], qs[d], qn2);
+  const float B = kScreenBoundC * sqrtf(qn2) * kmax + 1e-30f;
 
-  // 3. exact k-th largest among the candidates (keys relative to t_lo)
-  uint32_t T;
-  int need;
-  const int nbits = sh.cmax ? 32 - __clz(sh.cmax) : 0;
-  radix_kth([&](int64_t i) { return ck[i]; }, n_c, k, nbits, sh, T, need);
-
-  // 4. positions above T, and the positions tied at T (the lowest `need` of them are taken)
-  int* sorted = reinterpret_cast<int*>(buf);                 // [kTopkSortMax]
-  int* tied = reinterpret_cast<int*>(buf) + kTopkSortMax;    // [kEqMax]
-  for (int64_t i0 = 0; i0 < n_c; i0 += kTopkThreads) {
-    const int64_t i = i0 + tid;
+  // k-th largest screen score among the candidates
+  const uint32_t* ck = cand_key + (int64_t)row * cap;
+  const int32_t* cp = cand_pos + (int64_t)row * cap;
+  uint32_t Tk;
+  int unused;
+  radix_kth([&](int64_t i) { return ck[i]; }, n_c, k, 32, sh, Tk, unused);
+  const float s_k = key_value(Tk);
+  const float lo = s_k - 2.0f * B, hi = s_k + 2.0f * B;
+  // lo and hi, computed in fp32, sit within one rounding of s_k -/+ 2B; the 2B margin of the
+  // bound (C = 1e-4 against 6.8e-5) covers it
+  if (!(thr[row] <= lo)) {
+    full_row_exact(qs, k_idx, P, k, out, sh);
+    return;
+  }
+  // chosen outright (s~ > hi), and the band [lo, hi]
+  for (int i0 = 0; i0 < n_c; i0 += kTopkThreads) {
+    const int i = i0 + tid;
     const bool v = i < n_c;
-    const uint32_t u = v ? ck[i] : 0;
-    const int32_t j = v ? cp[i] : 0;
-    const bool gt = v && u > T, eq = v && u == T;
+    const float x = v ? key_value(ck[i]) : 0.0f;
+    const bool in = v && x > hi, bd = v && x >= lo && x <= hi;
+    if (__ballot(in)) {
+      const int slot = wave_append_slot(in, &n_in);
+      if (in && slot < kTopkSortMax) sel[slot] = cp[i];
+    }
+    if (__ballot(bd)) {
+      const int slot = wave_append_slot(bd, &n_band);
+      if (bd && slot < kTopkSortMax) band_pos[slot] = cp[i];
+    }
+  }
+  __syncthreads();
+  const int nb = n_band, ni = n_in;
+  if (nb > kTopkSortMax || ni >= k) {     // ni >= k cannot happen (s_k is the k-th largest)
+    full_row_exact(qs, k_idx, P, k, out, sh);
+    return;
+  }
+  // fp32 scores of the band, then its top (k - ni) by (score, position)
+  for (int b = tid; b < nb; b += kTopkThreads) band_key[b] = order_key(score_f32(qs, k_idx + (int64_t)band_pos[b] * kIdxDim));
+  __syncthreads();
+  const int want = k - ni;
+  uint32_t T2;
+  int need2;
+  radix_kth([&](int64_t i) { return band_key[i]; }, nb, want, 32, sh, T2, need2);
+  for (int b0 = 0; b0 < nb; b0 += kTopkThreads) {
+    const int b = b0 + tid;
+    const bool v = b < nb;
+    const uint32_t u = v ? band_key[b] : 0;
+    const bool gt = v && u > T2, eq = v && u == T2;
     if (__ballot(gt)) {
-      const int slot = wave_append_slot(gt, &sh.n_gt);
-      if (gt && slot < kTopkSortMax) sorted[slot] = j;
+      const int slot = wave_append_slot(gt, &n_take);
+      if (gt) sel[ni + slot] = band_pos[b];
     }
     if (__ballot(eq)) {
-      const int slot = wave_append_slot(eq, &sh.n_eq);
-      if (eq && slot < kEqMax) tied[slot] = j;
+      const int slot = wave_append_slot(eq, &n_tie);
+      if (eq) tied[slot] = band_pos[b];
     }
   }
   __syncthreads();
-  const int n_eq = sh.n_eq;
-  if (n_eq > kEqMax) {                   // too many ties at T to sort here
-    full_row_select(srow, P, k, out, sh);
-    return;
-  }
-  if (n_eq > need) {
-    const int n2 = pow2_ceil(n_eq);
-    for (int t = n_eq + tid; t < n2; t += kTopkThreads) tied[t] = 0x7FFFFFFF;
+  const int nt = n_tie;
+  if (nt > need2) {                      // the lowest positions among the tied
+    const int n2 = pow2_ceil(nt);
+    for (int t = nt + tid; t < n2; t += kTopkThreads) tied[t] = 0x7FFFFFFF;
     __syncthreads();
     bitonic_sort(tied, n2);
   }
-  const int n_gt = k - need;             // == sh.n_gt
-  for (int t = tid; t < need; t += kTopkThreads) sorted[n_gt + t] = tied[t];
+  const int base = ni + n_take;          // == k - need2
+  for (int t = tid; t < need2; t += kTopkThreads) sel[base + t] = tied[t];
   const int k2 = pow2_ceil(k);
-  for (int t = k + tid; t < k2; t += kTopkThreads) sorted[t] = 0x7FFFFFFF;
+  for (int t = k + tid; t < k2; t += kTopkThreads) sel[t] = 0x7FFFFFFF;
   __syncthreads();
-  bitonic_sort(sorted, k2);
-  for (int t = tid; t < k; t += kTopkThreads) out[t] = sorted[t];
+  bitonic_sort(sel, k2);
+  for (int t = tid; t < k; t += kTopkThreads) out[t] = sel[t];
 }
 
-hipError_t launch_index_scores(const float* q_idx, const float* k_idx, float* sigma, int64_t ld,
-                               int rows, int64_t P, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const int n_row_tiles = (rows + 127) / 128;
-  const int64_t n_kt = (P + 31) / 32;
-  // about 2048 workgroups in total
-  const int64_t splits = max((int64_t)1, min(n_kt, (int64_t)(2048 / n_row_tiles)));
-  const int per = (int)((n_kt + splits - 1) / splits);
-  const int64_t n_splits = (n_kt + per - 1) / per;
-  hipLaunchKernelGGL(index_scores_f32, dim3((unsigned)(n_row_tiles * n_splits)), dim3(256), 0, s, q_idx,
-                     k_idx, sigma, ld, rows, P, per);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(void* ws, int64_t P, int k, const Geom& g, int32_t* idx_out, hipStream_t s) {
+hipError_t launch_topk(const float* q_idx, const float* k_idx, void* ws, int64_t P, int k, const Geom& g,
+                       int32_t* idx_out, hipStream_t s) {
   const TopkPlan t = topk_plan(P, k);
-  const size_t rows = (size_t)g.K * g.R;
+  const int rows = g.K * g.R;
+  const TopkWs w = topk_ws(P, k, (size_t)rows);
   char* base = static_cast<char*>(ws);
-  const float* sigma = reinterpret_cast<const float*>(base);
-  const size_t o1 = align_up(rows * (size_t)t.ld * sizeof(float), 256);
-  const size_t o2 = o1 + align_up(rows * (size_t)t.cap * sizeof(uint32_t), 256);
-  uint32_t* ck = t.fast ? reinterpret_cast<uint32_t*>(base + o1) : nullptr;
-  int32_t* cp = t.fast ? reinterpret_cast<int32_t*>(base + o2) : nullptr;
-  hipLaunchKernelGGL(topk_select, dim3((unsigned)rows), dim3(kTopkThreads), 0, s, sigma, t.ld, P, k, g,
-                     idx_out, ck, cp, t.fast, t.sample_rank, t.cap);
+  float* thr = reinterpret_cast<float*>(base + w.thr);
+  int* cnt = reinterpret_cast<int*>(base + w.cnt);
+  float* knorm = reinterpret_cast<float*>(base + w.knorm);
+  char* region = base + w.region;
+  if (t.fast) {
+    const int n_rt = (rows + kScreenRows - 1) / kScreenRows;
+    float* samp = reinterpret_cast<float*>(region);
+    // sample scores: 256 sample tiles in 16 groups
+    hipLaunchKernelGGL(idx_screen<true>, dim3((unsigned)xcd_grid((int64_t)n_rt * 16)), dim3(512), 0, s, q_idx,
+                       k_idx, P, rows, n_rt, 16, (int64_t)(kSampleTiles / 16), g, nullptr, nullptr, nullptr,
+                       nullptr, 0, samp, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(idx_thresh, dim3((unsigned)rows), dim3(kTopkThreads), 0, s, samp, g, t.sample_rank, thr,
+                       cnt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint32_t* ck = reinterpret_cast<uint32_t*>(region);
+    int32_t* cp = reinterpret_cast<int32_t*>(region + align_up((size_t)rows * t.cap * 4, 256));
+    hipLaunchKernelGGL(idx_screen<false>, dim3((unsigned)xcd_grid((int64_t)n_rt * t.n_splits)), dim3(512), 0, s,
+                       q_idx, k_idx, P, rows, n_rt, t.n_splits, t.tiles_per_split, g, thr, cnt, ck, cp, t.cap,
+                       nullptr, knorm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(idx_select, dim3((unsigned)rows), dim3(kTopkThreads), 0, s, q_idx, k_idx, P, k, g, idx_out,
+                       1, thr, cnt, ck, cp, t.cap, knorm, t.n_splits);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(idx_select, dim3((unsigned)rows), dim3(kTopkThreads), 0, s, q_idx, k_idx, P, k, g, idx_out, 0,
+                     nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -53,10 +53,10 @@ hipError_t launch_zero_rows(float* x, int K, int R, int lo, int hi, int64_t row_
                             hipStream_t s);
 
 // Latent-page sparse variant (k_topk.hip, k_sparse.hip).
-hipError_t launch_index_scores(const float* q_idx, const float* k_idx, float* sigma, int64_t ld,
-                               int rows, int64_t P, hipStream_t s);
-// ws: the forward workspace of the latent problem (scores, then candidate buffers).
-hipError_t launch_topk(void* ws, int64_t P, int k, const Geom& g, int32_t* idx_out, hipStream_t s);
+// Exact top-k of every row by fp32 index scores (k_topk.hip); ws: the forward workspace of
+// the latent problem (topk_ws layout).
+hipError_t launch_topk(const float* q_idx, const float* k_idx, void* ws, int64_t P, int k, const Geom& g,
+                       int32_t* idx_out, hipStream_t s);
 hipError_t launch_sparse_fwd(const Geom& g, int topk, const void* q, const void* latent_p,
                              const void* latent_r, const int32_t* sel, float* o, float* lse,
                              hipStream_t s);

@@ -261,15 +261,12 @@ int rr_attn_fwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, 
   const Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
   if (p->latent) {
-    // index scores -> exact top-k per row -> attention over the selection + causal rows
-    float* sigma = carve(ws, 0);
-    const int64_t ld = topk_plan(p->P, p->topk).ld;
-    hipError_t e = timed("index_scores", s, [&] {
-      return launch_index_scores(q_idx, kv->k_idx, sigma, ld, p->K * p->R_max, p->P, s);
+    // exact top-k per row (screen + candidates + exact selection) -> attention over the
+    // selection + causal rows
+    hipError_t e = timed("topk_select", s, [&] {
+      return launch_topk(q_idx, kv->k_idx, ws, p->P, p->topk, g, topk_idx, s);
     });
-    if (e != hipSuccess) return hip_fail(e, "index_scores");
-    if ((e = timed("topk_select", s, [&] { return launch_topk(ws, p->P, p->topk, g, topk_idx, s); })))
-      return hip_fail(e, "topk_select");
+    if (e != hipSuccess) return hip_fail(e, "topk_select");
     if ((e = timed("sparse_fwd", s, [&] {
            return launch_sparse_fwd(g, p->topk, q, kv->k_p, k_r, topk_idx, o, lse, s);
          })))

@@ -103,30 +103,61 @@ inline int xty_n_chunks(int R_max) {
   return (R_max + cr - 1) / cr;
 }
 
-// Plan of the per-row top-k selection over P fp32 scores (k_topk.hip).  Fast path: a
-// sample of kTopkSample scores gives a threshold expected to keep about 3k positions
-// (at least 32 sample ranks above it); one pass keeps the positions at or above it as
-// candidates (at most `cap`), and the exact k-th largest is selected among them.  A row
-// whose candidate count falls outside [k, cap] takes the exact full-row path instead.
+// Plan of the per-row top-k selection (k_topk.hip).  The fp32 index score of (row, position)
+// is one fixed-order chain of 128 fused multiply-adds; the selection is the top k by it,
+// equal scores ordered by position.  Fast path (P >= kScreenMinP): a sample of
+// kTopkSample positions per row, scored by the screen, gives a threshold expected to keep
+// about 3k positions; a screen over every position (products of the bf16 hi/lo parts,
+// within a stated bound of the fp32 score) keeps those at or above it as candidates, key
+// range by key range, at most `cap` per row; the selection is then made exactly among
+// them, computing the fp32 score of every candidate the bound leaves undecided.  Rows the
+// screen cannot decide, and every row below kScreenMinP, take the exact full-row path.
 constexpr int kTopkSample = 8192;
 constexpr int kTopkSortMax = 4096;
+constexpr int64_t kScreenMinP = 65536;
+constexpr int kScreenKeys = 32;          // keys per screen tile
+constexpr int kScreenRows = 256;         // query rows per screen workgroup
 struct TopkPlan {
-  int fast;            // 1: sample + candidate path available for this (P, k)
+  int fast;            // 1: sample + screen path for this (P, k)
   int sample_rank;     // descending rank in the sample that sets the threshold
   int cap;             // candidate slots per row
-  int64_t ld;          // score row stride (P rounded up to a multiple of 4)
+  int n_splits;        // key ranges of the screen, each a run of whole 32-key tiles
+  int64_t tiles_per_split;
 };
 inline TopkPlan topk_plan(int64_t P, int k) {
   TopkPlan t{};
-  t.ld = (P + 3) / 4 * 4;
   const int64_t rs = (3 * (int64_t)k * kTopkSample + P - 1) / P;
   t.sample_rank = (int)(rs < 32 ? 32 : rs);
-  t.fast = P >= 8 * (int64_t)kTopkSample && k <= kTopkSortMax && t.sample_rank <= kTopkSample / 4;
+  t.fast = P >= kScreenMinP && k <= kTopkSortMax && t.sample_rank <= kTopkSample / 4;
   if (t.fast) {
     const int64_t expect = (int64_t)t.sample_rank * P / kTopkSample;   // candidates expected
     t.cap = (int)((2 * expect + 1024 + 255) / 256 * 256);
+    const int64_t n_kt = (P + kScreenKeys - 1) / kScreenKeys;
+    const int64_t want = 128;                                         // key ranges
+    t.tiles_per_split = (n_kt + want - 1) / want;
+    t.n_splits = (int)((n_kt + t.tiles_per_split - 1) / t.tiles_per_split);
   }
   return t;
+}
+
+// Forward workspace of the latent selection: per row the threshold and the candidate
+// count, the key-norm maximum of each key range, then one region that first holds the
+// sample scores [rows][kTopkSample] and then the candidates (keys [rows][cap], positions
+// [rows][cap]).
+struct TopkWs {
+  size_t thr, cnt, knorm, region, total;
+};
+inline TopkWs topk_ws(int64_t P, int k, size_t rows) {
+  const TopkPlan t = topk_plan(P, k);
+  TopkWs w{};
+  w.thr = 0;
+  w.cnt = align_up(rows * 4, 256);
+  w.knorm = w.cnt + align_up(rows * 4, 256);
+  w.region = w.knorm + align_up((size_t)(t.fast ? t.n_splits : 1) * 4, 256);
+  const size_t samp = t.fast ? rows * (size_t)kTopkSample * 4 : 0;
+  const size_t cand = t.fast ? 2 * align_up(rows * (size_t)t.cap * 4, 256) : 0;
+  w.total = w.region + align_up(samp > cand ? samp : cand, 256);
+  return w;
 }
 
 }  // namespace rr

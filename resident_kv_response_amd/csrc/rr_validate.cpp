@@ -88,13 +88,8 @@ static int check_aligned(const char* what, std::initializer_list<const void*> pt
 static size_t rows_total(const rr_problem* p) { return (size_t)p->K * p->R_max * p->Hq; }
 
 size_t ws_fwd_bytes(const rr_problem* p, bool exported) {
-  if (p->latent) {
-    // fp32 index scores [K*R][ld], then candidate keys and positions [K*R][cap] each
-    const TopkPlan t = topk_plan(p->P, p->topk);
-    const size_t rows = (size_t)p->K * p->R_max;
-    return align_up(rows * (size_t)t.ld * sizeof(float), 256) +
-           (t.fast ? 2 * align_up(rows * (size_t)t.cap * sizeof(uint32_t), 256) : 0);
-  }
+  if (p->latent)   // selection state and candidates (k_topk.hip)
+    return topk_ws(p->P, p->topk, (size_t)p->K * p->R_max).total;
   if (exported) return 0;
   const size_t n = (size_t)n_parts_of(p) * rows_total(p);
   return align_up(n * p->d_v * sizeof(float), 256) + align_up(n * sizeof(float), 256);

@@ -304,19 +304,26 @@ def test_latent_fwd_arguments_and_workspace():
     assert _latent_fwd(p, ws=FAKE + 8)[0] == R.RR_E_SHAPE            # misaligned workspace
     need = R.rr_workspace_bytes(p, R.RR_OP_FWD)
     assert _latent_fwd(p, ws_bytes=need - 1)[0] == R.RR_E_WORKSPACE
-    # scores [K*R][ld] fp32, then candidate keys and positions [K*R][cap] (sampled-threshold
-    # path: cap = 2 * expected candidates + 1024, expected = rank * P / 8192, rank = 3k*8192/P)
+    # per row a threshold and a candidate count, the key-norm maximum of each of the
+    # screen's key ranges, then one region holding first the sample scores [K*R][8192] and
+    # then the candidates (keys and positions [K*R][cap], cap = 2 * expected + 1024,
+    # expected = rank * P / 8192, rank = 3k * 8192 / P): no [K*R][P] score matrix
     up = lambda x: -(-x // 256) * 256
     rank = max(32, -(-3 * 2048 * 8192 // 1048576))
     cap = up(2 * (rank * 1048576 // 8192) + 1024)
-    assert need == up(4096 * 1048576 * 4) + 2 * up(4096 * cap * 4)
+    n_kt = 1048576 // 32
+    per = -(-n_kt // 128)
+    n_splits = -(-n_kt // per)
+    region = max(4096 * 8192 * 4, 2 * up(4096 * cap * 4))
+    assert need == 2 * up(4096 * 4) + up(n_splits * 4) + up(region)
+    assert need < 4096 * 1048576 // 8          # far below the 16 GiB a score matrix would take
     # backward: D, then P and dS of the response pairs [K][R][64][R] bf16 (+ one padded
     # segment), then the dK_r / dV_r chunk partials [16 chunks of 256 rows][K][R][576] fp32
     assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == (up(4096 * 64 * 4) + 2 * up((4096 * 64 * 4096 + 128) * 2)
                                                    + up(16 * 4096 * 576 * 4))
-    # small rows use the exact full-row path and need no candidate buffers
+    # short rows take the exact full-row path and need only the per-row arrays
     small = _latent(P=3000, R_max=96, topk=256)
-    assert R.rr_workspace_bytes(small, R.RR_OP_FWD) == up(96 * 3000 * 4)
+    assert R.rr_workspace_bytes(small, R.RR_OP_FWD) == 2 * up(96 * 4) + up(4)
 
 
 def test_blend_rejects_bad_arguments():
