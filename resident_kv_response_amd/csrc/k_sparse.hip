@@ -190,13 +190,25 @@ __global__ __launch_bounds__(256 * HT, 1) void sparse_fwd(Geom g, int topk, cons
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 < n_tiles) gather_tile<4 * HT>(nxt, latent_p, latent_rk, sel, topk, n_keys, (t + 1) * kLatKeys);
-    f32x16 sp;
+    // two independent accumulation chains (even and odd k-steps), each fragment read one
+    // MFMA ahead, so the matrix core does not wait on a dependent result or a LDS read
+    f32x16 sp, sq;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sp[e] = 0.0f;
+    for (int e = 0; e < 16; ++e) sp[e] = sq[e] = 0.0f;
     prio_mfma();
+    {
+      bf16x8 fcur = lat_row(cur, 9 * wave);
 #pragma unroll
-    for (int s = 0; s < 9; ++s) sp = mfma32x32x16(lat_row(cur, 9 * wave + s), qf[s], sp);
+      for (int s = 0; s < 9; ++s) {
+        const bf16x8 fnext = s + 1 < 9 ? lat_row(cur, 9 * wave + s + 1) : fcur;
+        if (s & 1) sq = mfma32x32x16(fcur, qf[s], sq);
+        else sp = mfma32x32x16(fcur, qf[s], sp);
+        fcur = fnext;
+      }
+    }
     prio_valu();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sp[e] += sq[e];
     xch_put(xch[HT == 2 ? ht : 0], sp, wave);
     __syncthreads();
     f32x16 sc;
@@ -242,9 +254,9 @@ __global__ __launch_bounds__(256 * HT, 1) void sparse_fwd(Geom g, int topk, cons
     }
     prio_mfma();
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int h2 = 0; h2 < 2; ++h2)       // four independent accumulators per k-step
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 128 * wave + 32 * dt), pf[h2], acc[dt]);
+      for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 128 * wave + 32 * dt), pf[h2], acc[dt]);
     prio_valu();
   };
   for (int t = 0; t < n_tiles; t += 2) {
@@ -283,6 +295,7 @@ __global__ __launch_bounds__(256 * HT, 1) void sparse_dq(Geom g, int topk, const
   __shared__ __attribute__((aligned(1024))) char kv1[kLatTile];
   __shared__ __attribute__((aligned(16))) Xch xs[HT];
   __shared__ __attribute__((aligned(16))) Xch xp[HT];
+  __shared__ __attribute__((aligned(16))) uint2 dsx[HT][4][64];   // dS of the tile, bf16, by owner wave
   __shared__ int32_t sel_lds[kLatSelMax];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = HT == 2 ? (int)blockIdx.x : (int)(blockIdx.x >> 1);
@@ -343,65 +356,75 @@ __global__ __launch_bounds__(256 * HT, 1) void sparse_dq(Geom g, int topk, const
 #pragma unroll
     for (int e = 0; e < 16; ++e) sp[e] = dpp[e] = 0.0f;
     prio_mfma();
+    {
+      // the S and dP chains (score dims, value dims) alternate, so consecutive MFMAs are
+      // independent
+      bf16x8 fs = lat_row(cur, 9 * wave), fp = lat_row(cur, 8 * wave);
 #pragma unroll
-    for (int s = 0; s < 9; ++s) sp = mfma32x32x16(lat_row(cur, 9 * wave + s), qf[s], sp);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) dpp = mfma32x32x16(lat_row(cur, 8 * wave + s), of[s], dpp);  // value dims
+      for (int s = 0; s < 9; ++s) {
+        const bf16x8 ns = s + 1 < 9 ? lat_row(cur, 9 * wave + s + 1) : fs;
+        const bf16x8 np = s + 1 < 8 ? lat_row(cur, 8 * wave + s + 1) : fp;
+        sp = mfma32x32x16(fs, qf[s], sp);
+        if (s < 8) dpp = mfma32x32x16(fp, of[s], dpp);   // value dims
+        fs = ns;
+        fp = np;
+      }
+    }
     prio_valu();
     xch_put(xs[xi], sp, wave);
     xch_put(xp[xi], dpp, wave);
     __syncthreads();
-    f32x16 sc, dp;
-    xch_sum(xs[xi], sc);
-    xch_sum(xp[xi], dp);
+    // This wave owns keys 8 wave + [0, 8) of the tile (C registers 4 wave .. 4 wave + 3 of
+    // every lane): it sums the four partials of those entries in wave order, forms p and
+    // dS = p (dP - D), shares dS in bf16, and writes the response pairs' P and dS.
     const int rel = t * kLatKeys;
-    float p[16], ds[16];
+    float4 sc = xs[xi].v[0][wave][lane], dp = xp[xi].v[0][wave][lane];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = rel + (e >> 2) * 8 + hl * 4 + (e & 3);
-      p[e] = key < n_keys ? fast_exp2(fmaf(sc[e], g.c2, -lse2)) : 0.0f;
-      ds[e] = p[e] * (dp[e] - dvv);
+    for (int w = 1; w < 4; ++w) {
+      const float4 a = xs[xi].v[w][wave][lane], b = xp[xi].v[w][wave][lane];
+      sc.x += a.x;
+      sc.y += a.y;
+      sc.z += a.z;
+      sc.w += a.w;
+      dp.x += b.x;
+      dp.y += b.y;
+      dp.z += b.z;
+      dp.w += b.w;
     }
+    const int key0 = rel + 8 * wave + 4 * hl;          // 4 consecutive keys
+    const float sv[4] = {sc.x, sc.y, sc.z, sc.w}, dv[4] = {dp.x, dp.y, dp.z, dp.w};
+    float pe[4], de[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pe[e] = key0 + e < n_keys ? fast_exp2(fmaf(sv[e], g.c2, -lse2)) : 0.0f;
+      de[e] = pe[e] * (dv[e] - dvv);
+    }
+    const uint2 dsw = make_uint2(pack_bf16x2(de[0], de[1]), pack_bf16x2(de[2], de[3]));
+    dsx[xi][wave][lane] = dsw;
+    if (key0 >= topk && key0 < n_keys) {              // response keys (keys past i: p = dS = 0)
+      const int j = key0 - topk;
+      *reinterpret_cast<uint2*>(p_row + j) = make_uint2(pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]));
+      *reinterpret_cast<uint2*>(ds_row + j) = dsw;   // j + 3 < jz_end: R_max % 4 == 0
+    }
+    __syncthreads();
     bf16x8 dsf[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      uint4 uu;
-      uu.x = pack_bf16x2(ds[8 * h2 + 0], ds[8 * h2 + 1]);
-      uu.y = pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]);
-      uu.z = pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]);
-      uu.w = pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7]);
-      dsf[h2] = as_bf16x8(uu);
-    }
-    // response keys: P and dS of (row i, head, key j) for the dK_r / dV_r contraction
-    if (wave == 0 && rel + kLatKeys > topk) {
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int key0 = rel + e4 * 8 + hl * 4;       // 4 consecutive keys
-        if (key0 >= topk && key0 < n_keys) {
-          const int j = key0 - topk;                  // keys past i carry p = dS = 0
-          uint2 pv, dv;
-          pv.x = pack_bf16x2(p[4 * e4], p[4 * e4 + 1]);
-          pv.y = pack_bf16x2(p[4 * e4 + 2], p[4 * e4 + 3]);
-          dv.x = pack_bf16x2(ds[4 * e4], ds[4 * e4 + 1]);
-          dv.y = pack_bf16x2(ds[4 * e4 + 2], ds[4 * e4 + 3]);
-          *reinterpret_cast<uint2*>(p_row + j) = pv;     // j + 3 < jz_end: R_max % 4 == 0
-          *reinterpret_cast<uint2*>(ds_row + j) = dv;
-        }
-      }
+      const uint2 lo = dsx[xi][2 * h2][lane], hi = dsx[xi][2 * h2 + 1][lane];
+      dsf[h2] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
     prio_mfma();
 #pragma unroll
-    for (int dt = 0; dt < 5; ++dt) {
-      if (dt < n_dt) {
+    for (int h2 = 0; h2 < 2; ++h2)       // independent accumulators per k-step
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 32 * (dt_lo + dt)), dsf[h2], acc[dt]);
-      }
-    }
+      for (int dt = 0; dt < 5; ++dt)
+        if (dt < n_dt) acc[dt] = mfma32x32x16(lat_trans(cur, h2, 32 * (dt_lo + dt)), dsf[h2], acc[dt]);
     prio_valu();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile_step(kv0, kv1, t);
-    if (t + 1 < n_tiles) tile_step(kv1, kv0, t + 1);
+  for (int t = 0; t < n_tiles; ++t) {   // one loop body, the two buffers alternating
+    char* const cur = (t & 1) ? kv1 : kv0;
+    char* const nxt = (t & 1) ? kv0 : kv1;
+    tile_step(cur, nxt, t);
   }
 
   float* dst = dq + hr * kLatD;
@@ -564,9 +587,9 @@ hipError_t launch_sparse_dq(const Geom& g, int topk, const void* q, const void* 
                             const void* latent_r, const int32_t* sel, const void* d_o,
                             const float* lse, const float* Dvec, float* dq, uint16_t* p_r,
                             uint16_t* ds_r, int accumulate, hipStream_t s) {
-  // one head tile per workgroup: with both, the per-wave state (Q and dO fragments, dQ^T
-  // accumulators) does not fit the 256 registers of two waves per SIMD and spills
-  hipLaunchKernelGGL(sparse_dq<1>, dim3((unsigned)(2 * g.K * g.R)), dim3(256), 0, s, g, topk,
+  // both head tiles per workgroup (8 waves, two per SIMD): each gathered tile serves all
+  // 64 heads
+  hipLaunchKernelGGL(sparse_dq<2>, dim3((unsigned)(g.K * g.R)), dim3(512), 0, s, g, topk,
                      (const uint16_t*)q, (const uint16_t*)latent_p, (const uint16_t*)latent_r, sel,
                      (const uint16_t*)d_o, lse, Dvec, dq, p_r, ds_r, accumulate);
   return hipGetLastError();
