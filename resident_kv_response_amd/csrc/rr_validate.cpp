@@ -53,6 +53,7 @@ int validate_problem(const rr_problem* p) {
                        p->topk);
     if (p->idx_dim != 128) return set_error(RR_E_UNSUPPORTED, "index keys must be 128 wide (got %d)", p->idx_dim);
     if (p->R_max % 8 != 0) return set_error(RR_E_SHAPE, "latent pages need R_max %% 8 == 0");
+    if (p->P >= ((int64_t)1 << 31)) return set_error(RR_E_SHAPE, "latent pages need P < 2^31 (int32 positions)");
     if (p->flags) return set_error(RR_E_UNSUPPORTED, "shard flags are not built for latent pages");
     if ((int64_t)p->K * p->R_max > (1 << 20)) return set_error(RR_E_SHAPE, "K*R_max too large");
     return RR_OK;
