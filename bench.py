@@ -51,7 +51,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="bf16_full_P2097152_G8")
-    ap.add_argument("--cpu-rows", type=int, default=12, help="oracle sample rows (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample rows (0 = skip)")
     ap.add_argument("--microbatch", type=int, default=1,
                     help="replay microbatch K: the group's members run as calls of K responses each")
     ap.add_argument("--full-sequence", action="store_true",
@@ -222,8 +222,13 @@ def run_dense(a, w) -> int:
     got = None
     if rows is not None:
         grp = w.Hq // w.Hkv
-        o0, _, dq0, _, _ = outs(len(mbs[0][0]), mbs[0][3].R_max)
-        got = {"o": o0[0, rows, :grp].double().cpu().numpy(), "dq": dq0[0, rows, :grp].double().cpu().numpy()}
+        o0, _, dq0, dk0, dv0 = outs(len(mbs[0][0]), mbs[0][3].R_max)
+        r0 = int(lens[0])
+        got = {"o": o0[0, rows, :grp].double().cpu().numpy(), "dq": dq0[0, rows, :grp].double().cpu().numpy(),
+               # response-key gradients of member 0's last TAIL keys, KV head 0 (only its last
+               # TAIL positions reach them)
+               "dk": dk0[0, r0 - TAIL:r0, 0].double().cpu().numpy(),
+               "dv": dv0[0, r0 - TAIL:r0, 0].double().cpu().numpy()}
 
     for _ in range(a.warmup):
         step()
@@ -291,7 +296,10 @@ def run_dense(a, w) -> int:
             kernels[k]["gbs"] = round(gbs, 1)
             kernels[k]["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 3)
 
-    # CPU baseline: the oracle on the machine's host cores, bounded sample of member 0
+    # CPU baseline: the oracle on the machine's host cores, on bounded legs of the work (the
+    # tiny fp32 configuration in full, sampled 2M rows, and the 2M response-key gradients of
+    # member 0's last keys); the full step's oracle time is an extrapolation at the
+    # measured oracle rate
     cpu = None
     parity = None
     if rows is not None:
@@ -303,28 +311,65 @@ def run_dense(a, w) -> int:
             blas_threads = None
         grp = w.Hq // w.Hkv
         f = lambda x: synth.as_f64(x, w.dtype)
+        legs = []
+        # leg 1: the tiny fp32 configuration, every row, forward and full response-only backward
+        wt = configs.TINY_F32
+        rt, mt = synth.resident(wt), synth.member(wt, 0)
+        ft = lambda x: synth.as_f64(x, wt.dtype)
+        tc = time.perf_counter()
+        dense.attend(ft(mt["q"]), ft(rt["k_p"]), ft(rt["v_p"]), ft(mt["k_r"]), ft(mt["v_r"]), wt.tau)
+        dense.attend_bwd(ft(mt["q"]), ft(rt["k_p"]), ft(rt["v_p"]), ft(mt["k_r"]), ft(mt["v_r"]), ft(mt["d_o"]),
+                         wt.tau)
+        legs.append({"leg": f"{wt.name}, all {wt.R} rows x {wt.Hq} heads, fwd + bwd (dQ, dK_r, dV_r)",
+                     "flops": configs.flops_dense(wt.Hq, wt.d_qk, wt.d_v, wt.R, wt.P)["total"],
+                     "s": time.perf_counter() - tc})
+        # leg 2: sampled rows of member 0 over all P prompt keys (also the parity gate)
         kp64, vp64 = f(res["k_p"][:, :1]), f(res["v_p"][:, :1])
         qs, kr, vr, do = f(host_m0["q"][:, :grp]), f(host_m0["k_r"][:, :1]), f(host_m0["v_r"][:, :1]), \
             f(host_m0["d_o"][:, :grp])
         tc = time.perf_counter()
         ro, _ = dense.attend(qs, kp64, vp64, kr, vr, w.tau, rows=rows)
         rgr = dense.attend_bwd(qs, kp64, vp64, kr, vr, do, w.tau, rows=rows)
-        cpu_s = time.perf_counter() - tc
-        cpu_flops = sum(grp * 10.0 * w.d_qk * (w.P + int(r) + 1) for r in rows)
+        legs.append({"leg": f"member 0 (R={int(lens[0])}): {len(rows)} sampled query rows "
+                            f"{list(map(int, rows))} x KV head 0's {grp} query heads, fwd + dQ over all "
+                            f"{w.P} prompt keys and the causal response keys",
+                     "flops": sum(grp * 10.0 * w.d_qk * (w.P + int(r) + 1) for r in rows),
+                     "s": time.perf_counter() - tc})
+        # leg 3: the response-key gradients dK_r, dV_r of member 0's last TAIL keys (KV head
+        # 0): every head of its last TAIL positions, forward and backward over all keys
+        r0 = int(lens[0])
+        tail_rows = np.repeat(np.arange(r0 - TAIL, r0), grp)
+        tail_heads = np.tile(np.arange(grp), TAIL)
+        tc = time.perf_counter()
+        rt_ = dense.attend_rows(qs, kp64, vp64, kr, vr, do, w.tau, tail_rows, tail_heads)
+        legs.append({"leg": f"member 0: dK_r, dV_r of its last {TAIL} keys (KV head 0) from every head "
+                            f"of its last {TAIL} positions, fwd + bwd over all keys",
+                     "flops": sum(grp * 10.0 * w.d_qk * (w.P + int(r) + 1) for r in range(r0 - TAIL, r0)),
+                     "s": time.perf_counter() - tc})
+        cpu_s = sum(l["s"] for l in legs)
+        cpu_flops = sum(l["flops"] for l in legs)
+        for l in legs:
+            l["tflops"] = round(l["flops"] / l["s"] / 1e12, 6)
+            l["s"] = round(l["s"], 2)
         cores = len(os.sched_getaffinity(0))
         cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
                "cores": blas_threads or cores, "kind": "oracle",
-               "sample": f"member 0 (R={int(lens[0])}), {len(rows)} query rows {list(map(int, rows))}, "
-                         f"KV head 0 and its {grp} query heads, fwd + dQ over all {w.P} prompt keys "
-                         f"plus causal response keys; {cpu_s:.1f} s",
-               "host_cpus_affinity": cores, "host_cpu_count": os.cpu_count(),
-               "extrapolated_full_step_s": round(flops_step / (cpu_flops / cpu_s), 1)}
+               "sample": "; ".join(l["leg"] for l in legs) + f" ({cpu_s:.1f} s in all)",
+               "legs": legs, "host_cpus_affinity": cores, "host_cpu_count": os.cpu_count(),
+               "extrapolated_full_step_s": round(flops_step / (cpu_flops / cpu_s), 1),
+               "extrapolation": "the full G=8 group at the oracle's measured rate (not run)"}
         rel = lambda x, y: float(np.linalg.norm(x - y) / np.linalg.norm(y))
         parity = {"rows": len(rows), "o_rel_l2": rel(got["o"], ro), "dq_rel_l2": rel(got["dq"], rgr["dq"]),
                   "o_max_abs": float(np.abs(got["o"] - ro).max()),
-                  "dq_max_abs": float(np.abs(got["dq"] - rgr["dq"]).max())}
-        parity["pass"] = bool(parity["o_rel_l2"] <= 5e-3 and parity["dq_rel_l2"] <= 5e-3
-                              and parity["o_max_abs"] <= 2e-2 and parity["dq_max_abs"] <= 2e-2)
+                  "dq_max_abs": float(np.abs(got["dq"] - rgr["dq"]).max()),
+                  "tail_keys": TAIL,
+                  "dk_rel_l2": rel(got["dk"], rt_["dk_r"][r0 - TAIL:r0, 0]),
+                  "dv_rel_l2": rel(got["dv"], rt_["dv_r"][r0 - TAIL:r0, 0]),
+                  "dk_max_abs": float(np.abs(got["dk"] - rt_["dk_r"][r0 - TAIL:r0, 0]).max()),
+                  "dv_max_abs": float(np.abs(got["dv"] - rt_["dv_r"][r0 - TAIL:r0, 0]).max())}
+        parity["pass"] = bool(all(parity[k] <= 5e-3 for k in ("o_rel_l2", "dq_rel_l2", "dk_rel_l2", "dv_rel_l2"))
+                              and all(parity[k] <= 2e-2 for k in ("o_max_abs", "dq_max_abs", "dk_max_abs",
+                                                                   "dv_max_abs")))
 
     fs = None
     if full:   # norms of the group's response-side and prompt-side gradients after the last step
@@ -365,6 +410,9 @@ LATENT_SOURCES = {
     "xty_dk": ["k_sparse.hip", "k_lds.h", "k_common.h"],
     "xty_dv": ["k_sparse.hip", "k_lds.h", "k_common.h"],
 }
+
+
+TAIL = 32   # response keys of member 0 whose dK_r / dV_r the bench's oracle leg checks
 
 
 def latent_kernel_model(w, R: int) -> dict:
@@ -665,7 +713,10 @@ def run_latent(a, w) -> int:
             parity.update({"o_rel_l2": rel(got["o"][s_], ro[s_]), "dq_rel_l2": rel(got["dq"][s_], rgr["dq"][s_]),
                            "o_max_abs": float(np.abs(got["o"][s_] - ro[s_]).max()),
                            "dq_max_abs": float(np.abs(got["dq"][s_] - rgr["dq"][s_]).max())})
-        parity["pass"] = bool(len(same) >= len(rows) // 2 and parity.get("o_rel_l2", 1) <= 5e-3
+        # the selections are decided by fp32 scores summed in different orders on the two
+        # sides; a near tie at the k-th place may rank differently, which the GPU tests bound
+        # position by position; here at most one sampled row in fifty may differ
+        parity["pass"] = bool(len(same) >= int(np.ceil(0.98 * len(rows))) and parity.get("o_rel_l2", 1) <= 5e-3
                               and parity.get("dq_rel_l2", 1) <= 5e-3 and parity.get("o_max_abs", 1) <= 2e-2
                               and parity.get("dq_max_abs", 1) <= 2e-2)
 

@@ -180,7 +180,7 @@ int rr_attn_fwd(const rr_problem* p, const rr_resident* kv,
  * architectures, same transaction" (rank-local softmax statistics composed into the
  * exact global attention output).  For every row:
  *   lse = ln sum_c exp(lse_c),   O = sum_c exp(lse_c - lse) * O_c,
- * summed in part order.  Parts with lse_c = -inf carry weight 0; a row whose parts are
+ * O summed in part order, the normaliser in a fixed order (deterministic).  Parts with lse_c = -inf carry weight 0; a row whose parts are
  * all -inf gets O = 0, lse = -inf.
  *
  *   part_o [n_parts][rows][d_v] fp32, part_lse [n_parts][rows] fp32 (inputs)

@@ -9,18 +9,18 @@ namespace rr {
 // Composition of softmax-statistics partials into the exact output
 // (ai.thesatyajit.com/articles/longstraw-2m-rl, section "Two incompatible
 // architectures, same transaction"): lse = ln sum_c e^{lse_c}, O = sum_c e^{lse_c-lse} O_c.
-// One thread owns VEC consecutive output elements of one row; the n_parts statistics of
-// the row are re-read from L1/L2 by each of its threads (tiny next to the O_c traffic).
+// One wave per row: lane c reads lse_c once (lanes c, c + 64, ... for more parts), the
+// wave reduces max and sum in a fixed order, and every lane then streams its VEC columns
+// of all parts in part order, the weights broadcast from the lanes that hold them, several
+// parts' loads in flight at once.
 template <int VEC>
 __global__ __launch_bounds__(256) void merge_kernel(int n_parts, int64_t rows, int d_v,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     float* __restrict__ o, float* __restrict__ lse,
                                                     bool use_geom, Geom g) {
-  const int tpr = (d_v + VEC - 1) / VEC;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = t / tpr;
-  const int col = (int)(t % tpr) * VEC;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   bool pad = false;
   if (use_geom) {
@@ -30,42 +30,78 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, int64_t rows, i
   }
   float m = -INFINITY;
   if (!pad)
-    for (int c = 0; c < n_parts; ++c) m = fmaxf(m, part_lse[(int64_t)c * rows + row]);
-  float acc[VEC];
+    for (int c = lane; c < n_parts; c += 64) m = fmaxf(m, part_lse[(int64_t)c * rows + row]);
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-  float out_lse = -INFINITY;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float out_lse = -INFINITY, inv = 0.0f;
   if (m != -INFINITY) {
     float den = 0.0f;
-    for (int c = 0; c < n_parts; ++c) den += expf(part_lse[(int64_t)c * rows + row] - m);
-    out_lse = m + logf(den);
-    for (int c = 0; c < n_parts; ++c) {
-      const float lc = part_lse[(int64_t)c * rows + row];
-      if (lc == -INFINITY) continue;
-      const float w = expf(lc - out_lse);
-      const float* src = part_o + ((int64_t)c * rows + row) * d_v + col;
-      if constexpr (VEC == 4) {
-        const float4 x = *reinterpret_cast<const float4*>(src);
-        acc[0] += w * x.x;
-        acc[1] += w * x.y;
-        acc[2] += w * x.z;
-        acc[3] += w * x.w;
-      } else {
+    for (int c = lane; c < n_parts; c += 64) den += expf(part_lse[(int64_t)c * rows + row] - m);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v)
-          if (col + v < d_v) acc[v] += w * src[v];
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+    out_lse = m + logf(den);
+    inv = 1.0f / den;
+  }
+  float* dst = o + row * d_v;
+  // every lane runs every iteration (the weight broadcasts need all lanes); lanes past d_v
+  // load and store nothing
+  for (int base = 0; base < d_v; base += 64 * VEC) {
+    const int col = base + lane * VEC;
+    const bool on = col < d_v;
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    if (m != -INFINITY) {
+      for (int c0 = 0; c0 < n_parts; c0 += 64) {
+        // weights of parts c0 .. c0 + 63, one per lane (0 for -inf parts and past the end)
+        const int cl = c0 + lane;
+        const float lc = cl < n_parts ? part_lse[(int64_t)cl * rows + row] : -INFINITY;
+        const float wl = lc == -INFINITY ? 0.0f : expf(lc - m) * inv;
+        const int n = min(64, n_parts - c0);
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {          // four parts' loads in flight
+          float x[4][VEC];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float* src = part_o + ((int64_t)(c0 + j + u) * rows + row) * d_v + col;
+            if constexpr (VEC == 4) {
+              const float4 y = on ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+              x[u][0] = y.x;
+              x[u][1] = y.y;
+              x[u][2] = y.z;
+              x[u][3] = y.w;
+            } else {
+              x[u][0] = on ? src[0] : 0.0f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float w = __shfl(wl, j + u, 64);
+            if (w != 0.0f) {
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) acc[v] += w * x[u][v];
+            }
+          }
+        }
+        for (; j < n; ++j) {
+          const float w = __shfl(wl, j, 64);
+          const float* src = part_o + ((int64_t)(c0 + j) * rows + row) * d_v + col;
+          if (w != 0.0f && on) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] += w * src[v];
+          }
+        }
+      }
+    }
+    if (on) {
+      if constexpr (VEC == 4) {
+        *reinterpret_cast<float4*>(dst + col) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else {
+        dst[col] = acc[0];
       }
     }
   }
-  float* dst = o + row * d_v + col;
-  if constexpr (VEC == 4) {
-    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  } else {
-#pragma unroll
-    for (int v = 0; v < VEC; ++v)
-      if (col + v < d_v) dst[v] = acc[v];
-  }
-  if (col == 0) lse[row] = out_lse;
+  if (lane == 0) lse[row] = out_lse;
 }
 
 hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
@@ -75,9 +111,7 @@ hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
   Geom g{};
   if (geom) g = *geom;
   const bool vec4 = (d_v % 4 == 0) && ((uintptr_t)part_o % 16 == 0) && ((uintptr_t)o % 16 == 0);
-  const int vec = vec4 ? 4 : 1;
-  const int64_t threads = rows * ((d_v + vec - 1) / vec);
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (rows + 3) / 4;            // four rows (waves) per workgroup
   if (vec4)
     hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, n_parts, rows, d_v,
                        part_o, part_lse, o, lse, geom != nullptr, g);
@@ -88,7 +122,8 @@ hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
 }
 
 // ---- D = rowsum(dO * O) ---------------------------------------------------------------
-// 16 threads per (k, r, h) row; dO in its stored dtype, O in fp32.
+// 16 threads per (k, r, h) row, each reading 8 consecutive elements per step (one 16-byte
+// load of bf16 dO, two of fp32 O); dO in its stored dtype.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Geom g, const float* __restrict__ o,
                                                       const void* __restrict__ d_o,
@@ -106,13 +141,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Geom g, const float* __res
   float acc = 0.0f;
   if (r < g.r_len[k]) {
     const float* orow = o + row * g.dv;
-    for (int d = lane16; d < g.dv; d += 16) {
-      float x;
-      if (BF16)
-        x = bf16_bits_to_f32(static_cast<const uint16_t*>(d_o)[row * g.dv + d]);
-      else
-        x = static_cast<const float*>(d_o)[row * g.dv + d];
-      acc += x * orow[d];
+    for (int d = 8 * lane16; d < g.dv; d += 128) {     // d_v is a multiple of 8
+      const float4 o0 = *reinterpret_cast<const float4*>(orow + d);
+      const float4 o1 = *reinterpret_cast<const float4*>(orow + d + 4);
+      float x[8];
+      if (BF16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(d_o) + row * g.dv + d);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = __uint_as_float(w[i] << 16);
+          x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else {
+        const float* src = static_cast<const float*>(d_o) + row * g.dv + d;
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      }
+      const float y[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(x[i], y[i], acc);
     }
   }
 #pragma unroll

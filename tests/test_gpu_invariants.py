@@ -112,6 +112,31 @@ def test_merge_handles_empty_parts():
     np.testing.assert_allclose(lse.cpu().numpy()[:4], rl_[:4], atol=1e-6)
 
 
+@pytest.mark.parametrize("n_parts,d_v", [(150, 512), (70, 70), (17, 128), (1, 64)])
+def test_merge_many_parts_and_widths(n_parts, d_v):
+    """rr_lse_merge over more parts than a wave has lanes, head dims that take several
+    column passes or no 16-byte vectors, and one part: every element against the
+    oracle's merge (fp32 inputs, fp64 reference), with -inf parts and an all-empty row."""
+    g = torch.Generator().manual_seed(900 + n_parts)
+    rows = 37
+    po = torch.randn(n_parts, rows, d_v, generator=g)
+    pl = 4.0 * torch.randn(n_parts, rows, generator=g)
+    pl[::3, 5] = float("-inf")
+    pl[:, 9] = float("-inf")
+    if n_parts > 1:
+        pl[1] = float("-inf")
+    ref_o, ref_l = dense.merge(po.double().numpy(), pl.double().numpy())
+    o = torch.full((rows, d_v), float("nan"), device="cuda")
+    lse = torch.full((rows,), float("nan"), device="cuda")
+    R.rr_lse_merge(po.cuda(), pl.cuda(), o, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o.cpu().numpy(), ref_o, rtol=0, atol=2e-5 * max(1.0, float(np.abs(ref_o).max())))
+    assert np.isneginf(lse[9].item()) and np.all(o[9].cpu().numpy() == 0)
+    keep = np.isfinite(ref_l)
+    np.testing.assert_allclose(lse.cpu().numpy()[keep], ref_l[keep], rtol=0,
+                               atol=2e-5 * (1.0 + float(np.abs(ref_l[keep]).max())))
+
+
 def _group_runs(w, seed_version=7):
     """The members of a small group, each replayed against one shared resident prompt
     state (one device copy of K_p, V_p with one version), plus the oracle's gradients."""
