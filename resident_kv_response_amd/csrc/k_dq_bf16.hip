@@ -317,12 +317,8 @@ __global__ __launch_bounds__(512, 1) void dq_partials_bf16(
     if (u < n_full) block(std::integral_constant<int, 7>{}, T{}, u++);
     // dQ of the last pipelined subtile
     const int ul = n_full - 1;
-    switch ((ul >> 1) & 3) {
-      case 0: dqr_dq<D>(fr, KT[0], ul & 1, dsp, acc); break;
-      case 1: dqr_dq<D>(fr, KT[1], ul & 1, dsp, acc); break;
-      case 2: dqr_dq<D>(fr, KT[2], ul & 1, dsp, acc); break;
-      default: dqr_dq<D>(fr, KT[3], ul & 1, dsp, acc); break;
-    }
+    const int bl = (ul >> 1) & 3;
+    dqr_dq<D>(fr, bl == 0 ? kt0 : bl == 1 ? kt1 : bl == 2 ? kt2 : kt3, ul & 1, dsp, acc);
   }
 
   // Masked subtiles near the causal diagonal or a chunk end.
