@@ -36,13 +36,16 @@
 // by scheduling barriers.
 //
 // resp_dkdv_bf16: the same pipeline for a tile of one response's own keys, over that
-// response's rows from the tile's first key on, in decreasing row order; the subtiles
-// at the causal diagonal run unpipelined with the mask.
+// response's rows from the tile's first key on, in decreasing row order, cut into
+// segments of stages so that the tiles' work items cost alike; the subtiles at the causal
+// diagonal run unpipelined with the mask.  resp_dkdv_reduce adds the later segments'
+// partial sums in segment order.
 #include <type_traits>
 
 #include "k_attn_tile.h"
 #include "k_lds.h"
 #include "k_ring.h"
+#include "k_split.h"
 #include "kernels.h"
 
 namespace rr {
@@ -53,7 +56,7 @@ namespace rr {
 
 namespace {
 
-constexpr int kPgStage = 64;   // stream rows per stage
+constexpr int kPgStage = kPgStageRows;
 
 template <int D>
 struct PgCfg {
@@ -458,19 +461,21 @@ __global__ __launch_bounds__(256, 1) void prompt_dkdv_bf16(
 }
 
 // ---- response keys: the causal dK_r, dV_r of the launch's rows ------------------------------
-// One workgroup per (response k, KV head g, 128 response keys j0 ..), four waves of 32 keys,
-// over the stream rows of response k that can see a key of the tile (rows r >= j0; the
-// stream holds the launch's rows [row_lo, row_hi), so keys from row_hi on are untouched).  The
-// stages run from the response's last stream stage down to the one holding row j0, and
-// each stage's two subtiles upper first, so rows decrease along the sequence: every
-// subtile before n_full holds only rows r >= j0 + 127, which see every key of the tile
-// (the pipelined blocks, as in the prompt kernel); the rest, near the causal diagonal, run
-// unpipelined with p = 0 wherever key > row.  Results are added to dk_r, dv_r.
+// A tile (response k, KV head g, 128 response keys j0 ..) sees the stream rows of response k
+// with r >= j0 (the stream holds the launch's rows [row_lo, row_hi), so keys from row_hi on
+// are untouched).  Its stages run from the response's last stream stage down to the one
+// holding row j0, each stage's two subtiles upper first, so rows decrease along the
+// sequence.  That run is cut into segments (k_split.h), one workgroup of four waves of 32
+// keys each.  Within a segment, every subtile before n_full holds only rows r >= j0 + 127,
+// which see every key of the tile (the pipelined blocks, as in the prompt kernel); the
+// rest, near the causal diagonal (only in a tile's last segment), run unpipelined with
+// p = 0 wherever key > row.  A tile's first segment adds its sums to dk_r, dv_r; a later
+// one writes them to its partial slot, which resp_dkdv_reduce adds afterwards.
 template <int D>
 __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
-    Geom g, PgGeom pg, const uint16_t* __restrict__ k_r, const uint16_t* __restrict__ v_r,
+    Geom g, PgGeom pg, DkdvSplit sp, const uint16_t* __restrict__ k_r, const uint16_t* __restrict__ v_r,
     const uint16_t* __restrict__ qs, const uint16_t* __restrict__ os, const float* __restrict__ sts,
-    float* __restrict__ dk_r, float* __restrict__ dv_r) {
+    float* __restrict__ slots, float* __restrict__ dk_r, float* __restrict__ dv_r) {
   using C = PgCfg<D>;
   constexpr int KS = C::KS, DT = C::DT;
   // the same fixed layout as prompt_dkdv_bf16
@@ -480,26 +485,12 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
   float* const st0 = reinterpret_cast<float*>(lds + 8 * C::TILE);
   float* const SB[4] = {st0, st0 + 2 * kPgStage, st0 + 4 * kPgStage, st0 + 6 * kPgStage};
 
-  // work item: (k, g) outer, key tiles inner (heaviest first); plain block order, so every
-  // XCD receives a mix of long and short tiles
-  int64_t idx = blockIdx.x;
-  int k = 0, gh = 0, kt = 0;
-  {
-    bool found = false;
-    for (int kk = 0; kk < g.K && !found; ++kk) {
-      const int kmax_k = g.r_len[kk] < g.row_hi ? g.r_len[kk] : g.row_hi;
-      const int64_t nt = (kmax_k + C::KEYS - 1) / C::KEYS;
-      if (idx < nt * g.Hkv) {
-        k = kk;
-        gh = (int)(idx / nt);
-        kt = (int)(idx % nt);
-        found = true;
-      } else {
-        idx -= nt * g.Hkv;
-      }
-    }
-    if (!found) return;
-  }
+  static_assert(C::KEYS == kRespKeys, "tile width");
+  // work item: (k, KV head, tile, segment); plain block order, so every XCD receives a mix
+  // of tiles
+  const DkdvItem item = dkdv_item(g, pg, sp, (int)blockIdx.x);
+  if (item.k < 0) return;
+  const int k = item.k, gh = item.gh, kt = item.kt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;   // keys the rows can see
@@ -516,16 +507,15 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
                               : make_uint4(0, 0, 0, 0));
   }
 
-  // stream stages of response k: [0, n_seg), stage s holding flattened rows m_lo + 64 s ..;
-  // those from s0 on hold a row r >= max(j0, row_lo)
+  // stream stages of response k: stage s holds flattened rows m_lo + 64 s ..; this item
+  // runs the segment's stages from stream stage n_top - 1 down
   const int grp = g.grp;
-  const int n_seg = (pg.off[k + 1] - pg.off[k]) / C::BM;
-  const int s0 = ((j0 > g.row_lo ? j0 : g.row_lo) * grp - pg.m_lo) / C::BM;
-  const int n_stages = n_seg > s0 ? n_seg - s0 : 0;
+  const int n_stages = item.n_stages;
+  const int n_top = item.n_top;
   const int n_sub = 2 * n_stages;
-  // subtile u of the sequence: stage n_seg - 1 - u / 2, upper half first; its first row is
-  // m = m_lo + 64 n_seg - 32 (u + 1)
-  const int m_top = pg.m_lo + C::BM * n_seg;
+  // subtile u of the sequence: stage n_top - 1 - u / 2, upper half first; its first row is
+  // m = m_lo + 64 n_top - 32 (u + 1)
+  const int m_top = pg.m_lo + C::BM * n_top;
   const int n_full_raw = (m_top - (j0 + C::KEYS - 1) * grp) / 32;
   const int n_full = n_full_raw < 0 ? 0 : (n_full_raw > n_sub ? n_sub : n_full_raw);
   const int64_t row0 = (int64_t)gh * pg.n_rows + pg.off[k];
@@ -540,9 +530,9 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
   FarFrags<D> far;
   far.template init<true, true>(fr);
 
-  // sequence stage t is stream stage n_seg - 1 - t
+  // sequence stage t is stream stage n_top - 1 - t
   auto issue_stage = [&](int b, int t) {
-    const int st = n_seg - 1 - t;
+    const int st = n_top - 1 - t;
     const int64_t off = (int64_t)st * C::TILE;
     dl.issue(lds_addr(QT[b]), qb + off, C::BM, (uint32_t)(D * 2));
     dl.issue(lds_addr(OT[b]), ob + off, C::BM, (uint32_t)(D * 2));
@@ -690,6 +680,21 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
   wait_vmcnt0();
 
   if (!kvalid) return;
+  if (item.slot >= 0) {
+    // a later segment: its partial sums go to its slot, for the ordered reduction
+    float* pk = slots + (item.slot * C::KEYS + wave * 32 + col) * (2 * D);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = dt * 32 + i4 * 8 + hl * 4;
+        *reinterpret_cast<float4*>(pk + d0) =
+            make_float4(dk[dt][4 * i4 + 0], dk[dt][4 * i4 + 1], dk[dt][4 * i4 + 2], dk[dt][4 * i4 + 3]);
+        *reinterpret_cast<float4*>(pk + D + d0) =
+            make_float4(dv[dt][4 * i4 + 0], dv[dt][4 * i4 + 1], dv[dt][4 * i4 + 2], dv[dt][4 * i4 + 3]);
+      }
+    return;
+  }
   float* dkq = dk_r + kvrow * D;
   float* dvq = dv_r + kvrow * D;
 #pragma unroll
@@ -710,6 +715,53 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
       *reinterpret_cast<float4*>(dkq + d0) = a;
       *reinterpret_cast<float4*>(dvq + d0) = b;
     }
+}
+
+// Ordered reduction of the later segments: one workgroup per (k, KV head, tile) in item
+// order; for each valid key of the tile, dk_r += tau (slot_1 + slot_2 + ...) and dv_r +=
+// the same sum of the dV halves, the slots added in segment order.
+template <int D>
+__global__ __launch_bounds__(256) void resp_dkdv_reduce(Geom g, PgGeom pg, DkdvSplit sp,
+                                                        const float* __restrict__ slots, float* __restrict__ dk_r,
+                                                        float* __restrict__ dv_r) {
+  int idx = (int)blockIdx.x;
+  int k = 0;
+  for (; k < g.K; ++k) {
+    const int n = g.Hkv * resp_tiles(g, k);
+    if (idx < n) break;
+    idx -= n;
+  }
+  if (k >= g.K) return;
+  const int nt = resp_tiles(g, k);
+  const int gh = idx / nt, kt = idx % nt;
+  const int n_items = resp_tile_items(g, pg, sp, k, kt);
+  if (n_items < 2) return;
+  const int64_t s0 = dkdv_tile_slot(g, pg, sp, k, gh, kt);
+  const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
+  constexpr int V4 = 2 * D / 4;   // float4 columns of a slot row (dK then dV)
+  for (int e = threadIdx.x; e < kRespKeys * V4; e += blockDim.x) {
+    const int key_in = e / V4, c = e % V4;
+    const int key = kt * kRespKeys + key_in;
+    if (key >= kmax) continue;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < n_items - 1; ++i) {
+      const float4 b = *reinterpret_cast<const float4*>(slots + ((s0 + i) * kRespKeys + key_in) * (2 * D) + 4 * c);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const int64_t kvrow = ((int64_t)k * g.R + key) * g.Hkv + gh;
+    const bool is_v = 4 * c >= D;
+    float* dst = (is_v ? dv_r : dk_r) + kvrow * D + (4 * c - (is_v ? D : 0));
+    const float sc = is_v ? 1.0f : g.tau;
+    float4 o = *reinterpret_cast<const float4*>(dst);
+    o.x += a.x * sc;
+    o.y += a.y * sc;
+    o.z += a.z * sc;
+    o.w += a.w * sc;
+    *reinterpret_cast<float4*>(dst) = o;
+  }
 }
 
 // ---- fp32 kernel --------------------------------------------------------------------------
@@ -812,21 +864,29 @@ hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void
 }
 
 hipError_t launch_resp_dkdv(const Geom& g, const PgGeom& pg, const void* k_r, const void* v_r, const void* qs,
-                            const void* os, const float* sts, float* dk_r, float* dv_r, hipStream_t s) {
-  int64_t n = 0;
-  for (int k = 0; k < g.K; ++k) {
-    const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
-    n += (int64_t)g.Hkv * ((kmax + PgCfg<128>::KEYS - 1) / PgCfg<128>::KEYS);
-  }
-  if (n == 0) return hipSuccess;
+                            const void* os, const float* sts, float* slots, float* dk_r, float* dv_r,
+                            hipStream_t s) {
+  DkdvSplit sp{};
+  int64_t n_slots = 0, tiles = 0;
+  const int64_t items = plan_dkdv_split(g, pg, kDkdvItemsTarget, kDkdvMinSeg, sp, n_slots, tiles);
+  if (items == 0) return hipSuccess;
+  // a later segment of response k holds seg[k] stages, so response k has at most
+  // total_k / seg[k] <= kDkdvItemsTarget of them
+  if (n_slots > (int64_t)g.K * dkdv_slots_per_response(g.R, g.Hkv, g.grp)) return hipErrorInvalidValue;
   const uint16_t *kr = (const uint16_t*)k_r, *vr = (const uint16_t*)v_r;
   const uint16_t *q16 = (const uint16_t*)qs, *o16 = (const uint16_t*)os;
   if (g.dqk == 64)
-    hipLaunchKernelGGL(resp_dkdv_bf16<64>, dim3((unsigned)n), dim3(256), 0, s, g, pg, kr, vr, q16, o16, sts, dk_r,
-                       dv_r);
+    hipLaunchKernelGGL(resp_dkdv_bf16<64>, dim3((unsigned)items), dim3(256), 0, s, g, pg, sp, kr, vr, q16, o16, sts,
+                       slots, dk_r, dv_r);
   else
-    hipLaunchKernelGGL(resp_dkdv_bf16<128>, dim3((unsigned)n), dim3(256), 0, s, g, pg, kr, vr, q16, o16, sts, dk_r,
-                       dv_r);
+    hipLaunchKernelGGL(resp_dkdv_bf16<128>, dim3((unsigned)items), dim3(256), 0, s, g, pg, sp, kr, vr, q16, o16,
+                       sts, slots, dk_r, dv_r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_slots == 0) return e;
+  if (g.dqk == 64)
+    hipLaunchKernelGGL(resp_dkdv_reduce<64>, dim3((unsigned)tiles), dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
+  else
+    hipLaunchKernelGGL(resp_dkdv_reduce<128>, dim3((unsigned)tiles), dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
   return hipGetLastError();
 }
 

@@ -79,8 +79,10 @@ hipError_t launch_pg_pack(const Geom& g, const PgGeom& pg, int dtype, const void
                           const float* lse, const void* d_o, void* qs, void* os, float* sts, hipStream_t s);
 // dk_r, dv_r += the causal response-key gradients of every row of every response (bf16),
 // over the same packed stream.
+// `slots`: kDkdvSlots partial slots of [128][d_qk + d_v] fp32 (free workspace).
 hipError_t launch_resp_dkdv(const Geom& g, const PgGeom& pg, const void* k_r, const void* v_r, const void* qs,
-                            const void* os, const float* sts, float* dk_r, float* dv_r, hipStream_t s);
+                            const void* os, const float* sts, float* slots, float* dk_r, float* dv_r,
+                            hipStream_t s);
 hipError_t launch_prompt_dkdv(const Geom& g, const PgGeom& pg, int dtype, const void* k_p, const void* v_p,
                               const void* qs, const void* os, const float* sts, int64_t key_lo, int64_t key_hi,
                               float* dk_p, float* dv_p, int accumulate, hipStream_t s);

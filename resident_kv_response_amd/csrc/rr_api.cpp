@@ -2,6 +2,7 @@
 // stream.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
@@ -391,14 +392,20 @@ int rr_attn_bwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, 
     const PgGeom pg = make_pg_geom(p, r_len, g.row_lo, g.row_hi);
     const size_t srows = (size_t)p->Hkv * pg.n_rows;
     const size_t sbytes = align_up(srows * p->d_qk * 2, 256);
+    const size_t dq_bytes = (size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float);
+    const size_t slot_bytes = ws_dkdv_slots_bytes(p);
     char* sbase = reinterpret_cast<char*>(carve(ws, align_up(rows * sizeof(float), 256) +
-                                                        align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256)));
+                                                        align_up(std::max(dq_bytes, slot_bytes), 256)));
     void* qs = sbase;
     void* os = sbase + sbytes;
     float* sts = reinterpret_cast<float*>(sbase + 2 * sbytes);
+    // the dQ partials are reduced by now: their region holds the dK/dV partial slots
+    float* slots = dq_part;
     if ((e = timed("pg_pack", s, [&] { return launch_pg_pack(g, pg, p->dtype, q, o, lse, d_o, qs, os, sts, s); })))
       return hip_fail(e, "pg_pack");
-    if ((e = timed("dkdv", s, [&] { return launch_resp_dkdv(g, pg, k_r, v_r, qs, os, sts, dk_r, dv_r, s); })))
+    if ((e = timed("dkdv", s, [&] {
+           return launch_resp_dkdv(g, pg, k_r, v_r, qs, os, sts, slots, dk_r, dv_r, s);
+         })))
       return hip_fail(e, "dkdv");
     return RR_OK;
   }

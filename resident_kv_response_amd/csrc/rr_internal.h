@@ -77,6 +77,24 @@ struct PgGeom {
   int32_t off[RR_MAX_K + 1];
 };
 PgGeom make_pg_geom(const rr_problem* p, const int32_t* r_len, int32_t row_lo, int32_t row_hi);
+// The response dK/dV kernel cuts each 128-key tile's run of stream stages into segments of
+// at most `seg` stages, one workgroup each, so that long and short tiles cost alike; the
+// first segment of a tile adds its sum to dk_r / dv_r, every later one writes a partial
+// slot ([128 keys][d] fp32 for dK, then for dV) that an ordered reduction adds afterwards.
+// seg is chosen per response so that each response of a launch has at most
+// kDkdvItemsTarget later segments, which the workspace's kDkdvSlots slots per response
+// bound with room to spare.
+constexpr int kDkdvItemsTarget = 768;
+constexpr int kDkdvSlots = 1024;
+constexpr int kDkdvMinSeg = 8;
+// Slots a response of at most R_max rows can need: kDkdvSlots, or fewer when its
+// stage-tiles (Hkv x 128-key tiles x 64-row stages) divided by kDkdvMinSeg are fewer.
+inline int64_t dkdv_slots_per_response(int64_t R_max, int64_t Hkv, int64_t grp) {
+  const int64_t stage_tiles = Hkv * ((R_max + 127) / 128) * ((R_max * grp + 63) / 64);
+  const int64_t by_size = stage_tiles / kDkdvMinSeg;
+  return by_size < kDkdvSlots ? by_size : kDkdvSlots;
+}
+size_t ws_dkdv_slots_bytes(const rr_problem* p);
 int validate_blend(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,
                    const void* x_layer, const void* x_last, const void* x_out);
 int validate_blend_bwd(int64_t rows, int32_t Hkv, int32_t d, int32_t dtype, const float* alpha,

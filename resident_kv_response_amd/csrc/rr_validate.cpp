@@ -106,10 +106,17 @@ size_t ws_bwd_bytes(const rr_problem* p) {
   if (p->latent)   // D, P and dS of the response pairs, chunk partials of dK_r / dV_r
     return align_up(rows * sizeof(float), 256) + 2 * ws_pds_bytes(p) +
            align_up((size_t)xty_n_chunks(p->R_max) * p->K * p->R_max * p->d_qk * sizeof(float), 256);
-  // D, the dQ partials, then (bf16) the packed row stream of the response dK/dV kernel
-  return align_up(rows * sizeof(float), 256) +
-         align_up((size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float), 256) +
+  // D, the dQ partials (whose region the response dK/dV partial slots reuse once dQ is
+  // reduced), then (bf16) the packed row stream of the response dK/dV kernel
+  const size_t dq_part = (size_t)n_parts_of(p) * rows * p->d_qk * sizeof(float);
+  const size_t slots = p->dtype == RR_BF16 ? ws_dkdv_slots_bytes(p) : 0;
+  return align_up(rows * sizeof(float), 256) + align_up(dq_part > slots ? dq_part : slots, 256) +
          (p->dtype == RR_BF16 ? ws_prompt_bytes(p) : 0);
+}
+
+size_t ws_dkdv_slots_bytes(const rr_problem* p) {
+  return (size_t)p->K * dkdv_slots_per_response(p->R_max, p->Hkv, p->Hq / p->Hkv) * 128 * (p->d_qk + p->d_v) *
+         sizeof(float);
 }
 
 // Stream rows per KV head bound for the workspace: every response at R_max rows.

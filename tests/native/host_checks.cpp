@@ -1,6 +1,7 @@
 // Host-compiled checks of the library's integer and host logic (no GPU): the address
 // arithmetic of the direct global->LDS loads (csrc/k_addr.h, the functions the kernels
-// call), the classification of pointer lookups, and the accumulation window's
+// call), the work split of the response dK/dV kernel (csrc/k_split.h), the
+// classification of pointer lookups, and the accumulation window's
 // version/resident checks (csrc/rr_validate.cpp).  Built and run by
 // tests/test_host_native.py; prints one line per group and exits non-zero on the first
 // failure.
@@ -8,9 +9,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "k_addr.h"
+#include "k_split.h"
 #include "rr_internal.h"
 
 using namespace rr;
@@ -200,8 +203,150 @@ static void check_accum() {
   std::printf("accumulator: ok\n");
 }
 
+// ---- work split of the response dK/dV kernel --------------------------------------------
+// Every (response, KV head, key tile) gets its stages [0, resp_tile_stages) from exactly one
+// segment each, in order; each item's stream stages lie inside the response's stream and
+// its 64-row stages hold rows that can see the tile (stage >= the one of row max(j0,
+// row_lo)); later segments get distinct slots below the workspace's bound, numbered as the
+// reduction reads them; and the grid's items after the last decode to nothing.
+static void check_dkdv_case(int K, const std::vector<int>& lens, int R_max, int Hq, int Hkv, int row_lo,
+                            int row_hi) {
+  rr_problem p{};
+  p.P = 4096;
+  p.chunk = 1024;
+  p.R_max = R_max;
+  p.K = K;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.d_qk = p.d_v = 128;
+  p.block = 2048;
+  p.dtype = RR_BF16;
+  p.tau = 0.088f;
+  Geom g = make_geom(&p, lens.data());
+  g.row_lo = row_lo;
+  g.row_hi = row_hi;
+  const PgGeom pg = make_pg_geom(&p, lens.data(), row_lo, row_hi);
+  DkdvSplit sp{};
+  int64_t n_slots = 0, tiles = 0;
+  const int64_t items = plan_dkdv_split(g, pg, kDkdvItemsTarget, kDkdvMinSeg, sp, n_slots, tiles);
+  CHECK(n_slots <= (int64_t)K * kDkdvItemsTarget &&
+            n_slots <= (int64_t)K * dkdv_slots_per_response(R_max, Hkv, Hq / Hkv),
+        "%lld slots", (long long)n_slots);
+  for (int k = 0; k < K; ++k) {
+    CHECK(sp.seg[k] >= kDkdvMinSeg, "segment of %d stages", sp.seg[k]);
+    CHECK(sp.slot_off[k + 1] - sp.slot_off[k] <= kDkdvItemsTarget, "response %d has %d slots", k,
+          sp.slot_off[k + 1] - sp.slot_off[k]);
+  }
+  // next stage expected per (k, gh, kt), and slot use
+  std::vector<std::vector<int>> next(K);
+  int64_t n_tiles = 0;
+  for (int k = 0; k < K; ++k) {
+    next[k].assign((size_t)Hkv * resp_tiles(g, k), 0);
+    n_tiles += (int64_t)Hkv * resp_tiles(g, k);
+  }
+  CHECK(n_tiles == tiles, "tile count %lld vs %lld", (long long)n_tiles, (long long)tiles);
+  std::vector<int> slot_used((size_t)n_slots, 0);
+  for (int64_t idx = 0; idx < items + 8; ++idx) {
+    const DkdvItem it = dkdv_item(g, pg, sp, (int)idx);
+    if (idx >= items) {
+      CHECK(it.k < 0, "item %lld past the end decodes to response %d", (long long)idx, it.k);
+      continue;
+    }
+    if (it.k < 0 || it.k >= K || it.gh < 0 || it.gh >= Hkv || it.kt < 0 || it.kt >= resp_tiles(g, it.k)) {
+      CHECK(false, "item %lld decodes to (%d, %d, %d)", (long long)idx, it.k, it.gh, it.kt);
+      continue;
+    }
+    int& nx = next[it.k][(size_t)it.gh * resp_tiles(g, it.k) + it.kt];
+    CHECK(it.t0 == nx, "item %lld starts at stage %d, expected %d", (long long)idx, it.t0, nx);
+    CHECK(it.n_stages >= 1 && it.n_stages <= sp.seg[it.k], "item %lld has %d stages", (long long)idx, it.n_stages);
+    nx = it.t0 + it.n_stages;
+    const int n_seg = (pg.off[it.k + 1] - pg.off[it.k]) / kPgStageRows;
+    const int j0 = it.kt * kRespKeys;
+    const int s0 = ((j0 > row_lo ? j0 : row_lo) * g.grp - pg.m_lo) / kPgStageRows;
+    const int lo_stage = it.n_top - it.n_stages, hi_stage = it.n_top - 1;
+    CHECK(hi_stage < n_seg && lo_stage >= s0 && lo_stage >= 0, "item %lld stream stages [%d, %d] outside [%d, %d)",
+          (long long)idx, lo_stage, hi_stage, s0, n_seg);
+    if (it.seg_idx == 0) {
+      CHECK(it.slot == -1, "first segment with slot %lld", (long long)it.slot);
+    } else {
+      const int64_t want = dkdv_tile_slot(g, pg, sp, it.k, it.gh, it.kt) + it.seg_idx - 1;
+      CHECK(it.slot == want, "item %lld slot %lld, the reduction reads %lld", (long long)idx, (long long)it.slot,
+            (long long)want);
+      if (it.slot >= 0 && it.slot < n_slots) slot_used[(size_t)it.slot]++;
+      else CHECK(false, "item %lld slot %lld outside [0, %lld)", (long long)idx, (long long)it.slot, (long long)n_slots);
+    }
+  }
+  for (int k = 0; k < K; ++k)
+    for (int gh = 0; gh < Hkv; ++gh)
+      for (int kt = 0; kt < resp_tiles(g, k); ++kt)
+        CHECK(next[k][(size_t)gh * resp_tiles(g, k) + kt] == resp_tile_stages(g, pg, k, kt),
+              "tile (%d, %d, %d) covered up to stage %d of %d", k, gh, kt,
+              next[k][(size_t)gh * resp_tiles(g, k) + kt], resp_tile_stages(g, pg, k, kt));
+  for (int64_t i = 0; i < n_slots; ++i) CHECK(slot_used[(size_t)i] == 1, "slot %lld used %d times", (long long)i, slot_used[(size_t)i]);
+}
+
+// A call over K responses cuts each response's tiles exactly as a call of that response
+// alone does (same segment length, same segments), so both sum every key's gradient in the
+// same order.
+static void check_dkdv_split_per_response(const std::vector<int>& lens, int R_max, int Hq, int Hkv) {
+  auto plan = [&](const std::vector<int>& ls, int R) {
+    rr_problem p{};
+    p.P = 4096;
+    p.chunk = 1024;
+    p.R_max = R;
+    p.K = (int)ls.size();
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d_qk = p.d_v = 128;
+    p.block = 2048;
+    p.dtype = RR_BF16;
+    p.tau = 0.088f;
+    const Geom g = make_geom(&p, ls.data());
+    const PgGeom pg = make_pg_geom(&p, ls.data(), 0, R);
+    DkdvSplit sp{};
+    int64_t n_slots = 0, tiles = 0;
+    const int64_t items = plan_dkdv_split(g, pg, kDkdvItemsTarget, kDkdvMinSeg, sp, n_slots, tiles);
+    // (k, gh, kt, seg_idx, t0, n_stages) of every item
+    std::vector<std::vector<int>> out;
+    for (int64_t i = 0; i < items; ++i) {
+      const DkdvItem it = dkdv_item(g, pg, sp, (int)i);
+      out.push_back({it.k, it.gh, it.kt, it.seg_idx, it.t0, it.n_stages});
+    }
+    return std::make_pair(sp, out);
+  };
+  const auto many = plan(lens, R_max);
+  for (int k = 0; k < (int)lens.size(); ++k) {
+    const auto one = plan({lens[k]}, lens[k] > 0 ? lens[k] : 1);
+    CHECK(many.first.seg[k] == one.first.seg[0], "response %d: segment %d in the call, %d alone", k,
+          many.first.seg[k], one.first.seg[0]);
+    std::vector<std::vector<int>> mine;
+    for (const auto& v : many.second)
+      if (v[0] == k) mine.push_back({0, v[1], v[2], v[3], v[4], v[5]});
+    CHECK(mine == one.second, "response %d is cut differently in the call of %zu", k, lens.size());
+  }
+}
+
+static void check_dkdv_split() {
+  check_dkdv_split_per_response({7666, 3930, 7116, 3152, 4233, 3153, 2159, 6650}, 8192, 24, 4);
+  check_dkdv_split_per_response({520, 300, 65, 1}, 520, 24, 4);
+  check_dkdv_split_per_response({90, 41, 7}, 96, 4, 1);
+  // the 2M group's members one by one (24 query heads on 4 KV heads)
+  for (int r : {7666, 3930, 7116, 3152, 4233, 3153, 2159, 6650}) check_dkdv_case(1, {r}, 8192, 24, 4, 0, 8192);
+  check_dkdv_case(1, {4096}, 4096, 32, 8, 0, 4096);                 // GQA, 32 heads on 8
+  check_dkdv_case(1, {8192}, 8192, 24, 4, 0, 8192);                 // one-rank share
+  for (int b = 0; b < 4; ++b) check_dkdv_case(1, {8192}, 8192, 24, 4, 2048 * b, 2048 * (b + 1));   // block walk
+  check_dkdv_case(1, {4096}, 4096, 32, 8, 2048, 4096);
+  check_dkdv_case(8, {7666, 3930, 7116, 3152, 4233, 3153, 2159, 6650}, 8192, 24, 4, 0, 8192);   // one call
+  check_dkdv_case(3, {1, 0, 300}, 384, 4, 1, 0, 384);               // tiny, empty and ragged
+  check_dkdv_case(4, {256, 129, 128, 77}, 256, 4, 2, 0, 256);
+  check_dkdv_case(2, {513, 1000}, 1000, 6, 2, 100, 700);           // a block walk with ragged ends
+  check_dkdv_case(1, {0}, 64, 4, 1, 0, 64);                         // nothing to do
+  std::printf("response dK/dV split: ok\n");
+}
+
 int main() {
   check_addresses();
+  check_dkdv_split();
   check_pointers();
   check_accum();
   if (g_fail) {

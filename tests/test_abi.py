@@ -160,6 +160,28 @@ def test_workspace_and_parts_formulas():
         R.rr_workspace_bytes(_prob(Hq=3, Hkv=2), R.RR_OP_FWD)
 
 
+def test_bwd_workspace_holds_the_key_gradient_slots():
+    # bf16: the dQ partials' region is reused, once dQ is reduced, for the partial slots
+    # ([128 keys][d_qk + d_v] fp32) of the response dK/dV kernel's later segments: per
+    # response min(1024, Hkv * key tiles * 64-row stages / 8); a small problem with a short
+    # prompt needs the slots' size, a large one the partials'
+    up = lambda x: -(-x // 256) * 256
+    p = _prob(P=64, R_max=2048, Hq=4, Hkv=1, d_qk=64, d_v=64, chunk=64, dtype=R.RR_BF16)
+    rows = 2048 * 4
+    slots = min(1024, 1 * 16 * 128 // 8) * 128 * (64 + 64) * 4
+    assert 2 * rows * 64 * 4 < slots
+    stream = 1 * 2048 * 4
+    assert R.rr_workspace_bytes(p, R.RR_OP_BWD) == (up(rows * 4) + up(slots) + 2 * up(stream * 64 * 2)
+                                                    + up(stream * 8))
+    # K responses: K times the slots
+    pk = _prob(P=64, R_max=2048, Hq=4, Hkv=1, d_qk=64, d_v=64, chunk=64, dtype=R.RR_BF16, K=3)
+    assert R.rr_workspace_bytes(pk, R.RR_OP_BWD) == (up(3 * rows * 4) + up(3 * slots) + 2 * up(3 * stream * 64 * 2)
+                                                     + up(3 * stream * 8))
+    # fp32 runs no segmented kernel: D and the dQ partials only
+    p32 = _prob(P=64, R_max=2048, Hq=4, Hkv=1, d_qk=64, d_v=64, chunk=64, dtype=R.RR_F32)
+    assert R.rr_workspace_bytes(p32, R.RR_OP_BWD) == up(rows * 4) + up(2 * rows * 64 * 4)
+
+
 def _accum(G=8, version=5):
     acc = R.CAccum()
     seen = (ctypes.c_uint8 * G)()
