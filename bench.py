@@ -57,7 +57,23 @@ def _args():
     ap.add_argument("--full-sequence", action="store_true",
                     help="full-sequence differential mode: every call also forms the prompt K/V "
                          "gradients (rr_attn_prompt_grads), summed over the group")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy and exit: the reference kernel for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
+
+
+def copy_calibration() -> int:
+    """One device copy of 2^28 fp32 (1 GiB read, 1 GiB written), for the counter scale."""
+    import torch
+
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": x.numel() * 4}))
+    return 0
 
 
 def kernel_flops(w, R: int) -> dict:
@@ -94,10 +110,11 @@ def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
 
 
 KERNEL_SOURCES = {
-    "fwd_partials": ["k_fwd_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "dq_partials": ["k_dq_bf16.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "dkdv": ["k_kv_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
-    "prompt_dkdv": ["k_kv_grads.hip", "k_ring.h", "k_lds.h", "k_attn_tile.h", "k_common.h"],
+    "fwd_partials": ["k_fwd_bf16.hip", "k_ring.h", "k_lds.h", "k_addr.h", "k_attn_tile.h", "k_common.h"],
+    "dq_partials": ["k_dq_bf16.hip", "k_ring.h", "k_lds.h", "k_addr.h", "k_attn_tile.h", "k_common.h"],
+    "dkdv": ["k_kv_grads.hip", "k_split.h", "k_ring.h", "k_lds.h", "k_addr.h", "k_attn_tile.h", "k_common.h"],
+    "prompt_dkdv": ["k_kv_grads.hip", "k_split.h", "k_ring.h", "k_lds.h", "k_addr.h", "k_attn_tile.h",
+                    "k_common.h"],
 }
 
 
@@ -114,6 +131,8 @@ def main() -> int:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
         return 2
+    if a.copy_calibration:
+        return copy_calibration()
     from resident_kv_response_amd import configs
 
     w = configs.BY_NAME[a.workload]
@@ -405,10 +424,10 @@ def run_dense(a, w) -> int:
 
 LATENT_SOURCES = {
     "topk_select": ["k_topk.hip", "k_common.h", "k_lds.h", "k_addr.h"],
-    "sparse_fwd": ["k_sparse.hip", "k_lds.h", "k_common.h"],
-    "sparse_dq": ["k_sparse.hip", "k_lds.h", "k_common.h"],
-    "xty_dk": ["k_sparse.hip", "k_lds.h", "k_common.h"],
-    "xty_dv": ["k_sparse.hip", "k_lds.h", "k_common.h"],
+    "sparse_fwd": ["k_sparse.hip", "k_lds.h", "k_addr.h", "k_common.h"],
+    "sparse_dq": ["k_sparse.hip", "k_lds.h", "k_addr.h", "k_common.h"],
+    "xty_dk": ["k_sparse.hip", "k_lds.h", "k_addr.h", "k_common.h"],
+    "xty_dv": ["k_sparse.hip", "k_lds.h", "k_addr.h", "k_common.h"],
 }
 
 

@@ -491,9 +491,10 @@ __global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
   }
 }
 
-// Launched with one 32-row tile per wave.  Two tiles per wave (64 rows, one wave per
-// SIMD) halve LDS reads per MFMA, but their accumulators, Q fragments and score tiles need
-// more registers than this compiler allocates without spilling.
+// Launched with one 32-row tile per wave, two waves per SIMD.  Two tiles per wave (64
+// rows, one wave per SIMD) halve LDS reads per MFMA; with the accumulators held in AGPRs
+// that form is correct but 12 % slower on MI355X: the second wave of a SIMD hides more
+// latency than the halved LDS traffic saves.
 hipError_t launch_fwd_partials_bf16(const Geom& g, const AttnPtrs& a, hipStream_t s) {
   const uint16_t *q = (const uint16_t*)a.q, *kp = (const uint16_t*)a.k_p, *vp = (const uint16_t*)a.v_p;
   const uint16_t *kr = (const uint16_t*)a.k_r, *vr = (const uint16_t*)a.v_r;
