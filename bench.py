@@ -79,14 +79,16 @@ def copy_calibration() -> int:
 def kernel_flops(w, R: int) -> dict:
     """Algorithmic flops of each launch kind for one member of length R (d_qk = d_v = d).
     dq_partials: S, dP and dQ over every visible pair; fwd_partials: S and PV over every
-    visible pair; dkdv: dK and dV over the response pairs (the S / dP it recomputes are
-    not counted); prompt_dkdv (full-sequence mode only): S, dP, dK and dV over every
-    (row, prompt key) pair, since without stored scores the prompt gradient needs all four."""
+    visible pair; dkdv: S, dP, dK and dV over the response pairs; prompt_dkdv (full-sequence
+    mode only): S, dP, dK and dV over every (row, prompt key) pair.  Each is the set of
+    contractions that kernel performs (without stored scores, a key-parallel gradient kernel
+    recomputes S and dP).  These are per-kernel figures: the step's value counts every pair's
+    S and dP once (configs.flops_dense), so the recomputation in dkdv adds nothing to it."""
     d, Hq = w.d_qk, w.Hq
     n_p, n_r = R * w.P, R * (R + 1) // 2
     return {"fwd_partials": 4.0 * d * Hq * (n_p + n_r),
             "dq_partials": 6.0 * d * Hq * (n_p + n_r),
-            "dkdv": 4.0 * d * Hq * n_r,
+            "dkdv": 8.0 * d * Hq * n_r,
             "prompt_dkdv": 8.0 * d * Hq * n_p}
 
 

@@ -717,14 +717,18 @@ __global__ __launch_bounds__(256, 1) void resp_dkdv_bf16(
     }
 }
 
-// Ordered reduction of the later segments: one workgroup per (k, KV head, tile) in item
-// order; for each valid key of the tile, dk_r += tau (slot_1 + slot_2 + ...) and dv_r +=
-// the same sum of the dV halves, the slots added in segment order.
+// Ordered reduction of the later segments: kDkdvReduceSplit workgroups per (k, KV head,
+// tile) in item order, each over 128 / kDkdvReduceSplit of the tile's keys; for each valid
+// key, dk_r += tau (slot_1 + slot_2 + ...) and dv_r += the same sum of the dV halves, the
+// slots added in segment order.
+constexpr int kDkdvReduceSplit = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void resp_dkdv_reduce(Geom g, PgGeom pg, DkdvSplit sp,
                                                         const float* __restrict__ slots, float* __restrict__ dk_r,
                                                         float* __restrict__ dv_r) {
-  int idx = (int)blockIdx.x;
+  int idx = (int)(blockIdx.x / kDkdvReduceSplit);
+  const int part = (int)(blockIdx.x % kDkdvReduceSplit);
   int k = 0;
   for (; k < g.K; ++k) {
     const int n = g.Hkv * resp_tiles(g, k);
@@ -738,9 +742,10 @@ __global__ __launch_bounds__(256) void resp_dkdv_reduce(Geom g, PgGeom pg, DkdvS
   if (n_items < 2) return;
   const int64_t s0 = dkdv_tile_slot(g, pg, sp, k, gh, kt);
   const int kmax = g.r_len[k] < g.row_hi ? g.r_len[k] : g.row_hi;
-  constexpr int V4 = 2 * D / 4;   // float4 columns of a slot row (dK then dV)
-  for (int e = threadIdx.x; e < kRespKeys * V4; e += blockDim.x) {
-    const int key_in = e / V4, c = e % V4;
+  constexpr int V4 = 2 * D / 4;                           // float4 columns of a slot row (dK then dV)
+  constexpr int KEYS = kRespKeys / kDkdvReduceSplit;      // keys of this workgroup
+  for (int e = threadIdx.x; e < KEYS * V4; e += blockDim.x) {
+    const int key_in = part * KEYS + e / V4, c = e % V4;
     const int key = kt * kRespKeys + key_in;
     if (key >= kmax) continue;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -883,10 +888,11 @@ hipError_t launch_resp_dkdv(const Geom& g, const PgGeom& pg, const void* k_r, co
                        sts, slots, dk_r, dv_r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_slots == 0) return e;
+  const dim3 rgrid((unsigned)(tiles * kDkdvReduceSplit));
   if (g.dqk == 64)
-    hipLaunchKernelGGL(resp_dkdv_reduce<64>, dim3((unsigned)tiles), dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
+    hipLaunchKernelGGL(resp_dkdv_reduce<64>, rgrid, dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
   else
-    hipLaunchKernelGGL(resp_dkdv_reduce<128>, dim3((unsigned)tiles), dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
+    hipLaunchKernelGGL(resp_dkdv_reduce<128>, rgrid, dim3(256), 0, s, g, pg, sp, slots, dk_r, dv_r);
   return hipGetLastError();
 }
 
