@@ -26,6 +26,7 @@
 // into chunks (one workgroup per chunk, key tile and dim tile) and the chunk partials are
 // added in chunk order, so the sums are deterministic.
 #include "k_lds.h"
+#include "k_ring.h"
 #include "kernels.h"
 
 namespace rr {
@@ -459,18 +460,26 @@ __device__ __forceinline__ void xty_rows(int c, int cr, int row_lo, int row_hi, 
 }
 
 // part[c][k][j][d] = sum over rows i of chunk c (xty_rows) and heads h of
-// X[k][i][h][j] * Y[k][i][h][d].  Workgroup tile: 128 keys j x 64 dims d (4 waves x 32
-// keys); inner dimension m = (i, h) in steps of 32.  Workgroups whose chunk has no rows
-// for their key tile return at once and write nothing.
+// X[k][i][h][j] * Y[k][i][h][d].  Workgroup tile: 128 keys j x 128 dims d, four waves of
+// 64 keys x 64 dims (each X^T and Y fragment feeds two MFMAs); inner dimension m = (i, h)
+// in stages of 64 (16 MFMAs per wave), loaded straight into a ring of three LDS buffers
+// (96 KiB) two stages ahead (the loads are issued from inline assembly and ordered by
+// explicit vmcnt waits, one barrier per stage).  The Y tile is two 64-dim halves; past n_d the second half re-reads the first
+// (its waves skip their MFMAs and writes), so every stage issues the same loads.
+// Workgroups whose chunk has no rows for their key tile return at once and write nothing.
+constexpr int kXtyM = 64;   // m rows per stage (a multiple of 32)
 __global__ __launch_bounds__(256, 2) void xty_gemm(const uint16_t* __restrict__ X,
                                                    const uint16_t* __restrict__ Y, int ldY, int n_d,
                                                    float* __restrict__ part, int R, int K, int row_lo,
                                                    int row_hi, int j_hi, int cr, Geom g) {
-  __shared__ __attribute__((aligned(1024))) char xb0[32 * 128 * 2];
-  __shared__ __attribute__((aligned(1024))) char yb0[32 * 64 * 2];
-  __shared__ __attribute__((aligned(1024))) char xb1[32 * 128 * 2];
-  __shared__ __attribute__((aligned(1024))) char yb1[32 * 64 * 2];
-  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 63) / 64;
+  __shared__ __attribute__((aligned(1024))) char xb0[kXtyM * 128 * 2];
+  __shared__ __attribute__((aligned(1024))) char xb1[kXtyM * 128 * 2];
+  __shared__ __attribute__((aligned(1024))) char xb2[kXtyM * 128 * 2];
+  __shared__ __attribute__((aligned(1024))) char yb0[2 * kXtyM * 64 * 2];
+  __shared__ __attribute__((aligned(1024))) char yb1[2 * kXtyM * 64 * 2];
+  __shared__ __attribute__((aligned(1024))) char yb2[2 * kXtyM * 64 * 2];
+  constexpr int YH = kXtyM * 64 * 2;   // bytes of one 64-dim half tile
+  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 127) / 128;
   int64_t idx = blockIdx.x;
   const int dt = (int)(idx % n_dt);
   idx /= n_dt;
@@ -480,62 +489,89 @@ __global__ __launch_bounds__(256, 2) void xty_gemm(const uint16_t* __restrict__ 
   const int c = (int)(idx / K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hl = lane >> 5, col = lane & 31;
-  const int j0 = jt * 128, d0 = dt * 64;
+  const int wk = wave & 1, wd = wave >> 1;   // this wave's 64 keys and 64 dims of the tile
+  const int j0 = jt * 128, d0 = dt * 128;
+  const bool second = d0 + 64 < n_d;         // the tile's second 64-dim half exists
+  const bool live = wd == 0 || second;
   const int rl = g.r_len[k];
   int i_lo, i_hi;
   xty_rows(c, cr, row_lo, row_hi, j0, rl, i_lo, i_hi);
   if (i_hi <= i_lo) return;
   const int64_t m_lo = (int64_t)i_lo * kLatH, m_hi = (int64_t)i_hi * kLatH;
-  const int n_steps = (int)((m_hi - m_lo) / 32);   // kLatH is a multiple of 32
-  const uint16_t* xs = X + ((int64_t)k * R * kLatH + m_lo) * R + j0;
-  const uint16_t* ys = Y + ((int64_t)k * R * kLatH + m_lo) * ldY + d0;
-  DirectLoad<128, 32, 4> dlx;
-  DirectLoad<64, 32, 4> dly;
-  dlx.init((int64_t)R * 2);
-  dly.init((int64_t)ldY * 2);
-  uint32_t xoff[2];                       // X^T fragment: key columns 32*wave .. +32
-  Frag<128>::trans_offsets(32 * wave, xoff);
+  const int n_steps = (int)((m_hi - m_lo) / kXtyM);   // kLatH is a multiple of kXtyM
+  const char* xs = reinterpret_cast<const char*>(X + ((int64_t)k * R * kLatH + m_lo) * R + j0);
+  const char* ys = reinterpret_cast<const char*>(Y + ((int64_t)k * R * kLatH + m_lo) * ldY + d0);
+  const char* ys2 = second ? ys + 64 * 2 : ys;
+  const uint32_t xstride = (uint32_t)R * 2, ystride = (uint32_t)ldY * 2;
+  DirectLoadRows<128, kXtyM, 4> dlx;
+  DirectLoadRows<64, kXtyM, 4> dly;
+  dlx.init();
+  dly.init();
+  constexpr int LOADS = DirectLoadRows<128, kXtyM, 4>::PER_WAVE + 2 * DirectLoadRows<64, kXtyM, 4>::PER_WAVE;
+  uint32_t xoff[2][2];                       // X^T fragments: key columns 64 wk + 32 kk .. +32
+  Frag<128>::trans_offsets(64 * wk, xoff[0]);
+  Frag<128>::trans_offsets(64 * wk + 32, xoff[1]);
   Frag<64> fy;
   fy.init();
-  f32x16 acc[2];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
-  dlx.issue(xb0, xs, 0, 32, (int64_t)R * 2);
-  dly.issue(yb0, ys, 0, 32, (int64_t)ldY * 2);
-  auto step = [&](const char* xc, const char* yc, char* xn, char* yn, int st) {
-    wait_vmcnt0();
-    __syncthreads();
-    if (st + 1 < n_steps) {
-      dlx.issue(xn, xs + (int64_t)(st + 1) * 32 * R, 0, 32, (int64_t)R * 2);
-      dly.issue(yn, ys + (int64_t)(st + 1) * 32 * ldY, 0, 32, (int64_t)ldY * 2);
-    }
-    prio_mfma();
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const bf16x8 a = Frag<128>::trans_at(xc, xoff, 0, h2);   // X^T: keys 32*wave .. +32
-#pragma unroll
-      for (int n = 0; n < 2; ++n) acc[n] = mfma32x32x16(a, fy.trans_frag(yc, 0, h2, n), acc[n]);
-    }
-    prio_valu();
+      for (int e = 0; e < 16; ++e) acc[kk][n][e] = 0.0f;
+  auto issue = [&](char* xb, char* yb, int st) {
+    dlx.issue(lds_addr(xb), xs + (int64_t)st * kXtyM * xstride, kXtyM, xstride);
+    dly.issue(lds_addr(yb), ys + (int64_t)st * kXtyM * ystride, kXtyM, ystride);
+    dly.issue(lds_addr(yb + YH), ys2 + (int64_t)st * kXtyM * ystride, kXtyM, ystride);
   };
-  for (int st = 0; st < n_steps; st += 2) {
-    step(xb0, yb0, xb1, yb1, st);
-    if (st + 1 < n_steps) step(xb1, yb1, xb0, yb0, st + 1);
+  // Stage st: its loads are done (only stage st+1's may be in flight), every wave is past
+  // its reads of stage st-1's buffer, which then receives stage st+2.
+  auto stage = [&](const char* xc, const char* yc, char* xn, char* yn, int st) {
+    if (st + 1 < n_steps) wait_vmcnt_n<LOADS>(); else wait_vmcnt0();
+    __syncthreads();
+    if (st + 2 < n_steps) issue(xn, yn, st + 2);
+    if (live) {
+      const char* yh = yc + wd * YH;
+      prio_mfma();
+#pragma unroll
+      for (int sub = 0; sub < kXtyM / 32; ++sub)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 a0 = Frag<128>::trans_at(xc, xoff[0], sub, h2);
+          const bf16x8 a1 = Frag<128>::trans_at(xc, xoff[1], sub, h2);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const bf16x8 b = fy.trans_frag(yh, sub, h2, n);
+            acc[0][n] = mfma32x32x16(a0, b, acc[0][n]);
+            acc[1][n] = mfma32x32x16(a1, b, acc[1][n]);
+          }
+        }
+      prio_valu();
+    }
+  };
+  issue(xb0, yb0, 0);
+  if (n_steps > 1) issue(xb1, yb1, 1);
+  for (int st = 0; st < n_steps; st += 3) {
+    stage(xb0, yb0, xb2, yb2, st);
+    if (st + 1 < n_steps) stage(xb1, yb1, xb0, yb0, st + 1);
+    if (st + 2 < n_steps) stage(xb2, yb2, xb1, yb1, st + 2);
   }
+  if (!live) return;
   // C layout: lane = dim column, registers = key rows
   float* pc = part + ((int64_t)c * K + k) * R * n_d;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    const int d = d0 + 32 * n + col;
+    const int d = d0 + 64 * wd + 32 * n + col;
     if (d >= n_d) continue;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = j0 + 32 * wave + (e >> 2) * 8 + 4 * hl + (e & 3);
-      if (j >= j_hi || j >= rl) continue;
-      pc[(int64_t)j * n_d + d] = acc[n][e];
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + 64 * wk + 32 * kk + (e >> 2) * 8 + 4 * hl + (e & 3);
+        if (j >= j_hi || j >= rl) continue;
+        pc[(int64_t)j * n_d + d] = acc[kk][n][e];
+      }
   }
 }
 
@@ -600,7 +636,7 @@ hipError_t launch_xty(const uint16_t* X, const uint16_t* Y, int ldY, int n_d, fl
                       hipStream_t s) {
   if (j_hi <= 0) return hipSuccess;
   const int cr = xty_chunk_rows(g.R), n_chunks = xty_n_chunks(g.R);
-  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 63) / 64;
+  const int n_jt = (j_hi + 127) / 128, n_dt = (n_d + 127) / 128;
   hipLaunchKernelGGL(xty_gemm, dim3((unsigned)((int64_t)n_chunks * g.K * n_jt * n_dt)), dim3(256), 0, s, X, Y,
                      ldY, n_d, part, g.R, g.K, row_lo, row_hi, j_hi, cr, g);
   hipError_t e = hipGetLastError();

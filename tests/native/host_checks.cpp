@@ -35,7 +35,9 @@ static int g_fail = 0;
 // key-parallel K/V-gradient kernels (64-row stream stages, 4 waves).
 struct RowsShape { int D, n_rows, waves; };
 
-static void check_rows_shape(const RowsShape& sh, uint32_t stride) {
+// slack: bytes past the last valid row that a load may touch (a row wider than the stride
+// runs into the next rows; the buffer ends in that much padding).
+static void check_rows_shape(const RowsShape& sh, uint32_t stride, uint32_t slack = 0) {
   const int G = sh.D / 8, RPI = 64 / G, ROW = sh.D * 2;
   const int per_wave = sh.n_rows * G / (64 * sh.waves);
   CHECK(per_wave * 64 * sh.waves == sh.n_rows * G, "tile does not split over the waves");
@@ -59,7 +61,7 @@ static void check_rows_shape(const RowsShape& sh, uint32_t stride) {
           const uint64_t exact = (uint64_t)a.src_row * stride + (uint64_t)((pos ^ swz(sh.D, t_row)) * 16);
           CHECK(a.src_off == exact, "offset %u != %llu (D %d row %d pos %d)", a.src_off,
                 (unsigned long long)exact, sh.D, t_row, pos);
-          CHECK((uint64_t)a.src_off + 16 <= (uint64_t)rows_valid * stride, "load past the stage's rows");
+          CHECK((uint64_t)a.src_off + 16 <= (uint64_t)rows_valid * stride + slack, "load past the stage's rows");
           (void)RPI;
         }
       }
@@ -121,6 +123,15 @@ static void check_addresses() {
     }
     // K/V-gradient kernels: packed stream rows of D bf16
     check_rows_shape({D, 64, 4}, (uint32_t)(D * 2));
+  }
+  // response-pair GEMM of the latent variant (ring form): 32- or 64-row stages of X rows of
+  // R bf16 (128 keys) and of Y rows of 576 or 512 dims (64-dim halves)
+  // (rows of fewer than 128 keys run into the next rows; the P / dS buffers end in one
+  // 128-key row segment of padding)
+  for (int rows : {32, 64}) {
+    for (uint32_t R : {32u, 64u, 96u, 4096u, 8192u, 65536u}) check_rows_shape({128, rows, 4}, R * 2, 256);
+    check_rows_shape({64, rows, 4}, 576 * 2);
+    check_rows_shape({64, rows, 4}, 512 * 2);
   }
   // part lengths: chunks and remainders of the workloads, response lengths, every small count
   for (int64_t n = 1; n <= 5000; ++n) check_stages(n, 64);
