@@ -64,7 +64,7 @@ SHARE_P256K = Workload("bf16_share_P262144_R8192", P=262144, R=8192, Hq=24, Hkv=
 
 # Full 2,097,152-position resident prompt, G=8 serial members, R_g uniform in [2048, 8192].
 FULL_P2M = Workload("bf16_full_P2097152_G8", P=2097152, R=8192, Hq=24, Hkv=4, d_qk=128,
-                    d_v=128, chunk=131072, block=2048, dtype="bf16", seed=1004, G=8,
+                    d_v=128, chunk=32768, block=2048, dtype="bf16", seed=1004, G=8,
                     r_min=2048)
 
 # Latent pages (512 + 64 rotary) shared by 64 heads, per-query top-2048 by fp32 index scores.
@@ -77,7 +77,7 @@ LATENT_P1M = Workload("bf16_latent_P1048576_R4096_top2048", P=1048576, R=4096, H
 # positions after P = 2,097,152 positions of history (256 completed chunks: last-layer K/V
 # of the older ones, the blended previous chunk), the 2M configuration's heads.
 LASTKV_P2M = Workload("bf16_lastkv_P2097152_C8192", P=2097152, R=8192, Hq=24, Hkv=4, d_qk=128,
-                      d_v=128, chunk=131072, block=2048, dtype="bf16", seed=1006)
+                      d_v=128, chunk=32768, block=2048, dtype="bf16", seed=1006)
 
 ALL = [TINY_F32, GQA_P128K, SHARE_P256K, FULL_P2M, LATENT_P1M, LASTKV_P2M]
 BY_NAME = {w.name: w for w in ALL}

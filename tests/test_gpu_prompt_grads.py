@@ -135,8 +135,9 @@ def test_full_size_key_sums():
       sum_j dV[j, g] = sum over rows i and heads h of g of dO[i, h]   (each row of P sums to 1)
       sum_j dK[j, g] = 0                                              (each row of dS sums to 0)
     The first is held to the bf16 bounds.  For the second the bf16 rounding of dS before
-    its product leaves a residue of about 1e-3 of |dK|; a term dropped over one 131,072-key
-    chunk leaves about 0.25, so the bound is 2e-2 of the norm of all dK rows."""
+    its product leaves a residue of about 1e-3 of |dK|; a term dropped over one prompt chunk
+    leaves about the square root of the chunk's share of the keys (0.25 for 131,072 of 2M
+    keys, 0.125 for 32,768), so the bound is 2e-2 of the norm of all dK rows."""
     w = configs.FULL_P2M
     Rg = int(synth.response_lengths(w)[0])
     print(f"[prompt_grads] {w.name} key sums, R={Rg}", flush=True)
