@@ -235,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void dq_partials_bf16(
   const bool valid = m < m_hi && r < rl;
   const int lim = resp ? min(r, n_keys - 1) : n_keys - 1;
   const int64_t row = ((int64_t)w.k * g.R + r) * g.Hq + h;
-  const int64_t orow = m < m_hi ? ((int64_t)w.part * g.K * g.R * g.Hq + row) : -1;
+  const int64_t orow = m < m_hi ? ((int64_t)w.part * g.part_step + row * g.row_step) : -1;
   const float lse2 = valid ? lse[row] * kLog2e : INFINITY;
   const float dvv = valid ? Dvec[row] : 0.0f;
   f32x16 dinit;

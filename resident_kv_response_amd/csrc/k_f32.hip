@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_partials_f32(Geom g, const float
     }
   }
   if (!in_range) return;
-  const int64_t orow = (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h;
+  const int64_t orow = (int64_t)w.part * g.part_step + (((int64_t)w.k * g.R + r) * g.Hq + h) * g.row_step;
   const bool live = valid && l > 0.0f;
   const float inv = live ? 1.0f / l : 0.0f;
 #pragma unroll
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kF32Rows) void dq_partials_f32(Geom g, const float*
     }
   }
   if (!in_range) return;
-  const int64_t orow = (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h;
+  const int64_t orow = (int64_t)w.part * g.part_step + (((int64_t)w.k * g.R + r) * g.Hq + h) * g.row_step;
 #pragma unroll
   for (int d = 0; d < D; ++d) dq_part[orow * D + d] = valid ? acc[d] * g.tau : 0.0f;
 }

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(512 / NT, 1) void fwd_partials_bf16(
     const int r = m / g.grp, h = w.g * g.grp + m % g.grp;
     valid[t] = m < m_hi && r < rl;
     lim[t] = resp ? min(r, n_keys - 1) : n_keys - 1;
-    orow[t] = m < m_hi ? (((int64_t)w.part * g.K + w.k) * g.R + r) * g.Hq + h : -1;
+    orow[t] = m < m_hi ? (int64_t)w.part * g.part_step + (((int64_t)w.k * g.R + r) * g.Hq + h) * g.row_step : -1;
     const uint16_t* qrow = q + (((int64_t)w.k * g.R + r) * g.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)

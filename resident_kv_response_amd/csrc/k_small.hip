@@ -9,16 +9,15 @@ namespace rr {
 // Composition of softmax-statistics partials into the exact output
 // (ai.thesatyajit.com/articles/longstraw-2m-rl, section "Two incompatible
 // architectures, same transaction"): lse = ln sum_c e^{lse_c}, O = sum_c e^{lse_c-lse} O_c.
-// One wave per row: lane c reads lse_c once (lanes c, c + 64, ... for more parts), the
-// wave reduces max and sum in a fixed order, and every lane then streams its VEC columns
-// of all parts in part order, the weights broadcast from the lanes that hold them, several
-// parts' loads in flight at once.
-template <int VEC>
+// Scalar form (any d_v or alignment): one wave per row, lane c reads lse_c once (lanes c,
+// c + 64, ... for more parts), the wave reduces max and sum in a fixed order, and every
+// lane then streams its column of all parts in part order, the weights broadcast from the
+// lanes that hold them, several parts' loads in flight at once.
 __global__ __launch_bounds__(256) void merge_kernel(int n_parts, int64_t rows, int d_v,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     float* __restrict__ o, float* __restrict__ lse,
-                                                    bool use_geom, Geom g) {
+                                                    bool use_geom, Geom g, int64_t ps, int64_t rs) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -29,14 +28,15 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, int64_t rows, i
     pad = r >= g.r_len[k];
   }
   float m = -INFINITY;
+  const float* lrow = part_lse + row * rs;   // part c of this row at lrow[c * ps]
   if (!pad)
-    for (int c = lane; c < n_parts; c += 64) m = fmaxf(m, part_lse[(int64_t)c * rows + row]);
+    for (int c = lane; c < n_parts; c += 64) m = fmaxf(m, lrow[(int64_t)c * ps]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   float out_lse = -INFINITY, inv = 0.0f;
   if (m != -INFINITY) {
     float den = 0.0f;
-    for (int c = lane; c < n_parts; c += 64) den += expf(part_lse[(int64_t)c * rows + row] - m);
+    for (int c = lane; c < n_parts; c += 64) den += expf(lrow[(int64_t)c * ps] - m);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
     out_lse = m + logf(den);
@@ -45,63 +45,122 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, int64_t rows, i
   float* dst = o + row * d_v;
   // every lane runs every iteration (the weight broadcasts need all lanes); lanes past d_v
   // load and store nothing
-  for (int base = 0; base < d_v; base += 64 * VEC) {
-    const int col = base + lane * VEC;
+  for (int base = 0; base < d_v; base += 64) {
+    const int col = base + lane;
     const bool on = col < d_v;
-    float acc[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    float acc = 0.0f;
     if (m != -INFINITY) {
       for (int c0 = 0; c0 < n_parts; c0 += 64) {
         // weights of parts c0 .. c0 + 63, one per lane (0 for -inf parts and past the end)
         const int cl = c0 + lane;
-        const float lc = cl < n_parts ? part_lse[(int64_t)cl * rows + row] : -INFINITY;
+        const float lc = cl < n_parts ? lrow[(int64_t)cl * ps] : -INFINITY;
         const float wl = lc == -INFINITY ? 0.0f : expf(lc - m) * inv;
         const int n = min(64, n_parts - c0);
         int j = 0;
         for (; j + 4 <= n; j += 4) {          // four parts' loads in flight
-          float x[4][VEC];
+          float x[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float* src = part_o + ((int64_t)(c0 + j + u) * rows + row) * d_v + col;
-            if constexpr (VEC == 4) {
-              const float4 y = on ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-              x[u][0] = y.x;
-              x[u][1] = y.y;
-              x[u][2] = y.z;
-              x[u][3] = y.w;
-            } else {
-              x[u][0] = on ? src[0] : 0.0f;
-            }
-          }
+          for (int u = 0; u < 4; ++u)
+            x[u] = on ? part_o[((int64_t)(c0 + j + u) * ps + row * rs) * d_v + col] : 0.0f;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float w = __shfl(wl, j + u, 64);
-            if (w != 0.0f) {
-#pragma unroll
-              for (int v = 0; v < VEC; ++v) acc[v] += w * x[u][v];
-            }
+            if (w != 0.0f) acc += w * x[u];
           }
         }
         for (; j < n; ++j) {
           const float w = __shfl(wl, j, 64);
-          const float* src = part_o + ((int64_t)(c0 + j) * rows + row) * d_v + col;
-          if (w != 0.0f && on) {
+          if (w != 0.0f && on) acc += w * part_o[((int64_t)(c0 + j) * ps + row * rs) * d_v + col];
+        }
+      }
+    }
+    if (on) dst[col] = acc;
+  }
+  if (lane == 0) lse[row] = out_lse;
+}
+
+// Two rows per wave for d_v % 4 == 0: lanes 0-31 merge one row, lanes 32-63 the next,
+// each lane four consecutive columns of a 128-column pass.  The 32 lanes of a row reduce
+// its lse_c (lane l holds parts l, l + 32, ...) in a fixed order, then stream the parts in
+// part order with sixteen parts' loads in flight, the weight of part c broadcast from the
+// lane that holds it.  Every lane of a 128-wide row is busy, where one wave per row left
+// half of them idle at d_v = 128.
+__global__ __launch_bounds__(256) void merge_rows_kernel(int n_parts, int64_t rows, int d_v,
+                                                         const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_lse,
+                                                         float* __restrict__ o, float* __restrict__ lse,
+                                                         bool use_geom, Geom g, int64_t ps, int64_t rs) {
+  const int l = threadIdx.x & 31;
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;   // whole 32-lane halves only: every shuffle below stays in its half
+  bool pad = false;
+  if (use_geom) {
+    const int64_t kr = row / g.Hq;
+    const int k = (int)(kr / g.R), r = (int)(kr % g.R);
+    pad = r >= g.r_len[k];
+  }
+  float m = -INFINITY;
+  const float* lrow = part_lse + row * rs;   // part c of this row at lrow[c * ps]
+  if (!pad)
+    for (int c = l; c < n_parts; c += 32) m = fmaxf(m, lrow[(int64_t)c * ps]);
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] += w * src[v];
+  for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+  float out_lse = -INFINITY, inv = 0.0f;
+  if (m != -INFINITY) {
+    float den = 0.0f;
+    for (int c = l; c < n_parts; c += 32) den += expf(lrow[(int64_t)c * ps] - m);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) den += __shfl_xor(den, off, 32);
+    out_lse = m + logf(den);
+    inv = 1.0f / den;
+  }
+  float* dst = o + row * d_v;
+  for (int base = 0; base < d_v; base += 128) {
+    const int col = base + 4 * l;
+    const bool on = col < d_v;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m != -INFINITY) {
+      const float* src0 = part_o + row * rs * d_v + col;
+      const int64_t pstride = ps * d_v;
+      for (int c0 = 0; c0 < n_parts; c0 += 32) {
+        // weights of parts c0 .. c0 + 31, one per lane (0 for -inf parts and past the end)
+        const int cl = c0 + l;
+        const float lc = cl < n_parts ? lrow[(int64_t)cl * ps] : -INFINITY;
+        const float wl = lc == -INFINITY ? 0.0f : expf(lc - m) * inv;
+        const int n = min(32, n_parts - c0);
+        int j = 0;
+        for (; j + 16 <= n; j += 16) {          // sixteen parts' loads in flight
+          float4 x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            x[u] = on ? *reinterpret_cast<const float4*>(src0 + (int64_t)(c0 + j + u) * pstride)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const float w = __shfl(wl, j + u, 32);
+            if (w != 0.0f) {
+              acc.x += w * x[u].x;
+              acc.y += w * x[u].y;
+              acc.z += w * x[u].z;
+              acc.w += w * x[u].w;
+            }
+          }
+        }
+        for (; j < n; ++j) {
+          const float w = __shfl(wl, j, 32);
+          if (w != 0.0f && on) {
+            const float4 x = *reinterpret_cast<const float4*>(src0 + (int64_t)(c0 + j) * pstride);
+            acc.x += w * x.x;
+            acc.y += w * x.y;
+            acc.z += w * x.z;
+            acc.w += w * x.w;
           }
         }
       }
     }
-    if (on) {
-      if constexpr (VEC == 4) {
-        *reinterpret_cast<float4*>(dst + col) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      } else {
-        dst[col] = acc[0];
-      }
-    }
+    if (on) *reinterpret_cast<float4*>(dst + col) = acc;
   }
-  if (lane == 0) lse[row] = out_lse;
+  if (l == 0) lse[row] = out_lse;
 }
 
 hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
@@ -110,14 +169,18 @@ hipError_t launch_merge(int n_parts, int64_t rows, int d_v, const float* part_o,
   if (rows == 0) return hipSuccess;
   Geom g{};
   if (geom) g = *geom;
+  // the fused path's partials carry their layout in the geometry; rr_lse_merge's are part-major
+  const int64_t ps = geom ? g.part_step : rows, rs = geom ? g.row_step : 1;
   const bool vec4 = (d_v % 4 == 0) && ((uintptr_t)part_o % 16 == 0) && ((uintptr_t)o % 16 == 0);
-  const int64_t blocks = (rows + 3) / 4;            // four rows (waves) per workgroup
-  if (vec4)
-    hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, n_parts, rows, d_v,
-                       part_o, part_lse, o, lse, geom != nullptr, g);
-  else
-    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, n_parts, rows, d_v,
-                       part_o, part_lse, o, lse, geom != nullptr, g);
+  if (vec4) {
+    const int64_t blocks = (rows + 7) / 8;          // eight rows (half-waves) per workgroup
+    hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, n_parts, rows, d_v,
+                       part_o, part_lse, o, lse, geom != nullptr, g, ps, rs);
+  } else {
+    const int64_t blocks = (rows + 3) / 4;          // four rows (waves) per workgroup
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, n_parts, rows, d_v,
+                       part_o, part_lse, o, lse, geom != nullptr, g, ps, rs);
+  }
   return hipGetLastError();
 }
 
@@ -183,7 +246,9 @@ hipError_t launch_bwd_pre(const Geom& g, int dtype, const float* o, const void* 
 }
 
 // ---- ordered dQ reduction ------------------------------------------------------------
-// dq = sum_c part_c in part order (deterministic); one float4 per thread.
+// dq = sum_c part_c in part order (deterministic); one float4 per thread.  The partials of
+// row m (part c at row index c * part_step + m * row_step) are one contiguous run when
+// they are row-major.
 __global__ __launch_bounds__(256) void dq_reduce_kernel(Geom g, const float* __restrict__ part,
                                                         float* __restrict__ dq, int accumulate) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -193,12 +258,16 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(Geom g, const float* __r
   const int k = (int)(t / per_k);
   const int64_t rem = t % per_k;
   const int r = g.row_lo + (int)(rem / ((int64_t)g.Hq * q4));
-  const int64_t off = (((int64_t)k * g.R + r) * g.Hq) * g.dqk + (rem % ((int64_t)g.Hq * q4)) * 4;
-  const int64_t stride = (int64_t)g.K * g.R * g.Hq * g.dqk;
+  const int hq4 = (int)(rem % ((int64_t)g.Hq * q4));
+  const int64_t m = ((int64_t)k * g.R + r) * g.Hq + hq4 / q4;   // row index (k, r, h)
+  const int col = (hq4 % q4) * 4;
+  const int64_t off = m * g.dqk + col;
+  const float* src = part + m * g.row_step * g.dqk + col;
+  const int64_t pstep = g.part_step * g.dqk;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (r < g.r_len[k]) {
     for (int c = 0; c < g.n_parts; ++c) {
-      const float4 x = *reinterpret_cast<const float4*>(part + c * stride + off);
+      const float4 x = *reinterpret_cast<const float4*>(src + c * pstep);
       acc.x += x.x;
       acc.y += x.y;
       acc.z += x.z;

@@ -259,7 +259,7 @@ int rr_attn_fwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, 
                         {"part_lse", part_lse}, {"topk_idx", topk_idx}, {"ws", ws_is_scratch ? nullptr : ws}})))
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Geom g = make_geom(p, r_len);
+  Geom g = make_geom(p, r_len);
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
   if (p->latent) {
     // exact top-k per row (screen + candidates + exact selection) -> attention over the
@@ -276,9 +276,10 @@ int rr_attn_fwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, 
   }
   float* po = part_o;
   float* pl = part_lse;
-  if (!po) {
+  if (!po) {   // partials in the workspace: row-major; an export buffer keeps part-major
     po = carve(ws, 0);
     pl = carve(ws, align_up((size_t)g.n_parts * rows * p->d_v * sizeof(float), 256));
+    set_parts_row_major(g);
   }
   AttnPtrs a{};
   a.q = q;
@@ -346,6 +347,7 @@ int rr_attn_bwd_impl(const rr_problem* p, const rr_resident* kv, const void* q, 
     return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Geom g = make_geom(p, r_len);
+  set_parts_row_major(g);   // the dQ partials live in the workspace
   const size_t rows = (size_t)p->K * p->R_max * p->Hq;
   if (p->latent) return latent_bwd(p, kv, q, k_r, r_len, topk_idx, o, lse, d_o, dq, dk_r, dv_r,
                                    accumulate, block_idx, ws, s);

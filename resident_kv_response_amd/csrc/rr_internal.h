@@ -25,7 +25,19 @@ struct Geom {
   int32_t resp_keys;  // 1: the response's own causal keys form the last part; 0: another
                       // prompt shard owns them and the last part is empty
   int32_t r_len[RR_MAX_K];
+  // Partial buffers (forward O_c / lse_c, dQ partials): the values of part c for row
+  // m = (k R + r) Hq + h start at row index c * part_step + m * row_step (times the head
+  // dim for O and dQ).  Part-major (part_step = K R Hq, row_step = 1) is the exported
+  // layout; the workspace holds them row-major (part_step = 1, row_step = n_parts), so the
+  // merge and the dQ reduction read each row's parts as one contiguous run.
+  int64_t part_step;
+  int64_t row_step;
 };
+
+inline void set_parts_row_major(Geom& g) {
+  g.part_step = 1;
+  g.row_step = g.n_parts;
+}
 
 // ---- validation (HIP-free; rr_validate.cpp) ----------------------------------------
 int set_error(int code, const char* fmt, ...);

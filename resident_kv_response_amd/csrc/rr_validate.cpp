@@ -387,6 +387,8 @@ Geom make_geom(const rr_problem* p, const int32_t* r_len) {
   g.c2 = (float)(p->tau * 1.4426950408889634);
   g.resp_keys = (p->flags & RR_FLAG_SHARD_NO_RESPONSE) ? 0 : 1;
   for (int k = 0; k < p->K; ++k) g.r_len[k] = r_len[k];
+  g.part_step = (int64_t)p->K * p->R_max * p->Hq;   // part-major unless a caller picks otherwise
+  g.row_step = 1;
   return g;
 }
 
