@@ -83,9 +83,7 @@ struct DirectLoad {
 // the barrier that publishes a stage, and no load into a buffer that a wave may still
 // read.  (When the compiler does track them it treats every outstanding LDS read as
 // unordered and waits for all of them before each use, which defeats reading fragments
-// ahead.)  The compiler counts M0 as reserved and ignores the asm's clobber of it (it
-// warns so); that is sound only while it neither writes nor reads M0 in the kernels
-// issuing these loads, which tests/test_m0_usage.py checks on their gfx950 assembly.
+// ahead.)
 template <int D, int N_ROWS, int WAVES>
 struct DirectLoadRows {
   using DL = DirectLoad<D, N_ROWS, WAVES>;
