@@ -130,7 +130,7 @@ def source_sha(files) -> str:
 def main() -> int:
     a = _args()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU (no path across GPUs); --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
         return 2
     if a.copy_calibration:
