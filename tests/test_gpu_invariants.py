@@ -87,6 +87,13 @@ def test_exported_partials_merge():
     torch.cuda.synchronize()
     np.testing.assert_allclose(o2.cpu().numpy(), run.o.cpu().numpy(), rtol=0, atol=1e-6)
     np.testing.assert_allclose(l2.cpu().numpy(), run.lse.cpu().numpy(), rtol=0, atol=1e-6)
+    # Exported partials are part-major, workspace partials row-major: the same arithmetic at
+    # other addresses, so the forward without export gives the same bits.
+    o_exp, l_exp = run.o.clone(), run.lse.clone()
+    run.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(run.o, o_exp) and torch.equal(run.lse, l_exp), "workspace and export layouts differ"
+    run.guard.check()
     # per-part statistics against the oracle's chunk partials (rows 0 and R-1)
     f = lambda x: synth.as_f64(x, W.dtype)
     rows = np.array([0, 255, W.R - 1])
